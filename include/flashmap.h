@@ -1,0 +1,199 @@
+/*
+ * flashmap.h - C ABI of the MI355X (gfx950) FlashMap drafting step.
+ *
+ * The method (five news pages about FlashMap):
+ *   - "FlashMap并行草拟加速大模型解码" (feinterview.poetries.top), first and
+ *     second sections: K = 16 tokens drafted at once and verified by the target
+ *     in one parallel pass, longest matching prefix kept; the drafter is a
+ *     6-block DiT of width 2048 with 16 heads that reads target layers 1, 9,
+ *     17, 25, 33 and reuses the target's frozen embedding and LM head; a flow
+ *     teacher over one-hot token blocks is distilled into a flow map that goes
+ *     from Gaussian noise to a whole block in one jump.
+ *   - wire.sakhanda.co, "Как работает FlashMap?": the student is a denoiser
+ *     with two time points; "Как развернуть FlashMap?": num_steps = 2 is an
+ *     option; drafter and target share one GPU.
+ *   - alphasignal.ai, "Why drafting still costs time": one cycle = propose a
+ *     block, score it in parallel, accept the longest valid prefix, resume
+ *     from a target token.
+ *
+ * Conventions for every entry point:
+ *   - Tensor arguments are DEVICE pointers owned by the caller, unless a
+ *     comment says "host".  They must stay valid until the stream reaches the
+ *     call (weights: for the handle's lifetime).
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Calls only enqueue work; they never synchronize and never allocate
+ *     device memory, so a draft+verify sequence can be captured in a HIP graph.
+ *   - Every argument check runs on the host before anything is enqueued.  On
+ *     an error status nothing has been enqueued and no output was written;
+ *     fm_last_error() describes the failure (thread-local string).
+ *   - Inputs are assumed finite; NaN handling is unspecified.
+ *   - Calls on one handle must not overlap on different streams.
+ */
+#ifndef FLASHMAP_H
+#define FLASHMAP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fm_status {
+  FM_OK = 0,
+  FM_EINVAL = 1,     /* bad argument (NULL, size, alignment, order)          */
+  FM_ECAPACITY = 2,  /* context or batch capacity of the handle exceeded     */
+  FM_EHIP = 3,       /* a HIP runtime call or kernel launch failed           */
+  FM_ESTATE = 4      /* call out of order (e.g. draft before set_weights)    */
+} fm_status;
+
+typedef enum fm_dtype {
+  FM_BF16 = 0,  /* bfloat16 storage, float32 accumulation                     */
+  FM_F32 = 1    /* float32 storage and arithmetic                             */
+} fm_dtype;
+
+/* Drafter shape and capacities.  Constraints checked by fm_create:
+ *   K == 16; d % 64 == 0; n_heads divides d with d / n_heads in {64, 128};
+ *   mlp_mult >= 1; n_ctx_layers == 5; V >= 16 and H >= 1 with V, H and d
+ *   multiples of 8 (bf16) or 4 (f32), so every row starts 16-byte aligned;
+ *   1 <= max_branches <= 4; 0 <= max_new <= 16; C_max >= 0; 1 <= max_steps <= 4. */
+typedef struct fm_config {
+  int K;             /* drafted block length (16)                            */
+  int V;             /* vocabulary size (151936 for Qwen3)                    */
+  int d;             /* drafter width (2048)                                  */
+  int L;             /* DiT blocks (6)                                        */
+  int n_heads;       /* attention heads (16)                                  */
+  int mlp_mult;      /* MLP width = mlp_mult * d (4)                          */
+  int H;             /* target hidden width per context layer                 */
+  int n_ctx_layers;  /* target layers read (5: layers 1, 9, 17, 25, 33)       */
+  int C_max;         /* context rows the cache can hold                       */
+  int max_branches;  /* noise branches per draft (1, or 4 for a draft tree)   */
+  int max_new;       /* context rows a single fm_draft call may append        */
+  int max_steps;     /* flow-map jumps per draft (1, or 2 for num_steps = 2)  */
+  fm_dtype dtype;    /* storage type of weights, features, noise              */
+} fm_config;
+
+/* Weights of one DiT block, all row-major [out][in], dtype = cfg.dtype:
+ *   W_ada [6d][d], b_ada [6d]  adaLN: shift1, scale1, gate1, shift2, scale2, gate2
+ *   W_qkv [3d][d], b_qkv [3d]  rows 0..d-1 query, d..2d-1 key, 2d..3d-1 value
+ *   W_o   [d][d],  b_o   [d]
+ *   W_1   [F][d],  b_1   [F]   F = mlp_mult * d
+ *   W_2   [d][F],  b_2   [d]                                                 */
+typedef struct fm_block_weights {
+  const void *W_ada, *b_ada, *W_qkv, *b_qkv, *W_o, *b_o, *W_1, *b_1, *W_2, *b_2;
+} fm_block_weights;
+
+/* All drafter weights (device pointers, dtype = cfg.dtype, borrowed for the
+ * handle's lifetime):
+ *   E    [V][d]   frozen token embedding, one row per token
+ *   W_lm [V][d]   frozen LM head, one row per token, no bias
+ *   W_f  [d][n_ctx_layers*H], b_f [d]   context-feature fusion
+ *   te_{s,t}_W1 [d][256], _b1 [d], _W2 [d][d], _b2 [d]   time embeddings of
+ *                 the jump's start time s and end time t
+ *   W_fa [2d][d], b_fa [2d]   final adaLN: shift, scale
+ *   blocks        HOST array of L block-weight structs (copied by the call)  */
+typedef struct fm_weights {
+  const void *E, *W_lm, *W_f, *b_f;
+  const void *te_s_W1, *te_s_b1, *te_s_W2, *te_s_b2;
+  const void *te_t_W1, *te_t_b1, *te_t_W2, *te_t_b2;
+  const void *W_fa, *b_fa;
+  const fm_block_weights *blocks;
+} fm_weights;
+
+typedef struct fm_handle fm_handle;
+
+/* Bytes of device workspace a handle with this configuration needs (context
+ * K/V cache [L][C_max][2][d], modulation vectors, activations, split-K
+ * partials and counters).  Returns 0 for an invalid configuration. */
+size_t fm_workspace_bytes(const fm_config *cfg);
+
+/* Create a handle on `device` using the caller's workspace (device memory of
+ * at least fm_workspace_bytes(cfg) bytes, 256-byte aligned, owned by the
+ * caller, not to be touched while the handle lives).  Enqueues a clear of the
+ * workspace's counters on the null stream and waits for it.  The context
+ * starts empty.  Errors: FM_EINVAL (config, NULL, alignment), FM_ECAPACITY
+ * (ws_bytes too small), FM_EHIP. */
+fm_status fm_create(const fm_config *cfg, void *workspace, size_t ws_bytes, int device,
+                    fm_handle **out);
+
+/* Release host state.  The workspace and weights stay the caller's. */
+void fm_destroy(fm_handle *h);
+
+/* Bind the weights (pointers are borrowed; nothing is copied on the device).
+ * Must precede fm_set_schedule, fm_context_append and fm_draft.  Errors:
+ * FM_EINVAL (a NULL or misaligned pointer). */
+fm_status fm_set_weights(fm_handle *h, const fm_weights *w);
+
+/* Precompute the adaLN vectors of every jump of a flow-map schedule
+ * (wire.sakhanda.co, "Как работает FlashMap?": a two-time-point denoiser;
+ * "Как развернуть FlashMap?": num_steps = 1 or 2).  `times` is a HOST array of
+ * num_steps + 1 floats rising strictly from times[0] = 0 to times[num_steps]
+ * = 1.  For each jump (s, t): c = TE_s(s) + TE_t(t); per block
+ * W_ada silu(c) + b_ada; final W_fa silu(c) + b_fa, all in float32, stored in
+ * the workspace.  The vectors depend only on (s, t) and the weights, so this
+ * runs once per schedule, off the per-draft path.  Errors: FM_EINVAL
+ * (order, num_steps outside 1..max_steps), FM_ESTATE (no weights), FM_EHIP. */
+fm_status fm_set_schedule(fm_handle *h, const float *times, int num_steps, void *stream);
+
+/* Append n rows of target hidden states to the context (prefill, or rows
+ * accepted outside fm_draft).  feats: [n][n_ctx_layers][H], layers in the
+ * order 1, 9, 17, 25, 33 (feinterview.poetries.top, second section).  For
+ * each row: u = LN(W_f concat(feats) + b_f); for each block the row's key and
+ * value (W_k u + b_k, W_v u + b_v) are written to the cache.  Errors:
+ * FM_EINVAL, FM_ECAPACITY (length + n > C_max), FM_ESTATE, FM_EHIP. */
+fm_status fm_context_append(fm_handle *h, const void *feats, int n, void *stream);
+
+/* Roll the context back (or forward over rows already written) to new_len
+ * rows: host bookkeeping only, nothing is enqueued.  Errors: FM_EINVAL
+ * (new_len < 0 or new_len > the highest row ever written). */
+fm_status fm_context_truncate(fm_handle *h, int new_len);
+
+/* Current context length (rows), or -1 for a NULL handle. */
+int fm_context_length(const fm_handle *h);
+
+/* One drafting step (feinterview.poetries.top, first section: the same noise
+ * decides every position of the block jointly; wire.sakhanda.co, "Что такое
+ * FlashMap?": K proposals from Gaussian noise in one step).
+ *   noise     [B][K][V]  Gaussian noise blocks, one per branch
+ *   B         branches, 1 <= B <= max_branches (B = 4: a draft tree whose
+ *             branches share the context and do not see each other)
+ *   new_feats [n_new][n_ctx_layers][H] context rows appended first (may be
+ *             NULL when n_new == 0); they become rows length..length+n_new-1
+ *   tokens    [B][K] int32 output: the draft
+ *   logits    [B][K][V] float32 output of the last jump, or NULL
+ *   hidden    [num_steps][L+1][B][K][d] float32 output: the residual stream
+ *             after the embedding and after every block, or NULL
+ * Computes, per jump (s, t) of the schedule: h = x_s E + P (P a fixed
+ * sinusoidal table over the K positions), the L blocks (adaLN-modulated
+ * attention of the block rows over [context; own block] keys, MLP), final
+ * LN/modulation, logits = z W_lm^T; at t = 1 the tokens are the row argmax
+ * of the float32 logits (lowest index among equal maxima); before t = 1 the
+ * state moves by the flow map of the linear interpolant.  The context length
+ * advances by n_new.  Errors: FM_EINVAL, FM_ECAPACITY, FM_ESTATE (no weights
+ * or no schedule), FM_EHIP. */
+fm_status fm_draft(fm_handle *h, const void *noise, int B, const void *new_feats, int n_new,
+                   int32_t *tokens, float *logits, float *hidden, void *stream);
+
+/* Greedy verification (feinterview.poetries.top, first section;
+ * wire.sakhanda.co, "Что такое FlashMap?"; alphasignal.ai, "Why drafting
+ * still costs time").  Stateless; needs no handle.
+ *   target_logits [B][K+1][V] (dtype): row j is the target's prediction for
+ *             draft slot j, row K the token after a fully accepted block
+ *   draft     [B][K] int32
+ *   emitted   [B][K+1] int32 output: draft[0..n-1], then y_n, then -1 padding
+ *   accept    [B] int32 output: n = longest prefix with draft[i] == y_i,
+ *             y_j = lowest-index argmax of row j
+ *   best      [1] int32 output: lowest branch index with the largest n
+ * Requires 1 <= B <= 64, 1 <= K <= 64, V >= 1.  Errors: FM_EINVAL, FM_EHIP. */
+fm_status fm_verify(const void *target_logits, fm_dtype dtype, int B, int K, int V,
+                    const int32_t *draft, int32_t *emitted, int32_t *accept, int32_t *best,
+                    void *stream);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char *fm_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLASHMAP_H */

@@ -187,7 +187,7 @@ def fuse_context(W, feats, prec):
 
     feats: [C][5][H] values in layer order 1, 9, 17, 25, 33."""
     C = feats.shape[0]
-    f = feats.reshape(C, -1)
+    f = feats.reshape(C, feats.shape[1] * feats.shape[2])  # C may be 0
     return prec.act(layer_norm(f @ W["W_f"].T + W["b_f"]))
 
 

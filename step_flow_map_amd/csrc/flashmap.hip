@@ -1,0 +1,729 @@
+// Host side of the FlashMap drafting library: argument checks, workspace
+// layout, launch planning and the launch sequences behind the C ABI declared
+// in include/flashmap.h.  Every check runs before anything is enqueued.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/flashmap.h"
+#include "attention.hpp"
+#include "common.hpp"
+#include "embed.hpp"
+#include "gemm.hpp"
+#include "lmhead.hpp"
+#include "norm.hpp"
+#include "schedule.hpp"
+#include "softmax.hpp"
+#include "verify.hpp"
+
+using namespace fm;
+
+namespace {
+
+thread_local std::string g_err;
+
+fm_status fail(fm_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+#define FM_HIP(call)                                                                   \
+  do {                                                                                 \
+    hipError_t e_ = (call);                                                            \
+    if (e_ != hipSuccess) return fail(FM_EHIP, "%s: %s", #call, hipGetErrorString(e_)); \
+  } while (0)
+
+#define FM_LAUNCHED(what)                                                                       \
+  do {                                                                                          \
+    hipError_t e_ = hipGetLastError();                                                          \
+    if (e_ != hipSuccess) return fail(FM_EHIP, "launch of %s: %s", what, hipGetErrorString(e_)); \
+  } while (0)
+
+#define FM_TRY(expr)                 \
+  do {                               \
+    fm_status s_ = (expr);           \
+    if (s_ != FM_OK) return s_;      \
+  } while (0)
+
+constexpr int KB = 16;             // block rows per branch (K)
+constexpr int ATT_CH = 64;         // keys per attention workgroup
+constexpr int GEMM_WAVES = 4;
+constexpr int LM_WAVES = 4;
+constexpr int EMB_WAVES = 4;
+constexpr int MAX_PREFILL_ROWS = 16;
+constexpr int GEMM_TARGET_WG = 512;
+constexpr int EMB_TARGET_WG = 1024;
+constexpr int LM_GRID = 512;
+constexpr int N_COUNTERS = 8192;
+constexpr int SOFTMAX_CHUNK = 4096;
+
+size_t esize(fm_dtype t) { return t == FM_BF16 ? 2 : 4; }
+int vec_elems(fm_dtype t) { return t == FM_BF16 ? 8 : 4; }
+int gemm_u(fm_dtype t) { return t == FM_BF16 ? 8 : 4; }
+int gemm_chunk(fm_dtype t) { return 4 * gemm_u(t) * vec_elems(t); }
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+struct GemmPlan {
+  int S, k_split, n_groups, grid;
+};
+
+GemmPlan plan_gemm(int N, int K, fm_dtype t) {
+  const int chunk = gemm_chunk(t);
+  GemmPlan p;
+  p.n_groups = cdiv(N, 16);
+  const int max_s = std::max(1, cdiv(K, chunk));
+  int S = std::min(max_s, std::max(1, cdiv(GEMM_TARGET_WG, p.n_groups)));
+  p.k_split = cdiv(cdiv(K, S), chunk) * chunk;
+  p.S = cdiv(K, p.k_split);
+  p.grid = p.n_groups * p.S;
+  return p;
+}
+
+struct EmbedPlan {
+  int S, rows_split, n_cb, grid;
+};
+
+EmbedPlan plan_embed(int V, int d, fm_dtype t) {
+  const int ve = vec_elems(t), rch = 4 * ve;
+  EmbedPlan p;
+  p.n_cb = d / (16 * ve);
+  int S = cdiv(EMB_TARGET_WG, p.n_cb);
+  S = std::min(S, cdiv(V, rch));
+  S = std::max(8, cdiv(S, 8) * 8);
+  p.rows_split = cdiv(cdiv(V, S), rch) * rch;
+  p.S = S;  // trailing splits may be empty; they still arrive
+  p.grid = p.n_cb * p.S;
+  return p;
+}
+
+struct Layout {
+  size_t cache, mods, sched, h, e_state, u_pre, act_qkv, act_d, attn_o, act_f, qkv;
+  size_t att_po, att_ml, partial, lm_part, counters, dsoft, logits_tmp, sm_part, total;
+};
+
+int max_rows(const fm_config& c) { return c.max_branches * KB; }
+int max_chunks(const fm_config& c) { return cdiv(c.C_max + KB, ATT_CH); }
+
+size_t partial_bytes(const fm_config& c) {
+  const int Mb = max_rows(c), F = c.mlp_mult * c.d, d = c.d;
+  struct S3 { int M, N, K; };
+  const S3 shapes[] = {{Mb + c.max_new, 3 * d, d}, {Mb, d, d}, {Mb, F, d}, {Mb, d, F},
+                       {MAX_PREFILL_ROWS, d, c.n_ctx_layers * c.H}, {MAX_PREFILL_ROWS, 2 * d, d}};
+  size_t mx = 0;
+  for (const S3& s : shapes) {
+    GemmPlan p = plan_gemm(s.N, s.K, c.dtype);
+    if (p.S > 1) mx = std::max(mx, (size_t)p.S * s.M * s.N * 4);
+  }
+  EmbedPlan e = plan_embed(c.V, c.d, c.dtype);
+  mx = std::max(mx, (size_t)e.S * Mb * d * 4);
+  return mx;
+}
+
+Layout make_layout(const fm_config& c) {
+  Layout L{};
+  const size_t es = esize(c.dtype);
+  const size_t d = c.d, F = (size_t)c.mlp_mult * c.d, Mb = max_rows(c), hd = c.d / c.n_heads;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align256(off + std::max<size_t>(bytes, 1));
+    return o;
+  };
+  L.cache = take((size_t)c.L * c.C_max * 2 * d * es);
+  L.mods = take((size_t)c.max_steps * (6 * c.L + 2) * d * 4);
+  L.sched = take(((size_t)2 * c.max_steps * 256 + 3 * (size_t)c.max_steps * d) * 4);
+  L.h = take(Mb * d * 4);
+  L.e_state = take(Mb * d * 4);
+  L.u_pre = take((size_t)std::max(MAX_PREFILL_ROWS, c.max_new) * d * 4);
+  L.act_qkv = take((Mb + std::max(MAX_PREFILL_ROWS, c.max_new)) * d * es);
+  L.act_d = take(Mb * d * es);
+  L.attn_o = take(Mb * d * es);
+  L.act_f = take(Mb * F * es);
+  L.qkv = take(Mb * 3 * d * es);
+  L.att_po = take((size_t)c.max_branches * c.n_heads * max_chunks(c) * KB * hd * 4);
+  L.att_ml = take((size_t)c.max_branches * c.n_heads * max_chunks(c) * KB * 2 * 4);
+  L.partial = take(partial_bytes(c));
+  L.lm_part = take((size_t)LM_GRID * Mb * 8);
+  L.counters = take((size_t)N_COUNTERS * 4);
+  if (c.max_steps > 1) {
+    L.dsoft = take(Mb * (size_t)c.V * es);
+    L.logits_tmp = take(Mb * (size_t)c.V * 4);
+    L.sm_part = take(Mb * (size_t)cdiv(c.V, SOFTMAX_CHUNK) * 2 * 4);
+  }
+  L.total = off;
+  return L;
+}
+
+fm_status check_config(const fm_config* c) {
+  if (!c) return fail(FM_EINVAL, "config is NULL");
+  if (c->dtype != FM_BF16 && c->dtype != FM_F32) return fail(FM_EINVAL, "dtype must be FM_BF16 or FM_F32");
+  const int ve = vec_elems(c->dtype);
+  if (c->K != KB) return fail(FM_EINVAL, "K must be 16 (got %d)", c->K);
+  if (c->d < 16 * ve || c->d % (16 * ve))
+    return fail(FM_EINVAL, "d must be a positive multiple of %d (got %d)", 16 * ve, c->d);
+  if (c->n_heads < 1 || c->d % c->n_heads) return fail(FM_EINVAL, "n_heads must divide d");
+  const int hd = c->d / c->n_heads;
+  if (hd != 64 && hd != 128) return fail(FM_EINVAL, "head width d/n_heads must be 64 or 128 (got %d)", hd);
+  if (c->d > 4096) return fail(FM_EINVAL, "d above 4096 is not supported (got %d)", c->d);
+  if (c->L < 1) return fail(FM_EINVAL, "L must be >= 1");
+  if (c->mlp_mult < 1) return fail(FM_EINVAL, "mlp_mult must be >= 1");
+  if (c->n_ctx_layers != 5) return fail(FM_EINVAL, "n_ctx_layers must be 5 (layers 1, 9, 17, 25, 33)");
+  if (c->V < 16 || c->V % ve) return fail(FM_EINVAL, "V must be >= 16 and a multiple of %d (got %d)", ve, c->V);
+  if (c->H < 1 || c->H % ve) return fail(FM_EINVAL, "H must be a positive multiple of %d (got %d)", ve, c->H);
+  if (c->C_max < 0) return fail(FM_EINVAL, "C_max must be >= 0");
+  if (c->max_branches < 1 || c->max_branches > 4) return fail(FM_EINVAL, "max_branches must be in 1..4");
+  if (c->max_new < 0 || c->max_new > 16) return fail(FM_EINVAL, "max_new must be in 0..16");
+  if (c->max_steps < 1 || c->max_steps > 4) return fail(FM_EINVAL, "max_steps must be in 1..4");
+  return FM_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+}  // namespace
+
+struct fm_handle {
+  fm_config cfg;
+  int device;
+  char* ws;
+  Layout lay;
+  fm_weights w;
+  std::vector<fm_block_weights> blocks;
+  bool has_weights = false;
+  int n_steps = 0;
+  float times[8];
+  int ctx_len = 0;
+  int ctx_high = 0;  // rows [0, ctx_high) have been written at least once
+
+  template <typename P> P* at(size_t off) { return reinterpret_cast<P*>(ws + off); }
+};
+
+namespace {
+
+// ------------------------------------------------------------------ launchers
+template <typename T, int MT, int EPI>
+void launch_gemm_mt(const GemmArgs& a, const EpiParams& e, int grid, hipStream_t st) {
+  constexpr int U = sizeof(T) == 2 ? 8 : 4;
+  hipLaunchKernelGGL((gemm_nt_kernel<T, MT, 1, U, GEMM_WAVES, EPI>), dim3(grid), dim3(GEMM_WAVES * 64), 0, st, a,
+                     e);
+}
+
+template <typename T, int EPI>
+fm_status launch_gemm_epi(const GemmArgs& a, const EpiParams& e, int grid, hipStream_t st) {
+  switch (cdiv(a.M, 16)) {
+    case 1: launch_gemm_mt<T, 1, EPI>(a, e, grid, st); break;
+    case 2: launch_gemm_mt<T, 2, EPI>(a, e, grid, st); break;
+    case 3: launch_gemm_mt<T, 3, EPI>(a, e, grid, st); break;
+    case 4: launch_gemm_mt<T, 4, EPI>(a, e, grid, st); break;
+    case 5: launch_gemm_mt<T, 5, EPI>(a, e, grid, st); break;
+    default: return fail(FM_EINVAL, "contraction with %d rows exceeds 80", a.M);
+  }
+  FM_LAUNCHED("gemm_nt_kernel");
+  return FM_OK;
+}
+
+// out[m][n] = epilogue( sum_k A[m][k] W[n][k] )
+template <typename T>
+fm_status gemm(fm_handle* h, int epi, const void* A, int lda, int M, const void* W, int N, int K,
+               const EpiParams& e, hipStream_t st) {
+  if (M <= 0) return FM_OK;
+  GemmPlan p = plan_gemm(N, K, h->cfg.dtype);
+  if (p.n_groups > N_COUNTERS) return fail(FM_EINVAL, "too many column groups");
+  GemmArgs a;
+  a.A = A;
+  a.lda = lda;
+  a.M = M;
+  a.W = W;
+  a.ldw = K;
+  a.N = N;
+  a.K = K;
+  a.S = p.S;
+  a.k_split = p.k_split;
+  a.partial = h->at<float>(h->lay.partial);
+  a.counters = h->at<uint32_t>(h->lay.counters);
+  switch (epi) {
+    case EPI_F32: return launch_gemm_epi<T, EPI_F32>(a, e, p.grid, st);
+    case EPI_ACT: return launch_gemm_epi<T, EPI_ACT>(a, e, p.grid, st);
+    case EPI_GELU: return launch_gemm_epi<T, EPI_GELU>(a, e, p.grid, st);
+    case EPI_RESID: return launch_gemm_epi<T, EPI_RESID>(a, e, p.grid, st);
+    default: return launch_gemm_epi<T, EPI_QKV>(a, e, p.grid, st);
+  }
+}
+
+template <typename T>
+fm_status ln_mod(fm_handle* h, const float* x, int rows, const float* shift, const float* scale, T* out, int ldo,
+                 hipStream_t st) {
+  if (rows <= 0) return FM_OK;
+  const int d = h->cfg.d;
+  if (d <= 1024)
+    hipLaunchKernelGGL((ln_mod_kernel<T, 4>), dim3(rows), dim3(256), 0, st, x, d, d, shift, scale, out, ldo, 1e-6f);
+  else if (d <= 2048)
+    hipLaunchKernelGGL((ln_mod_kernel<T, 8>), dim3(rows), dim3(256), 0, st, x, d, d, shift, scale, out, ldo, 1e-6f);
+  else
+    hipLaunchKernelGGL((ln_mod_kernel<T, 16>), dim3(rows), dim3(256), 0, st, x, d, d, shift, scale, out, ldo,
+                       1e-6f);
+  FM_LAUNCHED("ln_mod_kernel");
+  return FM_OK;
+}
+
+template <typename T>
+fm_status embed(fm_handle* h, const void* x, int ldx, int M, float alpha, float beta, hipStream_t st) {
+  const fm_config& c = h->cfg;
+  EmbedPlan p = plan_embed(c.V, c.d, c.dtype);
+  EmbedArgs a;
+  a.x = x;
+  a.ldx = ldx;
+  a.M = M;
+  a.V = c.V;
+  a.E = h->w.E;
+  a.d = c.d;
+  a.S = p.S;
+  a.rows_split = p.rows_split;
+  a.partial = h->at<float>(h->lay.partial);
+  a.counters = h->at<uint32_t>(h->lay.counters);
+  a.e_state = h->at<float>(h->lay.e_state);
+  a.h = h->at<float>(h->lay.h);
+  a.alpha = alpha;
+  a.beta = beta;
+  a.K = KB;
+  a.use_pos = 1;
+  switch (cdiv(M, 16)) {
+    case 1: hipLaunchKernelGGL((embed_kernel<T, 1, EMB_WAVES>), dim3(p.grid), dim3(EMB_WAVES * 64), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((embed_kernel<T, 2, EMB_WAVES>), dim3(p.grid), dim3(EMB_WAVES * 64), 0, st, a); break;
+    case 3: hipLaunchKernelGGL((embed_kernel<T, 3, EMB_WAVES>), dim3(p.grid), dim3(EMB_WAVES * 64), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((embed_kernel<T, 4, EMB_WAVES>), dim3(p.grid), dim3(EMB_WAVES * 64), 0, st, a); break;
+    default: return fail(FM_EINVAL, "embedding contraction with %d rows exceeds 64", M);
+  }
+  FM_LAUNCHED("embed_kernel");
+  return FM_OK;
+}
+
+template <typename T>
+fm_status attention(fm_handle* h, int l, int B, int C, hipStream_t st) {
+  const fm_config& c = h->cfg;
+  const int hd = c.d / c.n_heads;
+  AttnArgs a;
+  a.qkv = h->at<T>(h->lay.qkv);
+  a.ld_qkv = 3 * c.d;
+  a.cache = h->at<T>(h->lay.cache) + (size_t)l * c.C_max * 2 * c.d;
+  a.C = C;
+  a.K = KB;
+  a.d = c.d;
+  a.nh = c.n_heads;
+  a.n_chunks = cdiv(C + KB, ATT_CH);
+  a.part_o = h->at<float>(h->lay.att_po);
+  a.part_ml = h->at<float>(h->lay.att_ml);
+  a.counters = h->at<uint32_t>(h->lay.counters);
+  a.out = h->at<T>(h->lay.attn_o);
+  a.scale = 1.0f / std::sqrt((float)hd);
+  const int grid = B * c.n_heads * a.n_chunks;
+  if (hd == 128)
+    hipLaunchKernelGGL((attention_kernel<T, 128, ATT_CH>), dim3(grid), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((attention_kernel<T, 64, ATT_CH>), dim3(grid), dim3(256), 0, st, a);
+  FM_LAUNCHED("attention_kernel");
+  return FM_OK;
+}
+
+template <typename T>
+fm_status lm_head(fm_handle* h, const void* z, int M, float* logits, int32_t* tokens, hipStream_t st) {
+  const fm_config& c = h->cfg;
+  LmArgs a;
+  a.z = z;
+  a.M = M;
+  a.d = c.d;
+  a.W = h->w.W_lm;
+  a.V = c.V;
+  a.logits = logits;
+  a.partial = h->at<uint64_t>(h->lay.lm_part);
+  a.counter = h->at<uint32_t>(h->lay.counters);
+  a.tokens = tokens;
+  constexpr int U = sizeof(T) == 2 ? 8 : 4;
+  const int grid = std::min(LM_GRID, cdiv(cdiv(c.V, 16), LM_WAVES));
+  switch (cdiv(M, 16)) {
+    case 1: hipLaunchKernelGGL((lmhead_kernel<T, 1, 1, U, LM_WAVES>), dim3(grid), dim3(LM_WAVES * 64), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((lmhead_kernel<T, 2, 1, U, LM_WAVES>), dim3(grid), dim3(LM_WAVES * 64), 0, st, a); break;
+    case 3: hipLaunchKernelGGL((lmhead_kernel<T, 3, 1, U, LM_WAVES>), dim3(grid), dim3(LM_WAVES * 64), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((lmhead_kernel<T, 4, 1, U, LM_WAVES>), dim3(grid), dim3(LM_WAVES * 64), 0, st, a); break;
+    default: return fail(FM_EINVAL, "LM head with %d rows exceeds 64", M);
+  }
+  FM_LAUNCHED("lmhead_kernel");
+  return FM_OK;
+}
+
+template <typename T>
+fm_status softmax_rows(fm_handle* h, int M, hipStream_t st) {
+  const fm_config& c = h->cfg;
+  SoftmaxArgs a;
+  a.logits = h->at<float>(h->lay.logits_tmp);
+  a.V = c.V;
+  a.n_chunks = cdiv(c.V, SOFTMAX_CHUNK);
+  a.part = h->at<float>(h->lay.sm_part);
+  a.counters = nullptr;
+  a.out = h->at<T>(h->lay.dsoft);
+  hipLaunchKernelGGL((softmax_stats_kernel<SOFTMAX_CHUNK>), dim3(M * a.n_chunks), dim3(256), 0, st, a);
+  FM_LAUNCHED("softmax_stats_kernel");
+  hipLaunchKernelGGL((softmax_write_kernel<T, SOFTMAX_CHUNK>), dim3(M * a.n_chunks), dim3(256), 0, st, a);
+  FM_LAUNCHED("softmax_write_kernel");
+  return FM_OK;
+}
+
+fm_status trace_copy(const float* src, float* dst, size_t n, hipStream_t st) {
+  hipLaunchKernelGGL(copy_f32_kernel, dim3((unsigned)std::min<size_t>(1024, (n + 255) / 256)), dim3(256), 0, st, src,
+                     dst, n);
+  FM_LAUNCHED("copy_f32_kernel");
+  return FM_OK;
+}
+
+const void* blk(const fm_handle* h, int l, int which) {
+  const fm_block_weights& b = h->blocks[l];
+  const void* const p[] = {b.W_ada, b.b_ada, b.W_qkv, b.b_qkv, b.W_o, b.b_o, b.W_1, b.b_1, b.W_2, b.b_2};
+  return p[which];
+}
+enum { B_WADA, B_BADA, B_WQKV, B_BQKV, B_WO, B_BO, B_W1, B_B1, B_W2, B_B2 };
+
+template <typename T>
+const void* offset_rows(const void* p, size_t elems) {
+  return reinterpret_cast<const T*>(p) + elems;
+}
+
+// u rows (fusion + LN) for n context rows, written to out (storage type)
+template <typename T>
+fm_status fuse_rows(fm_handle* h, const void* feats, int n, T* out, hipStream_t st) {
+  const fm_config& c = h->cfg;
+  const int K5 = c.n_ctx_layers * c.H;
+  EpiParams e{};
+  e.bias = h->w.b_f;
+  e.out_f32 = h->at<float>(h->lay.u_pre);
+  e.ld_f32 = c.d;
+  FM_TRY(gemm<T>(h, EPI_F32, feats, K5, n, h->w.W_f, c.d, K5, e, st));
+  return ln_mod<T>(h, h->at<float>(h->lay.u_pre), n, nullptr, nullptr, out, c.d, st);
+}
+
+template <typename T>
+fm_status context_append_impl(fm_handle* h, const void* feats, int n, hipStream_t st) {
+  const fm_config& c = h->cfg;
+  const int K5 = c.n_ctx_layers * c.H;
+  T* stage = h->at<T>(h->lay.act_qkv);
+  for (int r0 = 0; r0 < n; r0 += MAX_PREFILL_ROWS) {
+    const int rows = std::min(MAX_PREFILL_ROWS, n - r0);
+    const void* f = reinterpret_cast<const T*>(feats) + (size_t)r0 * K5;
+    FM_TRY(fuse_rows<T>(h, f, rows, stage, st));
+    for (int l = 0; l < c.L; ++l) {
+      EpiParams e{};
+      e.bias = offset_rows<T>(blk(h, l, B_BQKV), c.d);
+      e.rows_block = 0;
+      e.cache = h->at<T>(h->lay.cache) + (size_t)l * c.C_max * 2 * c.d;
+      e.cache_pos0 = h->ctx_len + r0;
+      e.d = c.d;
+      e.col_offset = c.d;
+      FM_TRY(gemm<T>(h, EPI_QKV, stage, c.d, rows, offset_rows<T>(blk(h, l, B_WQKV), (size_t)c.d * c.d), 2 * c.d,
+                     c.d, e, st));
+    }
+  }
+  return FM_OK;
+}
+
+template <typename T>
+fm_status draft_impl(fm_handle* h, const void* noise, int B, const void* new_feats, int n_new, int32_t* tokens,
+                     float* logits, float* hidden, hipStream_t st) {
+  const fm_config& c = h->cfg;
+  const int d = c.d, F = c.mlp_mult * c.d, Mb = B * KB, L = c.L;
+  const int C = h->ctx_len + n_new;
+  T* act_qkv = h->at<T>(h->lay.act_qkv);
+  T* act_d = h->at<T>(h->lay.act_d);
+  T* act_f = h->at<T>(h->lay.act_f);
+  T* attn_o = h->at<T>(h->lay.attn_o);
+  T* qkv = h->at<T>(h->lay.qkv);
+  float* hres = h->at<float>(h->lay.h);
+  const float* mods_all = h->at<float>(h->lay.mods);
+
+  // context rows appended in this step: u goes below the block rows of act_qkv
+  if (n_new > 0) FM_TRY(fuse_rows<T>(h, new_feats, n_new, act_qkv + (size_t)Mb * d, st));
+
+  for (int j = 0; j < h->n_steps; ++j) {
+    const float s = h->times[j], t = h->times[j + 1];
+    const float* mods = mods_all + (size_t)j * (6 * L + 2) * d;
+    if (j == 0) {
+      FM_TRY(embed<T>(h, noise, c.V, Mb, 0.f, 1.f, st));
+    } else {
+      const float sp = h->times[j - 1];
+      FM_TRY(embed<T>(h, h->at<T>(h->lay.dsoft), c.V, Mb, (1.f - s) / (1.f - sp), (s - sp) / (1.f - sp), st));
+    }
+    if (hidden) FM_TRY(trace_copy(hres, hidden + ((size_t)j * (L + 1)) * Mb * d, (size_t)Mb * d, st));
+    const int m_qkv = Mb + (j == 0 ? n_new : 0);
+    for (int l = 0; l < L; ++l) {
+      const float* mv = mods + (size_t)6 * l * d;  // shift1 scale1 gate1 shift2 scale2 gate2
+      FM_TRY(ln_mod<T>(h, hres, Mb, mv + 0 * d, mv + 1 * d, act_qkv, d, st));
+      {
+        EpiParams e{};
+        e.bias = blk(h, l, B_BQKV);
+        e.out_act = qkv;
+        e.ld_act = 3 * d;
+        e.rows_block = Mb;
+        e.cache = h->at<T>(h->lay.cache) + (size_t)l * c.C_max * 2 * d;
+        e.cache_pos0 = h->ctx_len;
+        e.d = d;
+        e.col_offset = 0;
+        FM_TRY(gemm<T>(h, EPI_QKV, act_qkv, d, m_qkv, blk(h, l, B_WQKV), 3 * d, d, e, st));
+      }
+      FM_TRY(attention<T>(h, l, B, C, st));
+      {
+        EpiParams e{};
+        e.bias = blk(h, l, B_BO);
+        e.out_f32 = hres;
+        e.ld_f32 = d;
+        e.gate = mv + 2 * d;
+        FM_TRY(gemm<T>(h, EPI_RESID, attn_o, d, Mb, blk(h, l, B_WO), d, d, e, st));
+      }
+      FM_TRY(ln_mod<T>(h, hres, Mb, mv + 3 * d, mv + 4 * d, act_d, d, st));
+      {
+        EpiParams e{};
+        e.bias = blk(h, l, B_B1);
+        e.out_act = act_f;
+        e.ld_act = F;
+        FM_TRY(gemm<T>(h, EPI_GELU, act_d, d, Mb, blk(h, l, B_W1), F, d, e, st));
+      }
+      {
+        EpiParams e{};
+        e.bias = blk(h, l, B_B2);
+        e.out_f32 = hres;
+        e.ld_f32 = d;
+        e.gate = mv + 5 * d;
+        FM_TRY(gemm<T>(h, EPI_RESID, act_f, F, Mb, blk(h, l, B_W2), d, F, e, st));
+      }
+      if (hidden) FM_TRY(trace_copy(hres, hidden + ((size_t)j * (L + 1) + l + 1) * Mb * d, (size_t)Mb * d, st));
+    }
+    const float* fin = mods + (size_t)6 * L * d;  // shift_f, scale_f
+    FM_TRY(ln_mod<T>(h, hres, Mb, fin, fin + d, act_d, d, st));
+    if (t == 1.f) {
+      FM_TRY(lm_head<T>(h, act_d, Mb, logits, tokens, st));
+    } else {
+      FM_TRY(lm_head<T>(h, act_d, Mb, h->at<float>(h->lay.logits_tmp), nullptr, st));
+      FM_TRY(softmax_rows<T>(h, Mb, st));
+    }
+  }
+  return FM_OK;
+}
+
+template <typename T>
+fm_status schedule_impl(fm_handle* h, int n_jumps, hipStream_t st) {
+  const fm_config& c = h->cfg;
+  const int d = c.d, L = c.L;
+  float* feats = h->at<float>(h->lay.sched);             // [2*n][256]: feat(s_j), feat(t_j)
+  float* hid_s = feats + (size_t)2 * c.max_steps * 256;  // [n][d]
+  float* hid_t = hid_s + (size_t)c.max_steps * d;        // [n][d]
+  float* cvec = hid_t + (size_t)c.max_steps * d;         // [n][d]
+  float* mods = h->at<float>(h->lay.mods);               // [n][6L+2][d]
+  for (int j = 0; j < n_jumps; ++j)
+    for (int which = 0; which < 2; ++which) {
+      hipLaunchKernelGGL(time_features_kernel, dim3(1), dim3(128), 0, st, h->times[j + which],
+                         feats + (size_t)(2 * j + which) * 256);
+      FM_LAUNCHED("time_features_kernel");
+    }
+  auto gv = [&](const float* in, int ldi, const void* Wp, const void* bp, int N, int K, float* out, int ldo,
+                int in_silu, int out_silu, int acc) -> fm_status {
+    hipLaunchKernelGGL((gemv_kernel<T>), dim3(cdiv(N, 4)), dim3(256), 0, st, in, ldi, n_jumps,
+                       reinterpret_cast<const T*>(Wp), reinterpret_cast<const T*>(bp), N, K, out, ldo, in_silu,
+                       out_silu, acc);
+    FM_LAUNCHED("gemv_kernel");
+    return FM_OK;
+  };
+  FM_TRY(gv(feats, 512, h->w.te_s_W1, h->w.te_s_b1, d, 256, hid_s, d, 0, 1, 0));
+  FM_TRY(gv(feats + 256, 512, h->w.te_t_W1, h->w.te_t_b1, d, 256, hid_t, d, 0, 1, 0));
+  FM_TRY(gv(hid_s, d, h->w.te_s_W2, h->w.te_s_b2, d, d, cvec, d, 0, 0, 0));
+  FM_TRY(gv(hid_t, d, h->w.te_t_W2, h->w.te_t_b2, d, d, cvec, d, 0, 0, 1));
+  const int per_jump = (6 * L + 2) * d;
+  for (int l = 0; l < L; ++l)
+    FM_TRY(gv(cvec, d, blk(h, l, B_WADA), blk(h, l, B_BADA), 6 * d, d, mods + (size_t)6 * l * d, per_jump, 1, 0, 0));
+  FM_TRY(gv(cvec, d, h->w.W_fa, h->w.b_fa, 2 * d, d, mods + (size_t)6 * L * d, per_jump, 1, 0, 0));
+  return FM_OK;
+}
+
+template <typename T>
+fm_status verify_impl(const void* tl, int B, int K, int V, const int32_t* draft, int32_t* emitted, int32_t* accept,
+                      int32_t* best, hipStream_t st) {
+  hipLaunchKernelGGL((verify_argmax_kernel<T>), dim3(B * (K + 1)), dim3(1024), 0, st,
+                     reinterpret_cast<const T*>(tl), V, emitted);
+  FM_LAUNCHED("verify_argmax_kernel");
+  hipLaunchKernelGGL(verify_prefix_kernel, dim3(1), dim3(64), 0, st, draft, B, K, emitted, accept, best);
+  FM_LAUNCHED("verify_prefix_kernel");
+  return FM_OK;
+}
+
+fm_status check_weights(const fm_config& c, const fm_weights* w) {
+  if (!w) return fail(FM_EINVAL, "weights struct is NULL");
+  const void* top[] = {w->E, w->W_lm, w->W_f, w->b_f, w->te_s_W1, w->te_s_b1, w->te_s_W2, w->te_s_b2,
+                       w->te_t_W1, w->te_t_b1, w->te_t_W2, w->te_t_b2, w->W_fa, w->b_fa};
+  const char* names[] = {"E", "W_lm", "W_f", "b_f", "te_s_W1", "te_s_b1", "te_s_W2", "te_s_b2",
+                         "te_t_W1", "te_t_b1", "te_t_W2", "te_t_b2", "W_fa", "b_fa"};
+  for (int i = 0; i < 14; ++i) {
+    if (!top[i]) return fail(FM_EINVAL, "weight %s is NULL", names[i]);
+    if (!aligned16(top[i])) return fail(FM_EINVAL, "weight %s is not 16-byte aligned", names[i]);
+  }
+  if (!w->blocks) return fail(FM_EINVAL, "blocks array is NULL");
+  for (int l = 0; l < c.L; ++l) {
+    const fm_block_weights& b = w->blocks[l];
+    const void* p[] = {b.W_ada, b.b_ada, b.W_qkv, b.b_qkv, b.W_o, b.b_o, b.W_1, b.b_1, b.W_2, b.b_2};
+    for (int i = 0; i < 10; ++i) {
+      if (!p[i]) return fail(FM_EINVAL, "block %d weight %d is NULL", l, i);
+      if (!aligned16(p[i])) return fail(FM_EINVAL, "block %d weight %d is not 16-byte aligned", l, i);
+    }
+  }
+  return FM_OK;
+}
+
+}  // namespace
+
+// =================================================================== C ABI
+extern "C" {
+
+size_t fm_workspace_bytes(const fm_config* cfg) {
+  if (check_config(cfg) != FM_OK) return 0;
+  return make_layout(*cfg).total;
+}
+
+fm_status fm_create(const fm_config* cfg, void* workspace, size_t ws_bytes, int device, fm_handle** out) {
+  g_err.clear();
+  FM_TRY(check_config(cfg));
+  if (!out) return fail(FM_EINVAL, "out is NULL");
+  if (!workspace) return fail(FM_EINVAL, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(workspace) & 255) return fail(FM_EINVAL, "workspace is not 256-byte aligned");
+  if (device < 0) return fail(FM_EINVAL, "device must be >= 0");
+  Layout lay = make_layout(*cfg);
+  if (ws_bytes < lay.total)
+    return fail(FM_ECAPACITY, "workspace of %zu bytes is smaller than the %zu bytes needed", ws_bytes, lay.total);
+  fm_handle* h = new fm_handle();
+  h->cfg = *cfg;
+  h->device = device;
+  h->ws = reinterpret_cast<char*>(workspace);
+  h->lay = lay;
+  hipLaunchKernelGGL(zero_u32_kernel, dim3(32), dim3(256), 0, 0, h->at<uint32_t>(lay.counters), (size_t)N_COUNTERS);
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess) e = hipStreamSynchronize(0);
+  if (e != hipSuccess) {
+    delete h;
+    return fail(FM_EHIP, "clearing the workspace counters: %s", hipGetErrorString(e));
+  }
+  *out = h;
+  return FM_OK;
+}
+
+void fm_destroy(fm_handle* h) { delete h; }
+
+fm_status fm_set_weights(fm_handle* h, const fm_weights* w) {
+  g_err.clear();
+  if (!h) return fail(FM_EINVAL, "handle is NULL");
+  FM_TRY(check_weights(h->cfg, w));
+  h->w = *w;
+  h->blocks.assign(w->blocks, w->blocks + h->cfg.L);
+  h->w.blocks = h->blocks.data();
+  h->has_weights = true;
+  return FM_OK;
+}
+
+fm_status fm_set_schedule(fm_handle* h, const float* times, int num_steps, void* stream) {
+  g_err.clear();
+  if (!h) return fail(FM_EINVAL, "handle is NULL");
+  if (!times) return fail(FM_EINVAL, "times is NULL");
+  if (num_steps < 1 || num_steps > h->cfg.max_steps)
+    return fail(FM_EINVAL, "num_steps %d outside 1..%d", num_steps, h->cfg.max_steps);
+  if (times[0] != 0.f || times[num_steps] != 1.f) return fail(FM_EINVAL, "schedule must start at 0 and end at 1");
+  for (int j = 0; j < num_steps; ++j)
+    if (!(times[j + 1] > times[j])) return fail(FM_EINVAL, "schedule must rise strictly");
+  if (!h->has_weights) return fail(FM_ESTATE, "fm_set_schedule before fm_set_weights");
+  for (int j = 0; j <= num_steps; ++j) h->times[j] = times[j];
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  fm_status s = h->cfg.dtype == FM_BF16 ? schedule_impl<bf16_t>(h, num_steps, st) : schedule_impl<float>(h, num_steps, st);
+  if (s == FM_OK) h->n_steps = num_steps;
+  return s;
+}
+
+fm_status fm_context_append(fm_handle* h, const void* feats, int n, void* stream) {
+  g_err.clear();
+  if (!h) return fail(FM_EINVAL, "handle is NULL");
+  if (n < 0) return fail(FM_EINVAL, "n must be >= 0");
+  if (n == 0) return FM_OK;
+  if (!feats) return fail(FM_EINVAL, "feats is NULL");
+  if (!aligned16(feats)) return fail(FM_EINVAL, "feats is not 16-byte aligned");
+  if (!h->has_weights) return fail(FM_ESTATE, "fm_context_append before fm_set_weights");
+  if (h->ctx_len + n > h->cfg.C_max)
+    return fail(FM_ECAPACITY, "context of %d rows + %d exceeds C_max %d", h->ctx_len, n, h->cfg.C_max);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  fm_status s = h->cfg.dtype == FM_BF16 ? context_append_impl<bf16_t>(h, feats, n, st)
+                                        : context_append_impl<float>(h, feats, n, st);
+  if (s == FM_OK) {
+    h->ctx_len += n;
+    h->ctx_high = std::max(h->ctx_high, h->ctx_len);
+  }
+  return s;
+}
+
+fm_status fm_context_truncate(fm_handle* h, int new_len) {
+  g_err.clear();
+  if (!h) return fail(FM_EINVAL, "handle is NULL");
+  if (new_len < 0 || new_len > h->ctx_high)
+    return fail(FM_EINVAL, "new length %d outside 0..%d (rows written so far)", new_len, h->ctx_high);
+  h->ctx_len = new_len;
+  return FM_OK;
+}
+
+int fm_context_length(const fm_handle* h) { return h ? h->ctx_len : -1; }
+
+fm_status fm_draft(fm_handle* h, const void* noise, int B, const void* new_feats, int n_new, int32_t* tokens,
+                   float* logits, float* hidden, void* stream) {
+  g_err.clear();
+  if (!h) return fail(FM_EINVAL, "handle is NULL");
+  const fm_config& c = h->cfg;
+  if (!noise || !tokens) return fail(FM_EINVAL, "noise and tokens must not be NULL");
+  if (!aligned16(noise)) return fail(FM_EINVAL, "noise is not 16-byte aligned");
+  if (B < 1) return fail(FM_EINVAL, "B must be >= 1");
+  if (B > c.max_branches) return fail(FM_ECAPACITY, "B %d exceeds max_branches %d", B, c.max_branches);
+  if (n_new < 0) return fail(FM_EINVAL, "n_new must be >= 0");
+  if (n_new > c.max_new) return fail(FM_ECAPACITY, "n_new %d exceeds max_new %d", n_new, c.max_new);
+  if (n_new > 0 && !new_feats) return fail(FM_EINVAL, "new_feats is NULL with n_new > 0");
+  if (n_new > 0 && !aligned16(new_feats)) return fail(FM_EINVAL, "new_feats is not 16-byte aligned");
+  if (h->ctx_len + n_new > c.C_max)
+    return fail(FM_ECAPACITY, "context of %d rows + %d exceeds C_max %d", h->ctx_len, n_new, c.C_max);
+  if (!h->has_weights) return fail(FM_ESTATE, "fm_draft before fm_set_weights");
+  if (h->n_steps < 1) return fail(FM_ESTATE, "fm_draft before fm_set_schedule");
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  fm_status s = c.dtype == FM_BF16 ? draft_impl<bf16_t>(h, noise, B, new_feats, n_new, tokens, logits, hidden, st)
+                                   : draft_impl<float>(h, noise, B, new_feats, n_new, tokens, logits, hidden, st);
+  if (s == FM_OK) {
+    h->ctx_len += n_new;
+    h->ctx_high = std::max(h->ctx_high, h->ctx_len);
+  }
+  return s;
+}
+
+fm_status fm_verify(const void* target_logits, fm_dtype dtype, int B, int K, int V, const int32_t* draft,
+                    int32_t* emitted, int32_t* accept, int32_t* best, void* stream) {
+  g_err.clear();
+  if (!target_logits || !draft || !emitted || !accept || !best)
+    return fail(FM_EINVAL, "a pointer argument is NULL");
+  if (dtype != FM_BF16 && dtype != FM_F32) return fail(FM_EINVAL, "dtype must be FM_BF16 or FM_F32");
+  if (B < 1 || B > 64) return fail(FM_EINVAL, "B must be in 1..64 (got %d)", B);
+  if (K < 1 || K > 64) return fail(FM_EINVAL, "K must be in 1..64 (got %d)", K);
+  if (V < 1) return fail(FM_EINVAL, "V must be >= 1");
+  if (reinterpret_cast<uintptr_t>(target_logits) % esize(dtype))
+    return fail(FM_EINVAL, "target_logits is not aligned to its element size");
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  return dtype == FM_BF16 ? verify_impl<bf16_t>(target_logits, B, K, V, draft, emitted, accept, best, st)
+                          : verify_impl<float>(target_logits, B, K, V, draft, emitted, accept, best, st);
+}
+
+const char* fm_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

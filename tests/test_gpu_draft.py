@@ -1,0 +1,110 @@
+"""GPU parity of fm_draft against the oracle on small workloads (several tiles
+and ragged tails): tokens exact (near-ties reported), logits and the residual
+stream within the stated norm-wise tolerance."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+fm = pytest.importorskip("step_flow_map_amd")
+from gpu_util import check_draft, make_drafter, run_draft, rowwise_rel_err, to_dev  # noqa: E402
+
+TINY = synth.CONFIGS["tiny"]
+# bf16 with ragged vocabulary (1000 = 62.5 column tiles, 31.25 row chunks) and
+# a context width whose fused length 5*520 = 2600 is not a multiple of the chunk
+SMALL_BF16 = TINY.with_(name="small_bf16", dtype="bf16", V=1000, H=520)
+
+
+def _case(cfg, variant="random", B=1, seed_noise=None):
+    w = synth.make_weights(cfg, variant)
+    feats = synth.make_features(cfg)
+    noise = synth.make_noise(cfg, B)
+    return w, feats, noise
+
+
+@pytest.mark.parametrize("cfg", [TINY, SMALL_BF16], ids=["tiny_f32", "small_bf16"])
+@pytest.mark.parametrize("variant", ["random", "unit_gate", "gate_zero"])
+def test_draft_matches_oracle(cfg, variant):
+    print(f"[draft parity] {cfg.name} {variant}", flush=True)
+    w, feats, noise = _case(cfg, variant)
+    dr = make_drafter(cfg, w)
+    dr.set_schedule(cfg.times)
+    tok, logits, hidden = run_draft(dr, cfg, noise, feats, cfg.c_prefill, want_hidden=True)
+    rel, ties = check_draft(cfg, w, noise, feats, cfg.c_prefill, tok, logits, hidden)
+    print(f"  max row logit error {rel:.2e}, near-ties {ties}")
+    # per-block residual stream
+    W = oracle.Weights.from_storage(w)
+    ref = oracle.draft(W, cfg, noise[0], feats, trace=True)
+    for l, blk in enumerate(ref["jumps"][0]["blocks"]):
+        e = rowwise_rel_err(hidden[0, l + 1, 0], blk["h"])
+        assert e.max() < 2e-2, (l, e.max())
+
+
+def test_context_paths_agree():
+    """All context appended by fm_context_append, all appended inside fm_draft,
+    or split between the two: the same draft.  Truncate + re-append reproduces
+    a fresh build."""
+    cfg = SMALL_BF16
+    w, feats, noise = _case(cfg)
+    dr = make_drafter(cfg, w)
+    dr.set_schedule(cfg.times)
+    t_split, l_split, _ = run_draft(dr, cfg, noise, feats, 24)
+    dr.truncate(0)
+    t_pre, l_pre, _ = run_draft(dr, cfg, noise, feats, 32)
+    dr.truncate(16)
+    dr.append(to_dev(feats[16:32]))                 # re-append rows 16..31
+    t_tail, l_tail, _ = run_draft(dr, cfg, noise, feats[:0], 0)
+    assert np.array_equal(t_split, t_pre) and np.array_equal(t_pre, t_tail)
+    assert np.abs(l_split - l_pre).max() < 1e-2 * np.abs(l_pre).max()
+    assert np.array_equal(l_pre, l_tail)
+    assert dr.context_length == 32
+
+
+def test_empty_context_and_no_new_rows():
+    cfg = SMALL_BF16.with_(c_prefill=0, n_new=0)
+    w, _, noise = _case(cfg)
+    feats = np.zeros((0, 5, cfg.H), dtype=np.uint16)
+    dr = make_drafter(cfg, w, C_max=8)
+    dr.set_schedule(cfg.times)
+    tok, logits, _ = run_draft(dr, cfg, noise, feats, 0)
+    check_draft(cfg, w, noise, feats, 0, tok, logits)
+
+
+def test_bitwise_deterministic():
+    cfg = SMALL_BF16
+    w, feats, noise = _case(cfg)
+    dr = make_drafter(cfg, w)
+    dr.set_schedule(cfg.times)
+    a = run_draft(dr, cfg, noise, feats, cfg.c_prefill)
+    dr.truncate(cfg.c_prefill)
+    x = to_dev(noise)
+    new = to_dev(feats[cfg.c_prefill:])
+    logits = torch.empty(1, cfg.K, cfg.V, device="cuda")
+    tok = dr.draft(x, new_feats=new, logits=logits)
+    torch.cuda.synchronize()
+    assert np.array_equal(a[0], tok.cpu().numpy())
+    assert np.array_equal(a[1], logits.cpu().numpy())
+
+
+def test_errors_enqueue_nothing():
+    cfg = SMALL_BF16
+    w, feats, noise = _case(cfg)
+    dr = make_drafter(cfg, w)
+    x = to_dev(noise)
+    with pytest.raises(fm.FlashMapError) as e:
+        dr.draft(x)                                   # no schedule yet
+    assert e.value.status == fm.FM_ESTATE
+    dr.set_schedule(cfg.times)
+    with pytest.raises(fm.FlashMapError) as e:
+        dr.append(to_dev(synth.make_features(cfg, 40)))   # C_max = 32
+    assert e.value.status == fm.FM_ECAPACITY
+    assert dr.context_length == 0
+    with pytest.raises(fm.FlashMapError):
+        dr.set_schedule((0.0, 0.7, 0.5, 1.0))
+    with pytest.raises(fm.FlashMapError) as e:
+        dr.draft(to_dev(synth.make_noise(cfg, 2)))     # max_branches = 1
+    assert e.value.status == fm.FM_ECAPACITY

@@ -47,7 +47,7 @@ def _torch_forward(cfg, W, noise, feats, s=0.0, t=1.0):
     P = torch.cat([torch.sin(ang), torch.cos(ang)], 1)
     x = torch.from_numpy(oracle.from_storage(noise))
     h = x @ T["E"] + P
-    f = torch.from_numpy(oracle.from_storage(feats)).reshape(feats.shape[0], -1)
+    f = torch.from_numpy(oracle.from_storage(feats)).reshape(feats.shape[0], 5 * cfg.H)
     u = ln(f @ T["W_f"].T + T["b_f"])
     for l in range(cfg.L):
         p = f"blk{l}."
@@ -86,6 +86,19 @@ def test_forward_matches_independent_torch_composition(variant):
     if variant == "unit_gate":
         # blocks contribute at full strength: h moves far from h0
         assert np.abs(out["jumps"][0]["h"] - out["jumps"][0]["h0"]).max() > 0.5
+
+
+def test_empty_context_is_attention_over_the_block_alone():
+    """With no context rows the keys are the block's own rows only."""
+    cfg = TINY
+    w = synth.make_weights(cfg)
+    W = oracle.Weights.from_storage(w)
+    noise = synth.make_noise(cfg)[0]
+    empty = np.zeros((0, 5, cfg.H), dtype=np.float32)
+    out = oracle.draft(W, cfg, noise, empty)
+    ref_logits, ref_h = _torch_forward(cfg, W, noise, empty)
+    assert np.allclose(out["jumps"][0]["h"], ref_h, rtol=0, atol=1e-9)
+    assert np.allclose(out["logits"], ref_logits, rtol=1e-6, atol=1e-6)
 
 
 def test_gate_zero_reduces_to_two_matrix_products(tiny):
