@@ -1,0 +1,284 @@
+#!/usr/bin/env python3
+"""Benchmark one FlashMap drafting step + greedy verify on one MI355X.
+
+A step is fm_draft (one flow-map jump from a 16 x V Gaussian noise block to a
+16-token draft, with 8 new context rows fused in) followed by fm_verify
+against target logits [17][V].  Inputs are seeded synthetic tensors of the
+Qwen3-8B-shaped drafter, resident in HBM before the timed region.  Steps are
+replayed from HIP graphs (one per planted target-logit set) and timed with HIP
+events; the dominant kernel is timed live with events recorded around its
+launch (fm_set_probe).  The CPU oracle is timed on the host beside it.
+
+    python bench.py [--gpus 1] [--steps 500] [--warmup 50] [--config qwen3_8b]
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+METRIC = "draft+verify steps/sec at K=16, batch 1 (Qwen3-8B-shaped); % of HBM peak"
+KERNEL_SOURCES = {"lmhead_kernel": ["lmhead.hpp", "common.hpp"],
+                  "embed_kernel": ["embed.hpp", "common.hpp"]}
+
+
+def alg_bytes(cfg) -> dict:
+    """Algorithmic bytes of one step: every weight read once, the context K/V
+    read once, inputs and outputs once (adaLN vectors are precomputed)."""
+    es = 2 if cfg.dtype == "bf16" else 4
+    d, F, V, L, K, B = cfg.d, cfg.F, cfg.V, cfg.L, cfg.K, cfg.B
+    n = cfg.num_steps
+    Mb = B * K
+    parts = {
+        "E": n * V * d * es,
+        "W_lm": n * V * d * es,
+        "blocks": n * L * ((3 * d * d + d * d + F * d + d * F) + (3 * d + d + F + d)) * es,
+        "fusion": (d * 5 * cfg.H + d) * es,
+        "ctx_kv_read": n * L * cfg.C * 2 * d * es,
+        "ctx_kv_write": L * cfg.n_new * 2 * d * es,
+        "noise": Mb * V * es,
+        "feats": cfg.n_new * 5 * cfg.H * es,
+        "target_logits": B * (K + 1) * V * es,
+        "mod_vectors": n * (6 * L + 2) * d * 4,
+        "softmax_round_trip": (n - 1) * Mb * V * (4 + 4 + es + es),
+    }
+    parts["total"] = sum(parts.values())
+    return parts
+
+
+def kernel_alg_bytes(cfg, kernel: str) -> int:
+    es = 2 if cfg.dtype == "bf16" else 4
+    Mb = cfg.B * cfg.K
+    if kernel == "lmhead_kernel":      # W_lm, z in, tokens out
+        return cfg.V * cfg.d * es + Mb * cfg.d * es + Mb * 4
+    if kernel == "embed_kernel":       # E, x in, e and h out (float32)
+        return cfg.V * cfg.d * es + Mb * cfg.V * es + 2 * Mb * cfg.d * 4
+    raise KeyError(kernel)
+
+
+def source_hash(kernel: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "step_flow_map_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
+    if not os.path.exists(p):
+        return None
+    rec = json.load(open(p))
+    if rec.get("source_hash") != source_hash(kernel):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(cfg, w, noise, feats, T):
+    """Time the oracle (one full draft + verify of the same workload)."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    W = oracle.Weights.from_storage(w)
+    steps = 0
+    t0 = time.perf_counter()
+    while True:   # whole steps until about 10 s of CPU work
+        ref = oracle.draft(W, cfg, noise[0], feats)
+        oracle.verify(T[0], ref["tokens"])
+        steps += 1
+        dt = time.perf_counter() - t0
+        if dt >= 10.0 or steps >= 1000:
+            break
+    del W
+    return ref["tokens"], {
+        "value": steps / dt, "unit": "steps/s", "cores": int(threads), "kind": "oracle",
+        "sample": f"{steps} full {cfg.name} draft+verify steps (the oracle recomputes the "
+                  f"{cfg.C}-row context each step) in {dt:.1f} s",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--config", default="qwen3_8b", choices=sorted(synth.CONFIGS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true", help="time eager calls instead of graph replays")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the drafting step runs on the GPU that holds the "
+              "target (single-GPU build); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import step_flow_map_amd as fm
+
+    def to_dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+    def binding_weights(w):
+        return {k.replace("te_s.", "te_s_").replace("te_t.", "te_t_"): to_dev(v) for k, v in w.items()}
+
+    cfg = synth.CONFIGS[args.config]
+    t_gen = time.perf_counter()
+    w = synth.make_weights(cfg)
+    feats = synth.make_features(cfg)
+    noise = synth.make_noise(cfg)
+    T_raw = synth.make_target_logits(cfg)
+    print(f"[bench] inputs generated in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
+
+    baseline = None
+    ref_tokens = None
+    if not args.no_cpu_baseline:
+        ref_tokens, baseline = cpu_baseline(cfg, w, noise, feats, T_raw)
+        print(f"[bench] oracle {baseline['sample']}", file=sys.stderr, flush=True)
+
+    dev = torch.device("cuda", 0)
+    c = fm.make_config(K=cfg.K, V=cfg.V, d=cfg.d, L=cfg.L, n_heads=cfg.nh, H=cfg.H, C_max=cfg.capacity,
+                       dtype=cfg.dtype, max_branches=cfg.B, max_new=max(cfg.n_new, 1),
+                       max_steps=cfg.num_steps)
+    dr = fm.Drafter(c, binding_weights(w))
+    dr.set_schedule(cfg.times)
+    if cfg.c_prefill:
+        dr.append(to_dev(feats[:cfg.c_prefill]))
+    x = to_dev(noise)
+    new = to_dev(feats[cfg.c_prefill:]) if cfg.n_new else None
+    tokens = torch.empty(cfg.B, cfg.K, dtype=torch.int32, device=dev)
+    emitted = torch.empty(cfg.B, cfg.K + 1, dtype=torch.int32, device=dev)
+    accept = torch.empty(cfg.B, dtype=torch.int32, device=dev)
+    best = torch.empty(1, dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+
+    # draft once to learn the tokens when the oracle did not run
+    dr.truncate(cfg.c_prefill)
+    dr.draft(x, new_feats=new, tokens=tokens)
+    gpu_tokens = tokens.cpu().numpy()
+    plant_from = ref_tokens[None] if ref_tokens is not None else gpu_tokens
+    planted = synth.PLANTED_ACCEPT_TREE if cfg.B > 1 else synth.PLANTED_ACCEPT
+    sets = []
+    if cfg.B > 1:
+        src = np.stack([synth.plant(T_raw[b], gpu_tokens[b], planted[b]) for b in range(cfg.B)])
+        sets.append((to_dev(src), list(planted)))
+    else:
+        for n in planted:
+            sets.append((to_dev(synth.plant(T_raw[0], plant_from[0], n)[None]), [n]))
+
+    def step(T):
+        dr.truncate(cfg.c_prefill)
+        dr.draft(x, new_feats=new, tokens=tokens)
+        fm.fm_verify(T, tokens, emitted, accept, best)
+
+    stream = torch.cuda.current_stream()
+    graphs = []
+    if not args.eager:
+        for T, _ in sets:
+            step(T)   # warm the path outside capture
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            dr.truncate(cfg.c_prefill)
+            with torch.cuda.graph(g):
+                dr.draft(x, new_feats=new, tokens=tokens)
+                fm.fm_verify(T, tokens, emitted, accept, best)
+            graphs.append(g)
+        torch.cuda.synchronize()
+
+    def run(i):
+        if graphs:
+            graphs[i % len(graphs)].replay()
+        else:
+            step(sets[i % len(sets)][0])
+
+    # accept lengths of every planted set (checks the planted workload)
+    accepts = []
+    for i in range(len(sets)):
+        run(i)
+        torch.cuda.synchronize()
+        accepts.append(accept.cpu().numpy().tolist())
+
+    for i in range(args.warmup):
+        run(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        run(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+
+    # live per-kernel durations: events around the kernel's launch, eager calls
+    kernels = {}
+    for name, probe in (("lmhead_kernel", fm.FM_PROBE_LM_HEAD), ("embed_kernel", fm.FM_PROBE_EMBED)):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)   # torch creates the HIP events on first record
+        b.record(stream)
+        torch.cuda.synchronize()
+        fm.fm_set_probe(dr.handle, probe, a, b)
+        durs = []
+        for i in range(20):
+            step(sets[i % len(sets)][0])
+            torch.cuda.synchronize()
+            durs.append(a.elapsed_time(b))
+        fm.fm_set_probe(dr.handle, fm.FM_PROBE_NONE)
+        us = float(np.mean(durs[5:])) * 1e3
+        ab = kernel_alg_bytes(cfg, name)
+        kernels[name] = {"us": us, "alg_bytes": ab, "gbs": ab / us / 1e3}
+    dom = max(kernels, key=lambda k: kernels[k]["us"])
+    kd = kernels[dom]
+    traffic = measured_traffic(dom, cfg.name)
+    ab = alg_bytes(cfg)
+    out = {
+        "metric": METRIC,
+        "value": 1000.0 / ms,
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded random weights ~N(0,0.02), features/noise/target logits ~N(0,1); "
+                "target logits planted for accept lengths 7,7,7,7,7,7,7,6,6,6)",
+        "config": {"workload": cfg.name, "K": cfg.K, "V": cfg.V, "d": cfg.d, "L": cfg.L,
+                   "heads": cfg.nh, "H": cfg.H, "context": cfg.C, "new_rows_per_step": cfg.n_new,
+                   "branches": cfg.B, "schedule": list(cfg.times), "replay": "eager" if args.eager else "hipgraph"},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": kd["gbs"], "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": kd["gbs"] / HBM_PEAK_GBS, "traffic": traffic,
+                     "alg_bytes_per_launch": kd["alg_bytes"], "us_per_launch": kd["us"]},
+        "step_roofline": {"alg_bytes": ab["total"], "achieved_gbs": ab["total"] / ms / 1e6,
+                          "frac": ab["total"] / ms / 1e6 / HBM_PEAK_GBS},
+        "kernels": kernels,
+        "accept": accepts,
+        "tau": float(np.mean([np.mean(a) for a in accepts]) + 1.0),
+        "cpu_baseline": baseline,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

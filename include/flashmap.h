@@ -189,6 +189,22 @@ fm_status fm_verify(const void *target_logits, fm_dtype dtype, int B, int K, int
                     const int32_t *draft, int32_t *emitted, int32_t *accept, int32_t *best,
                     void *stream);
 
+/* Kernels a probe can bracket. */
+typedef enum fm_probe_kernel {
+  FM_PROBE_NONE = 0,
+  FM_PROBE_EMBED = 1,    /* noise-block embedding contraction (first jump)    */
+  FM_PROBE_LM_HEAD = 2,  /* LM head + fused argmax (last jump)                */
+  FM_PROBE_FC1 = 3,      /* first MLP contraction of block 0 (first jump)     */
+  FM_PROBE_VERIFY = 4    /* unused by fm_draft; reserved                      */
+} fm_probe_kernel;
+
+/* Profiling hook.  While set, every fm_draft call on this handle records the
+ * HIP event `ev_start` (a hipEvent_t passed as void*) on its stream right
+ * before launching `kernel` and `ev_stop` right after it, so the caller can
+ * read that kernel's duration with hipEventElapsedTime.  FM_PROBE_NONE clears
+ * the probe.  Events are borrowed.  Errors: FM_EINVAL. */
+fm_status fm_set_probe(fm_handle *h, fm_probe_kernel kernel, void *ev_start, void *ev_stop);
+
 /* Message of the last failed call on this thread ("" if none). */
 const char *fm_last_error(void);
 

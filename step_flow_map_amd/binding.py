@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libflashmap
 
 FM_OK, FM_EINVAL, FM_ECAPACITY, FM_EHIP, FM_ESTATE = range(5)
 FM_BF16, FM_F32 = 0, 1
+FM_PROBE_NONE, FM_PROBE_EMBED, FM_PROBE_LM_HEAD, FM_PROBE_FC1, FM_PROBE_VERIFY = range(5)
 STATUS_NAMES = {0: "FM_OK", 1: "FM_EINVAL", 2: "FM_ECAPACITY", 3: "FM_EHIP", 4: "FM_ESTATE"}
 
 BLOCK_FIELDS = ("W_ada", "b_ada", "W_qkv", "b_qkv", "W_o", "b_o", "W_1", "b_1", "W_2", "b_2")
@@ -77,6 +78,8 @@ def lib() -> ctypes.CDLL:
     L.fm_draft.restype = st
     L.fm_verify.argtypes = [vp, i, i, i, i, vp, vp, vp, vp, vp]
     L.fm_verify.restype = st
+    L.fm_set_probe.argtypes = [vp, i, vp, vp]
+    L.fm_set_probe.restype = st
     L.fm_last_error.argtypes = []
     L.fm_last_error.restype = ctypes.c_char_p
     _lib = L
@@ -185,6 +188,16 @@ def fm_verify(target_logits, draft, emitted, accept, best, stream=None):
     B, K1, V = (int(s) for s in target_logits.shape)
     _check(lib().fm_verify(_ptr(target_logits), dtype_code(target_logits.dtype), B, K1 - 1, V,
                            _ptr(draft), _ptr(emitted), _ptr(accept), _ptr(best), _stream(stream)))
+
+
+def fm_set_probe(h, kernel: int, ev_start=None, ev_stop=None):
+    """ev_start/ev_stop: torch.cuda.Event(enable_timing=True) objects or raw
+    hipEvent_t integers."""
+    def raw(e):
+        if e is None:
+            return ctypes.c_void_p(None)
+        return ctypes.c_void_p(e.cuda_event if hasattr(e, "cuda_event") else int(e))
+    _check(lib().fm_set_probe(h, int(kernel), raw(ev_start), raw(ev_stop)))
 
 
 # ----------------------------------------------------------------- convenience

@@ -205,6 +205,8 @@ struct fm_handle {
   float times[8];
   int ctx_len = 0;
   int ctx_high = 0;  // rows [0, ctx_high) have been written at least once
+  int probe = FM_PROBE_NONE;
+  hipEvent_t probe_start = nullptr, probe_stop = nullptr;
 
   template <typename P> P* at(size_t off) { return reinterpret_cast<P*>(ws + off); }
 };
@@ -386,6 +388,15 @@ fm_status trace_copy(const float* src, float* dst, size_t n, hipStream_t st) {
   return FM_OK;
 }
 
+fm_status probe_begin(fm_handle* h, int kernel, hipStream_t st) {
+  if (h->probe == kernel) FM_HIP(hipEventRecord(h->probe_start, st));
+  return FM_OK;
+}
+fm_status probe_end(fm_handle* h, int kernel, hipStream_t st) {
+  if (h->probe == kernel) FM_HIP(hipEventRecord(h->probe_stop, st));
+  return FM_OK;
+}
+
 const void* blk(const fm_handle* h, int l, int which) {
   const fm_block_weights& b = h->blocks[l];
   const void* const p[] = {b.W_ada, b.b_ada, b.W_qkv, b.b_qkv, b.W_o, b.b_o, b.W_1, b.b_1, b.W_2, b.b_2};
@@ -456,7 +467,9 @@ fm_status draft_impl(fm_handle* h, const void* noise, int B, const void* new_fea
     const float s = h->times[j], t = h->times[j + 1];
     const float* mods = mods_all + (size_t)j * (6 * L + 2) * d;
     if (j == 0) {
+      FM_TRY(probe_begin(h, FM_PROBE_EMBED, st));
       FM_TRY(embed<T>(h, noise, c.V, Mb, 0.f, 1.f, st));
+      FM_TRY(probe_end(h, FM_PROBE_EMBED, st));
     } else {
       const float sp = h->times[j - 1];
       FM_TRY(embed<T>(h, h->at<T>(h->lay.dsoft), c.V, Mb, (1.f - s) / (1.f - sp), (s - sp) / (1.f - sp), st));
@@ -493,7 +506,10 @@ fm_status draft_impl(fm_handle* h, const void* noise, int B, const void* new_fea
         e.bias = blk(h, l, B_B1);
         e.out_act = act_f;
         e.ld_act = F;
+        const int pk = (j == 0 && l == 0) ? FM_PROBE_FC1 : -1;
+        FM_TRY(probe_begin(h, pk, st));
         FM_TRY(gemm<T>(h, EPI_GELU, act_d, d, Mb, blk(h, l, B_W1), F, d, e, st));
+        FM_TRY(probe_end(h, pk, st));
       }
       {
         EpiParams e{};
@@ -508,7 +524,9 @@ fm_status draft_impl(fm_handle* h, const void* noise, int B, const void* new_fea
     const float* fin = mods + (size_t)6 * L * d;  // shift_f, scale_f
     FM_TRY(ln_mod<T>(h, hres, Mb, fin, fin + d, act_d, d, st));
     if (t == 1.f) {
+      FM_TRY(probe_begin(h, FM_PROBE_LM_HEAD, st));
       FM_TRY(lm_head<T>(h, act_d, Mb, logits, tokens, st));
+      FM_TRY(probe_end(h, FM_PROBE_LM_HEAD, st));
     } else {
       FM_TRY(lm_head<T>(h, act_d, Mb, h->at<float>(h->lay.logits_tmp), nullptr, st));
       FM_TRY(softmax_rows<T>(h, Mb, st));
@@ -722,6 +740,17 @@ fm_status fm_verify(const void* target_logits, fm_dtype dtype, int B, int K, int
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   return dtype == FM_BF16 ? verify_impl<bf16_t>(target_logits, B, K, V, draft, emitted, accept, best, st)
                           : verify_impl<float>(target_logits, B, K, V, draft, emitted, accept, best, st);
+}
+
+fm_status fm_set_probe(fm_handle* h, fm_probe_kernel kernel, void* ev_start, void* ev_stop) {
+  g_err.clear();
+  if (!h) return fail(FM_EINVAL, "handle is NULL");
+  if (kernel < FM_PROBE_NONE || kernel > FM_PROBE_VERIFY) return fail(FM_EINVAL, "unknown probe kernel %d", (int)kernel);
+  if (kernel != FM_PROBE_NONE && (!ev_start || !ev_stop)) return fail(FM_EINVAL, "probe events are NULL");
+  h->probe = kernel;
+  h->probe_start = reinterpret_cast<hipEvent_t>(ev_start);
+  h->probe_stop = reinterpret_cast<hipEvent_t>(ev_stop);
+  return FM_OK;
 }
 
 const char* fm_last_error(void) { return g_err.c_str(); }
