@@ -137,24 +137,48 @@ __device__ __forceinline__ float warp_max(float v) {
 }
 
 // ------------------------------------------------------- cross-workgroup sync
-// The last of `expected` workgroups to arrive on `counter` returns true; it
-// resets the counter so the next launch finds it at zero.  Every wave issues
-// an agent-scope release fence (its own stores drain and the XCD's L2 is
-// written back) before the arrival, and the last block issues an acquire
-// fence (stale L2/L1 lines are invalidated) before reading other blocks' data.
-__device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t expected, int* lds_flag) {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+// Data one workgroup hands to another inside a launch is written with
+// device-coherent stores and read with device-coherent loads (agent-scope
+// relaxed atomics: they write through / bypass the XCD-local L2), so no L2
+// writeback or invalidate is needed.  arrive() waits until this workgroup's
+// coherent stores are acknowledged, then bumps `counter`; the workgroup that
+// brings it to `expected` gets true and resets it to zero for the next launch.
+// A device-scope atomic on one address costs a few hundred ns and serialises,
+// so every counter is given only a handful of arrivals.
+__device__ __forceinline__ void st_coh(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_coh(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_coh(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_coh(const uint64_t* p) {
+  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ bool arrive(uint32_t* counter, uint32_t expected, int* lds_flag) {
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): coherent stores acknowledged
   __syncthreads();
   if (threadIdx.x == 0) {
-    uint32_t old = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    int last = (old == expected - 1);
+    const uint32_t old = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int last = old == expected - 1;
     if (last) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     *lds_flag = last;
   }
   __syncthreads();
-  bool last = *lds_flag != 0;
-  if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  return last;
+  return *lds_flag != 0;
+}
+
+// counters live 32 words (128 bytes) apart so contended lines never share
+constexpr int COUNTER_STRIDE = 32;
+
+// compiler barrier + LDS ordering point inside one wave
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 __device__ __forceinline__ float gelu_tanh(float x) {

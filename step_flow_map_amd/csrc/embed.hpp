@@ -7,30 +7,35 @@
 // the denoiser's softmax before a later jump), E the frozen embedding [V][d]
 // stored one row per token.  The reduction runs over E's rows, which are
 // contiguous along c, so a lane loads a VE x VE block (VE rows, VE adjacent
-// columns, one 16-byte load per row) and transposes it in registers into VE
-// MFMA B operands, one per column; E is read exactly once with fully used
-// 16-byte loads and no LDS round trip.
+// columns, one 16-byte load per row; every load instruction covers four rows x
+// 256 contiguous bytes) and transposes it in registers into VE MFMA B
+// operands, one per column; E is read exactly once.
 //
 // Work split: a wave covers 16*VE columns; a workgroup's waves take
-// interleaved 4*VE-row chunks of one row range (a deterministic split of V);
-// partials are reduced in fixed order by the last workgroup of each column
-// block.  Workgroups that read the same x rows (same split) are placed on the
-// same XCD (the hardware deals workgroups round-robin over the 8 XCDs), so x
-// is fetched once per XCD.
+// interleaved 4*VE-row chunks (next chunk in flight) of one row range.  The
+// S = S1*S2 row splits of a column block reduce in two levels of at most a few
+// arrivals each (a device-scope counter with many arrivals serialises): the
+// last of each group of S1 splits sums their partials, the last of the S2
+// groups sums the group sums, in order, and writes e and h.  Workgroups that
+// read the same x rows are placed on the same XCD (the hardware deals
+// workgroups round-robin over the 8 XCDs), so x is fetched once per XCD.
 #pragma once
 #include "common.hpp"
 
 namespace fm {
+
+constexpr int EMB_LEVEL_MAX = 4;  // splits per group and groups per column block
 
 struct EmbedArgs {
   const void* x;      // [M][ldx]
   int ldx, M, V;
   const void* E;      // [V][d]
   int d;
-  int S;              // splits of V (multiple of 8)
+  int S1, S2;         // splits of V: S = S1*S2 (multiple of 8), groups of S1
   int rows_split;     // rows of V per split (multiple of 4*VE)
   float* partial;     // [S][M][d]
-  uint32_t* counters; // one per column block
+  float* gpartial;    // [S2][M][d]
+  uint32_t* counters; // n_cb*S2 first-level counters, then n_cb second-level
   float* e_state;     // [M][d] in/out
   float* h;           // [M][d] out
   float alpha, beta;  // alpha == 0: e_state is not read
@@ -48,8 +53,8 @@ __device__ __forceinline__ float pos_table(int k, int c, int d) {
   return c < half ? sinf(a) : cosf(a);
 }
 
-template <typename T, int MT, int WAVES>
-__global__ __launch_bounds__(WAVES * 64) void embed_kernel(EmbedArgs g) {
+template <typename T, int MT, int NW>
+__global__ __launch_bounds__(NW * 64) void embed_kernel(EmbedArgs g) {
   typedef typename Vec<T>::type VT;
   constexpr int VE = Vec<T>::N;
   constexpr int RCH = 4 * VE;   // rows per wave iteration
@@ -61,6 +66,7 @@ __global__ __launch_bounds__(WAVES * 64) void embed_kernel(EmbedArgs g) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int j = lane & 15, grp = lane >> 4;
   const int n_cb = g.d / COLS;
+  const int S = g.S1 * g.S2;
   // XCD-aware placement: blocks bid, bid+8, ... run on one XCD
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
   const int cb = slot % n_cb;
@@ -87,23 +93,46 @@ __global__ __launch_bounds__(WAVES * 64) void embed_kernel(EmbedArgs g) {
   }
   const T* ecol = E + c0 + j * VE;
 
-  for (int v0 = v_begin + wave * RCH; v0 < v_end; v0 += WAVES * RCH) {
-    const int vr = v0 + grp * VE;  // first of this lane's VE rows
-    const bool ok = vr < v_end;    // V and the split are multiples of VE
-    VT in[VE], bt[VE], a[MT];
+  // this lane's VE rows of chunk v0 start at v0 + grp*VE; V and the split are
+  // multiples of VE, so a lane's rows are all in range or all out
+  auto load = [&](VT (&in)[VE], VT (&a)[MT], int v0) {
+    const int vr = v0 + grp * VE;
+    const bool ok = vr < v_end;
+    const int vs = ok ? vr : 0;
 #pragma unroll
-    for (int r = 0; r < VE; ++r) in[r] = ok ? vload<T>(ecol + (size_t)(vr + r) * g.d) : vzero<VT>();
+    for (int r = 0; r < VE; ++r) {
+      const VT v = vload<T>(ecol + (size_t)(vs + r) * g.d);
+      in[r] = ok ? v : vzero<VT>();
+    }
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) a[mt] = (ok && xok[mt]) ? vload<T>(xrow[mt] + vr) : vzero<VT>();
+    for (int mt = 0; mt < MT; ++mt) {
+      const VT v = vload<T>(xrow[mt] + vs);
+      a[mt] = (ok && xok[mt]) ? v : vzero<VT>();
+    }
+  };
+  auto compute = [&](const VT (&in)[VE], const VT (&a)[MT]) {
+    VT bt[VE];
     transpose_block(in, bt);
 #pragma unroll
     for (int t = 0; t < VE; ++t)
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) mma(acc[mt][t], a[mt], bt[t]);
+  };
+
+  VT in0[VE], in1[VE], a0[MT], a1[MT];
+  const int first = v_begin + wave * RCH, step = NW * RCH;
+  if (first < v_end) load(in0, a0, first);
+  for (int v0 = first; v0 < v_end; v0 += 2 * step) {
+    if (v0 + step < v_end) load(in1, a1, v0 + step);
+    compute(in0, a0);
+    if (v0 + step < v_end) {
+      if (v0 + 2 * step < v_end) load(in0, a0, v0 + 2 * step);
+      compute(in1, a1);
+    }
   }
 
   // ---- fixed-order reduction over waves (wave 0 stores, others add in turn)
-  for (int w = 0; w < WAVES; ++w) {
+  for (int w = 0; w < NW; ++w) {
     if (wave == w) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
@@ -117,30 +146,55 @@ __global__ __launch_bounds__(WAVES * 64) void embed_kernel(EmbedArgs g) {
     }
     __syncthreads();
   }
-  constexpr int PER_THREAD = ELEMS / (WAVES * 64);
+  constexpr int PER_THREAD = (ELEMS + NW * 64 - 1) / (NW * 64);
   int em[PER_THREAD], ec[PER_THREAD];
+  float val[PER_THREAD];
 #pragma unroll
   for (int r = 0; r < PER_THREAD; ++r) {
-    const int el = threadIdx.x + r * WAVES * 64;
+    const int el = threadIdx.x + r * NW * 64;
     const int ln = el & 63, q = el >> 6;  // q = (mt*VE + t)*4 + i
     const int i = q & 3, t = (q >> 2) % VE, mt = (q >> 2) / VE;
-    em[r] = mt * 16 + 4 * (ln >> 4) + i;
+    em[r] = el < ELEMS ? mt * 16 + 4 * (ln >> 4) + i : g.M;
     ec[r] = c0 + (ln & 15) * VE + t;
-    if (em[r] < g.M) g.partial[((size_t)s * g.M + em[r]) * g.d + ec[r]] = red[el];
+    val[r] = el < ELEMS ? red[el] : 0.f;
+    if (em[r] < g.M) st_coh(&g.partial[((size_t)s * g.M + em[r]) * g.d + ec[r]], val[r]);
   }
-  if (!arrive_last(&g.counters[cb], (uint32_t)g.S, &flag)) return;
+  // level 1: the last of the S1 splits of this group sums them in order
+  const int grp1 = s / g.S1;
+  if (!arrive(&g.counters[(cb * g.S2 + grp1) * COUNTER_STRIDE], (uint32_t)g.S1, &flag)) return;
+#pragma unroll
+  for (int r = 0; r < PER_THREAD; ++r) {
+    const bool ok = em[r] < g.M;
+    float pv[EMB_LEVEL_MAX];
+#pragma unroll
+    for (int q = 0; q < EMB_LEVEL_MAX; ++q)
+      pv[q] = (ok && q < g.S1) ? ld_coh(&g.partial[((size_t)(grp1 * g.S1 + q) * g.M + em[r]) * g.d + ec[r]]) : 0.f;
+    float v = 0.f;
+#pragma unroll
+    for (int q = 0; q < EMB_LEVEL_MAX; ++q) v += pv[q];
+    if (ok) st_coh(&g.gpartial[((size_t)grp1 * g.M + em[r]) * g.d + ec[r]], v);
+  }
+  // level 2: the last group sums the group sums in order and writes e and h
+  if (!arrive(&g.counters[(n_cb * g.S2 + cb) * COUNTER_STRIDE], (uint32_t)g.S2, &flag)) return;
 #pragma unroll
   for (int r = 0; r < PER_THREAD; ++r) {
     const int m = em[r], c = ec[r];
-    if (m >= g.M) continue;
+    const bool ok = m < g.M;
+    float pv[EMB_LEVEL_MAX];
+#pragma unroll
+    for (int q = 0; q < EMB_LEVEL_MAX; ++q)
+      pv[q] = (ok && q < g.S2) ? ld_coh(&g.gpartial[((size_t)q * g.M + m) * g.d + c]) : 0.f;
+    if (!ok) continue;
     float v = 0.f;
-    for (int ss = 0; ss < g.S; ++ss) v += g.partial[((size_t)ss * g.M + m) * g.d + c];
+#pragma unroll
+    for (int q = 0; q < EMB_LEVEL_MAX; ++q) v += pv[q];
     const size_t o = (size_t)m * g.d + c;
     float e = g.beta * v;
     if (g.alpha != 0.f) e += g.alpha * g.e_state[o];
     g.e_state[o] = e;
     g.h[o] = e + (g.use_pos ? pos_table(m % g.K, c, g.d) : 0.f);
   }
+  (void)S;
 }
 
 }  // namespace fm

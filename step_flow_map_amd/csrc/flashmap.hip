@@ -20,6 +20,7 @@
 #include "norm.hpp"
 #include "schedule.hpp"
 #include "softmax.hpp"
+#include "stream.hpp"
 #include "verify.hpp"
 
 using namespace fm;
@@ -57,21 +58,22 @@ fm_status fail(fm_status st, const char* fmt, ...) {
   } while (0)
 
 constexpr int KB = 16;             // block rows per branch (K)
-constexpr int ATT_CH = 64;         // keys per attention workgroup
+constexpr int ATT_SUB = 64;        // keys per attention sub-chunk
+constexpr int ATT_MAX_RANGES = ATT_RANGES_MAX;
 constexpr int GEMM_WAVES = 4;
-constexpr int LM_WAVES = 4;
-constexpr int EMB_WAVES = 4;
-constexpr int MAX_PREFILL_ROWS = 16;
 constexpr int GEMM_TARGET_WG = 512;
-constexpr int EMB_TARGET_WG = 1024;
-constexpr int LM_GRID = 512;
-constexpr int N_COUNTERS = 8192;
+constexpr int GEMM_MAX_SPLIT = GEMM_SPLIT_MAX;
+constexpr int LM_WAVES = 8;
+constexpr int LM_GRID = 256;
+constexpr int EMB_WAVES = 8;
+constexpr int EMB_S1 = EMB_LEVEL_MAX, EMB_S2 = EMB_LEVEL_MAX;  // 16 splits of V, two levels of 4
+constexpr int MAX_PREFILL_ROWS = 16;
+constexpr int N_COUNTER_SLOTS = 1024;  // counters, COUNTER_STRIDE words apart
 constexpr int SOFTMAX_CHUNK = 4096;
 
 size_t esize(fm_dtype t) { return t == FM_BF16 ? 2 : 4; }
 int vec_elems(fm_dtype t) { return t == FM_BF16 ? 8 : 4; }
-int gemm_u(fm_dtype t) { return t == FM_BF16 ? 8 : 4; }
-int gemm_chunk(fm_dtype t) { return 4 * gemm_u(t) * vec_elems(t); }
+int gemm_chunk(fm_dtype t) { return 32 * vec_elems(t); }  // k elements per streamed chunk
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 int cdiv(int a, int b) { return (a + b - 1) / b; }
 
@@ -79,13 +81,17 @@ struct GemmPlan {
   int S, k_split, n_groups, grid;
 };
 
+// one workgroup per (16-row tile, k split); splits keep every wave of a
+// workgroup busy and stay within GEMM_MAX_SPLIT arrivals per tile counter
 GemmPlan plan_gemm(int N, int K, fm_dtype t) {
   const int chunk = gemm_chunk(t);
   GemmPlan p;
   p.n_groups = cdiv(N, 16);
-  const int max_s = std::max(1, cdiv(K, chunk));
-  int S = std::min(max_s, std::max(1, cdiv(GEMM_TARGET_WG, p.n_groups)));
-  p.k_split = cdiv(cdiv(K, S), chunk) * chunk;
+  const int nch = std::max(1, cdiv(K, chunk));
+  int S = 1;
+  if (p.n_groups < GEMM_TARGET_WG)
+    S = std::min({GEMM_MAX_SPLIT, cdiv(GEMM_TARGET_WG, p.n_groups), std::max(1, nch / GEMM_WAVES)});
+  p.k_split = cdiv(nch, S) * chunk;
   p.S = cdiv(K, p.k_split);
   p.grid = p.n_groups * p.S;
   return p;
@@ -99,12 +105,22 @@ EmbedPlan plan_embed(int V, int d, fm_dtype t) {
   const int ve = vec_elems(t), rch = 4 * ve;
   EmbedPlan p;
   p.n_cb = d / (16 * ve);
-  int S = cdiv(EMB_TARGET_WG, p.n_cb);
-  S = std::min(S, cdiv(V, rch));
-  S = std::max(8, cdiv(S, 8) * 8);
-  p.rows_split = cdiv(cdiv(V, S), rch) * rch;
-  p.S = S;  // trailing splits may be empty; they still arrive
+  p.S = EMB_S1 * EMB_S2;  // a multiple of 8 (XCD placement); empty splits still arrive
+  p.rows_split = cdiv(cdiv(V, p.S), rch) * rch;
   p.grid = p.n_cb * p.S;
+  return p;
+}
+
+struct AttnPlan {
+  int n_ranges, range_keys;
+};
+
+AttnPlan plan_attention(int total_keys) {
+  AttnPlan p;
+  const int nsub = std::max(1, cdiv(total_keys, ATT_SUB));
+  const int per = cdiv(nsub, std::min(ATT_MAX_RANGES, nsub));
+  p.n_ranges = cdiv(nsub, per);
+  p.range_keys = per * ATT_SUB;
   return p;
 }
 
@@ -114,7 +130,6 @@ struct Layout {
 };
 
 int max_rows(const fm_config& c) { return c.max_branches * KB; }
-int max_chunks(const fm_config& c) { return cdiv(c.C_max + KB, ATT_CH); }
 
 size_t partial_bytes(const fm_config& c) {
   const int Mb = max_rows(c), F = c.mlp_mult * c.d, d = c.d;
@@ -127,7 +142,7 @@ size_t partial_bytes(const fm_config& c) {
     if (p.S > 1) mx = std::max(mx, (size_t)p.S * s.M * s.N * 4);
   }
   EmbedPlan e = plan_embed(c.V, c.d, c.dtype);
-  mx = std::max(mx, (size_t)e.S * Mb * d * 4);
+  mx = std::max(mx, (size_t)(e.S + EMB_S2) * Mb * d * 4);
   return mx;
 }
 
@@ -152,11 +167,11 @@ Layout make_layout(const fm_config& c) {
   L.attn_o = take(Mb * d * es);
   L.act_f = take(Mb * F * es);
   L.qkv = take(Mb * 3 * d * es);
-  L.att_po = take((size_t)c.max_branches * c.n_heads * max_chunks(c) * KB * hd * 4);
-  L.att_ml = take((size_t)c.max_branches * c.n_heads * max_chunks(c) * KB * 2 * 4);
+  L.att_po = take((size_t)c.max_branches * c.n_heads * ATT_MAX_RANGES * KB * hd * 4);
+  L.att_ml = take((size_t)c.max_branches * c.n_heads * ATT_MAX_RANGES * KB * 2 * 4);
   L.partial = take(partial_bytes(c));
   L.lm_part = take((size_t)LM_GRID * Mb * 8);
-  L.counters = take((size_t)N_COUNTERS * 4);
+  L.counters = take((size_t)N_COUNTER_SLOTS * COUNTER_STRIDE * 4);
   if (c.max_steps > 1) {
     L.dsoft = take(Mb * (size_t)c.V * es);
     L.logits_tmp = take(Mb * (size_t)c.V * 4);
@@ -216,9 +231,7 @@ namespace {
 // ------------------------------------------------------------------ launchers
 template <typename T, int MT, int EPI>
 void launch_gemm_mt(const GemmArgs& a, const EpiParams& e, int grid, hipStream_t st) {
-  constexpr int U = sizeof(T) == 2 ? 8 : 4;
-  hipLaunchKernelGGL((gemm_nt_kernel<T, MT, 1, U, GEMM_WAVES, EPI>), dim3(grid), dim3(GEMM_WAVES * 64), 0, st, a,
-                     e);
+  hipLaunchKernelGGL((gemm_kernel<T, MT, GEMM_WAVES, EPI>), dim3(grid), dim3(GEMM_WAVES * 64), 0, st, a, e);
 }
 
 template <typename T, int EPI>
@@ -231,7 +244,7 @@ fm_status launch_gemm_epi(const GemmArgs& a, const EpiParams& e, int grid, hipSt
     case 5: launch_gemm_mt<T, 5, EPI>(a, e, grid, st); break;
     default: return fail(FM_EINVAL, "contraction with %d rows exceeds 80", a.M);
   }
-  FM_LAUNCHED("gemm_nt_kernel");
+  FM_LAUNCHED("gemm_kernel");
   return FM_OK;
 }
 
@@ -241,7 +254,7 @@ fm_status gemm(fm_handle* h, int epi, const void* A, int lda, int M, const void*
                const EpiParams& e, hipStream_t st) {
   if (M <= 0) return FM_OK;
   GemmPlan p = plan_gemm(N, K, h->cfg.dtype);
-  if (p.n_groups > N_COUNTERS) return fail(FM_EINVAL, "too many column groups");
+  if (p.S > 1 && p.n_groups > N_COUNTER_SLOTS) return fail(FM_EINVAL, "too many column tiles for split-K");
   GemmArgs a;
   a.A = A;
   a.lda = lda;
@@ -290,9 +303,11 @@ fm_status embed(fm_handle* h, const void* x, int ldx, int M, float alpha, float 
   a.V = c.V;
   a.E = h->w.E;
   a.d = c.d;
-  a.S = p.S;
+  a.S1 = EMB_S1;
+  a.S2 = EMB_S2;
   a.rows_split = p.rows_split;
   a.partial = h->at<float>(h->lay.partial);
+  a.gpartial = a.partial + (size_t)p.S * M * c.d;
   a.counters = h->at<uint32_t>(h->lay.counters);
   a.e_state = h->at<float>(h->lay.e_state);
   a.h = h->at<float>(h->lay.h);
@@ -300,11 +315,12 @@ fm_status embed(fm_handle* h, const void* x, int ldx, int M, float alpha, float 
   a.beta = beta;
   a.K = KB;
   a.use_pos = 1;
+  const dim3 grid(p.grid), block(EMB_WAVES * 64);
   switch (cdiv(M, 16)) {
-    case 1: hipLaunchKernelGGL((embed_kernel<T, 1, EMB_WAVES>), dim3(p.grid), dim3(EMB_WAVES * 64), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((embed_kernel<T, 2, EMB_WAVES>), dim3(p.grid), dim3(EMB_WAVES * 64), 0, st, a); break;
-    case 3: hipLaunchKernelGGL((embed_kernel<T, 3, EMB_WAVES>), dim3(p.grid), dim3(EMB_WAVES * 64), 0, st, a); break;
-    case 4: hipLaunchKernelGGL((embed_kernel<T, 4, EMB_WAVES>), dim3(p.grid), dim3(EMB_WAVES * 64), 0, st, a); break;
+    case 1: hipLaunchKernelGGL((embed_kernel<T, 1, EMB_WAVES>), grid, block, 0, st, a); break;
+    case 2: hipLaunchKernelGGL((embed_kernel<T, 2, EMB_WAVES>), grid, block, 0, st, a); break;
+    case 3: hipLaunchKernelGGL((embed_kernel<T, 3, EMB_WAVES>), grid, block, 0, st, a); break;
+    case 4: hipLaunchKernelGGL((embed_kernel<T, 4, EMB_WAVES>), grid, block, 0, st, a); break;
     default: return fail(FM_EINVAL, "embedding contraction with %d rows exceeds 64", M);
   }
   FM_LAUNCHED("embed_kernel");
@@ -315,6 +331,7 @@ template <typename T>
 fm_status attention(fm_handle* h, int l, int B, int C, hipStream_t st) {
   const fm_config& c = h->cfg;
   const int hd = c.d / c.n_heads;
+  AttnPlan p = plan_attention(C + KB);
   AttnArgs a;
   a.qkv = h->at<T>(h->lay.qkv);
   a.ld_qkv = 3 * c.d;
@@ -323,17 +340,18 @@ fm_status attention(fm_handle* h, int l, int B, int C, hipStream_t st) {
   a.K = KB;
   a.d = c.d;
   a.nh = c.n_heads;
-  a.n_chunks = cdiv(C + KB, ATT_CH);
+  a.n_ranges = p.n_ranges;
+  a.range_keys = p.range_keys;
   a.part_o = h->at<float>(h->lay.att_po);
   a.part_ml = h->at<float>(h->lay.att_ml);
   a.counters = h->at<uint32_t>(h->lay.counters);
   a.out = h->at<T>(h->lay.attn_o);
   a.scale = 1.0f / std::sqrt((float)hd);
-  const int grid = B * c.n_heads * a.n_chunks;
+  const int grid = B * c.n_heads * p.n_ranges;
   if (hd == 128)
-    hipLaunchKernelGGL((attention_kernel<T, 128, ATT_CH>), dim3(grid), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((attention_kernel<T, 128>), dim3(grid), dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL((attention_kernel<T, 64, ATT_CH>), dim3(grid), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((attention_kernel<T, 64>), dim3(grid), dim3(256), 0, st, a);
   FM_LAUNCHED("attention_kernel");
   return FM_OK;
 }
@@ -349,18 +367,25 @@ fm_status lm_head(fm_handle* h, const void* z, int M, float* logits, int32_t* to
   a.V = c.V;
   a.logits = logits;
   a.partial = h->at<uint64_t>(h->lay.lm_part);
-  a.counter = h->at<uint32_t>(h->lay.counters);
-  a.tokens = tokens;
-  constexpr int U = sizeof(T) == 2 ? 8 : 4;
   const int grid = std::min(LM_GRID, cdiv(cdiv(c.V, 16), LM_WAVES));
-  switch (cdiv(M, 16)) {
-    case 1: hipLaunchKernelGGL((lmhead_kernel<T, 1, 1, U, LM_WAVES>), dim3(grid), dim3(LM_WAVES * 64), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((lmhead_kernel<T, 2, 1, U, LM_WAVES>), dim3(grid), dim3(LM_WAVES * 64), 0, st, a); break;
-    case 3: hipLaunchKernelGGL((lmhead_kernel<T, 3, 1, U, LM_WAVES>), dim3(grid), dim3(LM_WAVES * 64), 0, st, a); break;
-    case 4: hipLaunchKernelGGL((lmhead_kernel<T, 4, 1, U, LM_WAVES>), dim3(grid), dim3(LM_WAVES * 64), 0, st, a); break;
-    default: return fail(FM_EINVAL, "LM head with %d rows exceeds 64", M);
+  const dim3 block(LM_WAVES * 64);
+  const bool zlds = M <= 16 && 16 * (c.d / vec_elems(c.dtype)) <= LM_ZLDS_U4;
+  if (zlds) {
+    hipLaunchKernelGGL((lmhead_kernel<T, 1, LM_WAVES, true>), dim3(grid), block, 0, st, a);
+  } else {
+    switch (cdiv(M, 16)) {
+      case 1: hipLaunchKernelGGL((lmhead_kernel<T, 1, LM_WAVES, false>), dim3(grid), block, 0, st, a); break;
+      case 2: hipLaunchKernelGGL((lmhead_kernel<T, 2, LM_WAVES, false>), dim3(grid), block, 0, st, a); break;
+      case 3: hipLaunchKernelGGL((lmhead_kernel<T, 3, LM_WAVES, false>), dim3(grid), block, 0, st, a); break;
+      case 4: hipLaunchKernelGGL((lmhead_kernel<T, 4, LM_WAVES, false>), dim3(grid), block, 0, st, a); break;
+      default: return fail(FM_EINVAL, "LM head with %d rows exceeds 64", M);
+    }
   }
   FM_LAUNCHED("lmhead_kernel");
+  if (tokens) {
+    hipLaunchKernelGGL(argmax_finalize_kernel, dim3(1), dim3(256), 0, st, a.partial, grid, M, tokens);
+    FM_LAUNCHED("argmax_finalize_kernel");
+  }
   return FM_OK;
 }
 
@@ -627,7 +652,8 @@ fm_status fm_create(const fm_config* cfg, void* workspace, size_t ws_bytes, int 
   h->device = device;
   h->ws = reinterpret_cast<char*>(workspace);
   h->lay = lay;
-  hipLaunchKernelGGL(zero_u32_kernel, dim3(32), dim3(256), 0, 0, h->at<uint32_t>(lay.counters), (size_t)N_COUNTERS);
+  hipLaunchKernelGGL(zero_u32_kernel, dim3(64), dim3(256), 0, 0, h->at<uint32_t>(lay.counters),
+                     (size_t)N_COUNTER_SLOTS * COUNTER_STRIDE);
   hipError_t e = hipGetLastError();
   if (e == hipSuccess) e = hipStreamSynchronize(0);
   if (e != hipSuccess) {

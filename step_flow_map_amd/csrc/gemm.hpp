@@ -3,16 +3,18 @@
 //   out[m][n] = sum_k A[m][k] * W[n][k]        (W row-major [N][K], k contiguous)
 //
 // M is small (block rows of every branch, plus the context rows appended in the
-// step: at most 80), so each 16-byte weight vector loaded from HBM feeds M/16
-// MFMAs and the layer is bound by streaming W.  A workgroup owns NT 16-column
-// tiles and one K range of a deterministic split-K; its waves take interleaved
-// k chunks (so the four waves of a workgroup read adjacent bytes of every
-// weight row), reduce through LDS in a fixed order, and either run the
-// epilogue (one split) or publish a float32 partial.  The last workgroup to
-// arrive on a column tile sums the partials in split order and runs the
-// epilogue, so results never depend on scheduling.
+// step: at most 80), so the layer is bound by streaming W once from HBM.
+// A workgroup owns one 16-row tile of W and one k range of a deterministic
+// split-K; its waves take interleaved 8 KB chunks of that range, stream them
+// through their LDS tile into MFMA operands (stream.hpp) with the next chunk
+// already in flight, and reduce across waves through LDS in wave order.  With
+// one split the workgroup runs the epilogue; otherwise it publishes a float32
+// partial with coherent stores and the last of the (few) splits of the tile
+// sums them in split order and runs the epilogue.  Results never depend on
+// scheduling.
 #pragma once
 #include "common.hpp"
+#include "stream.hpp"
 
 namespace fm {
 
@@ -38,15 +40,17 @@ struct EpiParams {
   int col_offset;       // EPI_QKV: logical qkv column of n = 0 (d for a K/V-only call)
 };
 
+constexpr int GEMM_SPLIT_MAX = 8;  // k splits per tile (= arrivals per counter)
+
 struct GemmArgs {
   const void* A;
   int lda, M;
   const void* W;
   int ldw, N, K;
-  int S;          // k splits
+  int S;          // k splits (<= 8: arrivals per counter)
   int k_split;    // k elements per split (multiple of the chunk)
   float* partial; // [S][M][N] float32 when S > 1
-  uint32_t* counters;  // one per column group, zero on entry, zero on exit
+  uint32_t* counters;  // one per 16-row tile, COUNTER_STRIDE apart; zero on entry and exit
 };
 
 template <typename T, int EPI>
@@ -74,38 +78,28 @@ __device__ __forceinline__ void epilogue(const EpiParams& e, int m, int n, float
   }
 }
 
-template <typename T, int MT, int NT, int U, int WAVES, int EPI>
-__global__ __launch_bounds__(WAVES * 64) void gemm_nt_kernel(GemmArgs g, EpiParams e) {
+template <typename T, int MT, int NW, int EPI>
+__global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs g, EpiParams e) {
   typedef typename Vec<T>::type VT;
-  constexpr int VE = Vec<T>::N;
-  constexpr int CHUNK = 4 * U * VE;  // k elements per wave iteration
-  constexpr int ELEMS = MT * NT * 4 * 64;
-  __shared__ float red[WAVES > 1 ? WAVES * ELEMS : 1];
+  constexpr int VE = ChunkT<T>::VE;
+  constexpr int KC = ChunkT<T>::KC;
+  constexpr int ELEMS = MT * 256;  // outputs of the tile: MT*16 rows x 16 columns
+  constexpr int RED_U4 = (NW * ELEMS + 3) / 4;
+  constexpr int TILE_U4 = NW * 512;
+  __shared__ uint4 smem[TILE_U4 > RED_U4 ? TILE_U4 : RED_U4];
   __shared__ int flag;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int j = lane & 15, grp = lane >> 4;
-  const int group = blockIdx.x / g.S, s = blockIdx.x % g.S;
-  const int n0 = group * 16 * NT;
+  const int tile = blockIdx.x / g.S, s = blockIdx.x % g.S;
+  const int n0 = tile * 16;
   const int k_begin = s * g.k_split;
   const int k_end = min(g.K, k_begin + g.k_split);
+  const int nch = k_end > k_begin ? (k_end - k_begin + KC - 1) / KC : 0;
   const T* A = reinterpret_cast<const T*>(g.A);
   const T* W = reinterpret_cast<const T*>(g.W);
+  uint4* wt = smem + wave * 512;
 
-  f32x4 acc[MT][NT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const T* wrow[NT];
-  bool wok[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int n = n0 + nt * 16 + j;
-    wok[nt] = n < g.N;
-    wrow[nt] = W + (size_t)(wok[nt] ? n : 0) * g.ldw;
-  }
   const T* arow[MT];
   bool aok[MT];
 #pragma unroll
@@ -114,62 +108,62 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_nt_kernel(GemmArgs g, EpiPara
     aok[mt] = m < g.M;
     arow[mt] = A + (size_t)(aok[mt] ? m : 0) * g.lda;
   }
+  f32x4 acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int kc = k_begin + wave * CHUNK; kc < k_end; kc += WAVES * CHUNK) {
-    const int kl = kc + grp * U * VE;
-    VT b[NT][U], a[MT][U];
+  auto process = [&](const uint4 (&r)[8], int c) {
+    const int k0 = k_begin + c * KC;
+    chunk_to_lds(r, wt);
+    wave_lds_sync();
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
+    for (int st = 0; st < 8; ++st) {
+      const VT b = as_vec<T>(chunk_frag(wt, st));
+      const int k = k0 + (4 * st + grp) * VE;
+      const bool kok = k < k_end;
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int k = kl + u * VE;
-        b[nt][u] = (wok[nt] && k < k_end) ? vload<T>(wrow[nt] + k) : vzero<VT>();
+      for (int mt = 0; mt < MT; ++mt) {
+        const bool ok = kok && aok[mt];
+        const VT av = vload<T>(arow[mt] + (ok ? k : 0));
+        mma(acc[mt], ok ? av : vzero<VT>(), b);
       }
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int k = kl + u * VE;
-        a[mt][u] = (aok[mt] && k < k_end) ? vload<T>(arow[mt] + k) : vzero<VT>();
-      }
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) mma(acc[mt][nt], a[mt][u], b[nt][u]);
+    }
+    wave_lds_sync();
+  };
+
+  uint4 r0[8], r1[8];
+  if (wave < nch) chunk_load<T>(r0, W, g.ldw, n0, g.N, k_begin + wave * KC, k_end);
+  for (int c = wave; c < nch; c += 2 * NW) {
+    if (c + NW < nch) chunk_load<T>(r1, W, g.ldw, n0, g.N, k_begin + (c + NW) * KC, k_end);
+    process(r0, c);
+    if (c + NW < nch) {
+      if (c + 2 * NW < nch) chunk_load<T>(r0, W, g.ldw, n0, g.N, k_begin + (c + 2 * NW) * KC, k_end);
+      process(r1, c + NW);
+    }
   }
 
   // ---- fixed-order reduction over the waves of the workgroup
-  float val[MT * NT];  // this thread's elements e = threadIdx.x + r * WAVES * 64
-  if (WAVES > 1) {
+  __syncthreads();  // every wave is done with its LDS tile
+  float* red = reinterpret_cast<float*>(smem);
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          red[wave * ELEMS + ((mt * NT + nt) * 4 + i) * 64 + lane] = acc[mt][nt][i];
-    __syncthreads();
-  }
-  constexpr int PER_THREAD = ELEMS / (WAVES * 64);
-  static_assert(ELEMS % (WAVES * 64) == 0, "elements must split evenly over threads");
+    for (int i = 0; i < 4; ++i) red[wave * ELEMS + (mt * 4 + i) * 64 + lane] = acc[mt][i];
+  __syncthreads();
+  constexpr int PER_THREAD = (ELEMS + NW * 64 - 1) / (NW * 64);
+  float val[PER_THREAD];
   int em[PER_THREAD], en[PER_THREAD];
 #pragma unroll
   for (int r = 0; r < PER_THREAD; ++r) {
-    const int el = threadIdx.x + r * WAVES * 64;
-    const int ln = el & 63, q = el >> 6;  // q = (mt*NT + nt)*4 + i
-    const int i = q & 3, tile = q >> 2;
-    const int mt = tile / NT, nt = tile % NT;
-    em[r] = mt * 16 + 4 * (ln >> 4) + i;
-    en[r] = n0 + nt * 16 + (ln & 15);
-    float v;
-    if (WAVES > 1) {
-      v = 0.f;
+    const int el = threadIdx.x + r * NW * 64;
+    const int ln = el & 63, q = el >> 6;  // q = mt*4 + i
+    const int i = q & 3, mt = q >> 2;
+    em[r] = el < ELEMS ? mt * 16 + 4 * (ln >> 4) + i : g.M;
+    en[r] = n0 + (ln & 15);
+    float v = 0.f;
+    if (el < ELEMS) {
 #pragma unroll
-      for (int w = 0; w < WAVES; ++w) v += red[w * ELEMS + el];
-    } else {
-      v = acc[mt][nt][i];
+      for (int w = 0; w < NW; ++w) v += red[w * ELEMS + el];
     }
     val[r] = v;
   }
@@ -182,16 +176,20 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_nt_kernel(GemmArgs g, EpiPara
   }
 #pragma unroll
   for (int r = 0; r < PER_THREAD; ++r)
-    if (em[r] < g.M && en[r] < g.N)
-      g.partial[((size_t)s * g.M + em[r]) * g.N + en[r]] = val[r];
-  if (!arrive_last(&g.counters[group], (uint32_t)g.S, &flag)) return;
+    if (em[r] < g.M && en[r] < g.N) st_coh(&g.partial[((size_t)s * g.M + em[r]) * g.N + en[r]], val[r]);
+  if (!arrive(&g.counters[tile * COUNTER_STRIDE], (uint32_t)g.S, &flag)) return;
+  // all coherent loads in flight together, then summed in split order
 #pragma unroll
   for (int r = 0; r < PER_THREAD; ++r) {
-    if (em[r] < g.M && en[r] < g.N) {
-      float v = 0.f;
-      for (int ss = 0; ss < g.S; ++ss) v += g.partial[((size_t)ss * g.M + em[r]) * g.N + en[r]];
-      epilogue<T, EPI>(e, em[r], en[r], v);
-    }
+    const bool ok = em[r] < g.M && en[r] < g.N;
+    float pv[GEMM_SPLIT_MAX];
+#pragma unroll
+    for (int ss = 0; ss < GEMM_SPLIT_MAX; ++ss)
+      pv[ss] = (ok && ss < g.S) ? ld_coh(&g.partial[((size_t)ss * g.M + em[r]) * g.N + en[r]]) : 0.f;
+    float v = 0.f;
+#pragma unroll
+    for (int ss = 0; ss < GEMM_SPLIT_MAX; ++ss) v += pv[ss];
+    if (ok) epilogue<T, EPI>(e, em[r], en[r], v);
   }
 }
 

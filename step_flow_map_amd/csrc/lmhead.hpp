@@ -3,14 +3,16 @@
 //   logits[m][v] = sum_c z[m][c] * W_lm[v][c]      (float32, no bias)
 //   tokens[m]    = lowest v among the maxima of logits[m][:]
 //
-// Each wave owns NT 16-column (vocabulary) tiles at a time and walks the full
-// width d; the workgroups stride over all tiles of the vocabulary.  The
-// running best of each row is an order-preserving 64-bit key (value, then
-// lower index), so the reduction across lanes, waves and workgroups is a plain
-// max in any order.  The last workgroup to finish reduces the per-workgroup
-// keys and writes the tokens.  Optionally the float32 logits are written out.
+// Persistent grid: every wave walks a fixed set of 16-row vocabulary tiles
+// (tile t, t + waves, ...), streaming each tile's d-wide rows chunk by chunk
+// through its LDS tile into MFMA operands with the next chunk in flight.  z is
+// staged once per workgroup in LDS (XOR-swizzled rows) when it fits.  The
+// running best of each row is an order-preserving 64-bit key (value, then lower
+// index), so lanes, waves and workgroups combine with a plain max in any order;
+// each workgroup writes its keys and argmax_finalize_kernel reduces them.
 #pragma once
 #include "common.hpp"
+#include "stream.hpp"
 
 namespace fm {
 
@@ -21,24 +23,34 @@ struct LmArgs {
   int V;
   float* logits;      // [M][V] or null
   uint64_t* partial;  // [gridDim.x][M]
-  uint32_t* counter;
-  int32_t* tokens;    // [M] or null
 };
 
-template <typename T, int MT, int NT, int U, int WAVES>
-__global__ __launch_bounds__(WAVES * 64) void lmhead_kernel(LmArgs g) {
+constexpr int LM_ZLDS_U4 = 4096;  // 64 KB of z in LDS
+
+template <typename T, int MT, int NW, bool ZLDS>
+__global__ __launch_bounds__(NW * 64) void lmhead_kernel(LmArgs g) {
   typedef typename Vec<T>::type VT;
-  constexpr int VE = Vec<T>::N;
-  constexpr int CHUNK = 4 * U * VE;
-  constexpr int MROWS = MT * 16;
-  __shared__ uint64_t wbest[WAVES][MROWS];
-  __shared__ int flag;
+  constexpr int VE = ChunkT<T>::VE;
+  constexpr int KC = ChunkT<T>::KC;
+  static_assert(!ZLDS || MT == 1, "z in LDS holds one 16-row tile");
+  __shared__ uint4 wtiles[NW * 512];
+  __shared__ uint4 zs[ZLDS ? LM_ZLDS_U4 : 1];
+  __shared__ uint64_t wbest[NW][MT * 16];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int j = lane & 15, grp = lane >> 4;
   const T* Z = reinterpret_cast<const T*>(g.z);
   const T* W = reinterpret_cast<const T*>(g.W);
-  const int n_groups = (g.V + 16 * NT - 1) / (16 * NT);
+  const int pieces = g.d / VE;  // 16-byte pieces per z row
+
+  if (ZLDS) {  // rows m < M, piece p at m*pieces + (p ^ (m & 15))
+    const uint4* zg = reinterpret_cast<const uint4*>(Z);
+    for (int i = threadIdx.x; i < 16 * pieces; i += NW * 64) {
+      const int m = i / pieces, p = i % pieces;
+      zs[m * pieces + (p ^ (m & 15))] = m < g.M ? zg[(size_t)m * pieces + p] : make_uint4(0, 0, 0, 0);
+    }
+    __syncthreads();
+  }
 
   const T* zrow[MT];
   bool zok[MT];
@@ -54,63 +66,74 @@ __global__ __launch_bounds__(WAVES * 64) void lmhead_kernel(LmArgs g) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) best[mt][i] = 0ull;
 
-  for (int tg = blockIdx.x * WAVES + wave; tg < n_groups; tg += gridDim.x * WAVES) {
-    const int n0 = tg * 16 * NT;
-    f32x4 acc[MT][NT];
+  const int ntiles = (g.V + 15) / 16, nch = (g.d + KC - 1) / KC;
+  const int gw = blockIdx.x * NW + wave, nw = gridDim.x * NW;
+  const int total = gw < ntiles ? ((ntiles - 1 - gw) / nw + 1) * nch : 0;
+  uint4* wt = wtiles + wave * 512;
+  f32x4 acc[MT];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto load = [&](uint4 (&r)[8], int q) {
+    const int t = gw + (q / nch) * nw, c = q % nch;
+    chunk_load<T>(r, W, g.d, t * 16, g.V, c * KC, g.d);
+  };
+  auto process = [&](const uint4 (&r)[8], int q) {
+    const int t = gw + (q / nch) * nw, c = q % nch;
+    const int k0 = c * KC;
+    chunk_to_lds(r, wt);
+    wave_lds_sync();
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const T* wrow[NT];
-    bool wok[NT];
+    for (int st = 0; st < 8; ++st) {
+      const VT b = as_vec<T>(chunk_frag(wt, st));
+      const int k = k0 + (4 * st + grp) * VE;
+      const bool kok = k < g.d;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int n = n0 + nt * 16 + j;
-      wok[nt] = n < g.V;
-      wrow[nt] = W + (size_t)(wok[nt] ? n : 0) * g.d;
-    }
-    for (int kc = 0; kc < g.d; kc += CHUNK) {
-      const int kl = kc + grp * U * VE;
-      VT b[NT][U], a[MT][U];
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int k = kl + u * VE;
-          b[nt][u] = (wok[nt] && k < g.d) ? vload<T>(wrow[nt] + k) : vzero<VT>();
+      for (int mt = 0; mt < MT; ++mt) {
+        VT av;
+        if (ZLDS) {
+          const int p = kok ? k / VE : 0;
+          av = as_vec<T>(zs[j * pieces + (p ^ j)]);
+          av = kok ? av : vzero<VT>();
+        } else {
+          const bool ok = kok && zok[mt];
+          av = vload<T>(zrow[mt] + (ok ? k : 0));
+          av = ok ? av : vzero<VT>();
         }
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int k = kl + u * VE;
-          a[mt][u] = (zok[mt] && k < g.d) ? vload<T>(zrow[mt] + k) : vzero<VT>();
-        }
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) mma(acc[mt][nt], a[mt][u], b[nt][u]);
+        mma(acc[mt], av, b);
+      }
     }
+    wave_lds_sync();
+    if (c == nch - 1) {
+      const int n = t * 16 + j;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+      for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = mt * 16 + 4 * grp + i;
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          const int n = n0 + nt * 16 + j;
+        for (int i = 0; i < 4; ++i) {
+          const int m = mt * 16 + 4 * grp + i;
           if (n < g.V && m < g.M) {
-            const float v = acc[mt][nt][i];
+            const float v = acc[mt][i];
             best[mt][i] = umax64(best[mt][i], argmax_key(v, (uint32_t)n));
             if (g.logits) g.logits[(size_t)m * g.V + n] = v;
           }
         }
+        acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
+    }
+  };
+
+  uint4 r0[8], r1[8];
+  if (total > 0) load(r0, 0);
+  for (int q = 0; q < total; q += 2) {
+    if (q + 1 < total) load(r1, q + 1);
+    process(r0, q);
+    if (q + 1 < total) {
+      if (q + 2 < total) load(r0, q + 2);
+      process(r1, q + 1);
+    }
   }
 
-  // reduce over the 16 lanes that share a row group, then over waves
+  // reduce over the 16 lanes that share a row group, then over the waves
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -121,24 +144,26 @@ __global__ __launch_bounds__(WAVES * 64) void lmhead_kernel(LmArgs g) {
       if (j == 0) wbest[wave][mt * 16 + 4 * grp + i] = k;
     }
   __syncthreads();
-  for (int m = threadIdx.x; m < g.M; m += WAVES * 64) {
+  for (int m = threadIdx.x; m < g.M; m += NW * 64) {
     uint64_t k = 0ull;
 #pragma unroll
-    for (int w = 0; w < WAVES; ++w) k = umax64(k, wbest[w][m]);
+    for (int w = 0; w < NW; ++w) k = umax64(k, wbest[w][m]);
     g.partial[(size_t)blockIdx.x * g.M + m] = k;
   }
-  if (!arrive_last(g.counter, gridDim.x, &flag)) return;
+}
 
-  // final reduction: TPR threads per row, consecutive lanes of one wave
-  int mp = WAVES;  // at most 64 threads per row, so one wave holds a row
-  while (mp < g.M) mp <<= 1;
-  const int tpr = (WAVES * 64) / mp;  // host guarantees M <= WAVES * 64
+// tokens[m] = index of max over G workgroup keys; 256 threads, tpr threads per
+// row on consecutive lanes (M <= 64)
+__global__ __launch_bounds__(256) void argmax_finalize_kernel(const uint64_t* partial, int G, int M, int32_t* tokens) {
+  int mp = 4;
+  while (mp < M) mp <<= 1;
+  const int tpr = 256 / mp;
   const int m = threadIdx.x / tpr, sub = threadIdx.x % tpr;
   uint64_t k = 0ull;
-  if (m < g.M)
-    for (int blk = sub; blk < (int)gridDim.x; blk += tpr) k = umax64(k, g.partial[(size_t)blk * g.M + m]);
+  if (m < M)
+    for (int b = sub; b < G; b += tpr) k = umax64(k, partial[(size_t)b * M + m]);
   for (int o = 1; o < tpr; o <<= 1) k = umax64(k, shfl_xor_u64(k, o));
-  if (m < g.M && sub == 0 && g.tokens) g.tokens[m] = (int32_t)argmax_key_index(k);
+  if (m < M && sub == 0) tokens[m] = (int32_t)argmax_key_index(k);
 }
 
 }  // namespace fm
