@@ -108,3 +108,31 @@ def test_errors_enqueue_nothing():
     with pytest.raises(fm.FlashMapError) as e:
         dr.draft(to_dev(synth.make_noise(cfg, 2)))     # max_branches = 1
     assert e.value.status == fm.FM_ECAPACITY
+
+
+@pytest.mark.parametrize("cfg", [TINY, SMALL_BF16], ids=["tiny_f32", "small_bf16"])
+def test_two_step_schedule(cfg):
+    cfg = cfg.with_(times=(0.0, 0.5, 1.0))
+    w, feats, noise = _case(cfg)
+    dr = make_drafter(cfg, w)
+    dr.set_schedule(cfg.times)
+    tok, logits, hidden = run_draft(dr, cfg, noise, feats, cfg.c_prefill, want_hidden=True)
+    rel, ties = check_draft(cfg, w, noise, feats, cfg.c_prefill, tok, logits, hidden)
+    print(f"  2-step {cfg.name}: logit error {rel:.2e}, near-ties {ties}")
+
+
+@pytest.mark.parametrize("cfg", [TINY, SMALL_BF16], ids=["tiny_f32", "small_bf16"])
+def test_draft_tree_of_four(cfg):
+    cfg = cfg.with_(B=4)
+    w, feats, noise = _case(cfg, B=4)
+    dr = make_drafter(cfg, w)
+    dr.set_schedule(cfg.times)
+    tok, logits, hidden = run_draft(dr, cfg, noise, feats, cfg.c_prefill, want_hidden=True)
+    rel, ties = check_draft(cfg, w, noise, feats, cfg.c_prefill, tok, logits, hidden)
+    print(f"  tree {cfg.name}: logit error {rel:.2e}, near-ties {ties}")
+    # the branches are independent: branch 2 alone gives the same draft
+    dr1 = make_drafter(cfg.with_(B=1), w)
+    dr1.set_schedule(cfg.times)
+    t1, l1, _ = run_draft(dr1, cfg.with_(B=1), noise[2:3], feats, cfg.c_prefill)
+    assert np.array_equal(t1[0], tok[2])
+    assert np.abs(l1[0] - logits[2]).max() <= 1e-3 * np.abs(logits[2]).max()
