@@ -174,12 +174,12 @@ __device__ __forceinline__ bool arrive(uint32_t* counter, uint32_t expected, int
 // counters live 32 words (128 bytes) apart so contended lines never share
 constexpr int COUNTER_STRIDE = 32;
 
-// compiler barrier + LDS ordering point inside one wave
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
+// Ordering point between a wave's LDS writes and its reads of other lanes'
+// data.  No fence is needed: the compiler cannot prove the per-lane addresses
+// differ, so it keeps the accesses in program order, and the LDS executes one
+// wave's accesses in order.  (A release fence here would also wait for every
+// outstanding global load, draining the next chunk's prefetch.)
+__device__ __forceinline__ void wave_lds_sync() {}
 
 __device__ __forceinline__ float gelu_tanh(float x) {
   const float k0 = 0.7978845608028654f;  // sqrt(2/pi)

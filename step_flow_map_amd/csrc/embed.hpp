@@ -21,6 +21,7 @@
 // workgroups round-robin over the 8 XCDs), so x is fetched once per XCD.
 #pragma once
 #include "common.hpp"
+#include "stream.hpp"
 
 namespace fm {
 
@@ -94,29 +95,25 @@ __global__ __launch_bounds__(NW * 64) void embed_kernel(EmbedArgs g) {
   const T* ecol = E + c0 + j * VE;
 
   // this lane's VE rows of chunk v0 start at v0 + grp*VE; V and the split are
-  // multiples of VE, so a lane's rows are all in range or all out
+  // multiples of VE, so a lane's rows are all in range or all out.  Loads use
+  // clamped addresses; the range check is applied to x at use (an out-of-range
+  // chunk contributes x = 0), so no loaded value is selected before the MFMA.
   auto load = [&](VT (&in)[VE], VT (&a)[MT], int v0) {
     const int vr = v0 + grp * VE;
-    const bool ok = vr < v_end;
-    const int vs = ok ? vr : 0;
+    const int vs = vr < v_end ? vr : 0;
 #pragma unroll
-    for (int r = 0; r < VE; ++r) {
-      const VT v = vload<T>(ecol + (size_t)(vs + r) * g.d);
-      in[r] = ok ? v : vzero<VT>();
-    }
+    for (int r = 0; r < VE; ++r) in[r] = as_vec<T>(ldg_stream(ecol + (size_t)(vs + r) * g.d));
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const VT v = vload<T>(xrow[mt] + vs);
-      a[mt] = (ok && xok[mt]) ? v : vzero<VT>();
-    }
+    for (int mt = 0; mt < MT; ++mt) a[mt] = vload<T>(xrow[mt] + vs);
   };
-  auto compute = [&](const VT (&in)[VE], const VT (&a)[MT]) {
+  auto compute = [&](const VT (&in)[VE], const VT (&a)[MT], int v0) {
+    const bool ok = v0 + grp * VE < v_end;
     VT bt[VE];
     transpose_block(in, bt);
 #pragma unroll
     for (int t = 0; t < VE; ++t)
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) mma(acc[mt][t], a[mt], bt[t]);
+      for (int mt = 0; mt < MT; ++mt) mma(acc[mt][t], (ok && xok[mt]) ? a[mt] : vzero<VT>(), bt[t]);
   };
 
   VT in0[VE], in1[VE], a0[MT], a1[MT];
@@ -124,10 +121,10 @@ __global__ __launch_bounds__(NW * 64) void embed_kernel(EmbedArgs g) {
   if (first < v_end) load(in0, a0, first);
   for (int v0 = first; v0 < v_end; v0 += 2 * step) {
     if (v0 + step < v_end) load(in1, a1, v0 + step);
-    compute(in0, a0);
+    compute(in0, a0, v0);
     if (v0 + step < v_end) {
       if (v0 + 2 * step < v_end) load(in0, a0, v0 + 2 * step);
-      compute(in1, a1);
+      compute(in1, a1, v0 + step);
     }
   }
 

@@ -60,8 +60,6 @@ fm_status fail(fm_status st, const char* fmt, ...) {
 constexpr int KB = 16;             // block rows per branch (K)
 constexpr int ATT_SUB = 64;        // keys per attention sub-chunk
 constexpr int ATT_MAX_RANGES = ATT_RANGES_MAX;
-constexpr int GEMM_WAVES = 4;
-constexpr int GEMM_TARGET_WG = 512;
 constexpr int GEMM_MAX_SPLIT = GEMM_SPLIT_MAX;
 constexpr int LM_WAVES = 8;
 constexpr int LM_GRID = 256;
@@ -78,19 +76,21 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 int cdiv(int a, int b) { return (a + b - 1) / b; }
 
 struct GemmPlan {
-  int S, k_split, n_groups, grid;
+  int S, k_split, n_groups, grid, waves;
 };
 
-// one workgroup per (16-row tile, k split); splits keep every wave of a
-// workgroup busy and stay within GEMM_MAX_SPLIT arrivals per tile counter
+// One workgroup per (16-row tile, k split).  Without a split there is no
+// cross-workgroup reduction at all; a split is used only when the tiles alone
+// cannot cover the CUs and the k range is long (a device-scope arrival costs a
+// memory round trip).  Workgroups of 8 waves when tiles are few, else 4.
 GemmPlan plan_gemm(int N, int K, fm_dtype t) {
   const int chunk = gemm_chunk(t);
   GemmPlan p;
   p.n_groups = cdiv(N, 16);
   const int nch = std::max(1, cdiv(K, chunk));
+  p.waves = p.n_groups < 256 ? 8 : 4;
   int S = 1;
-  if (p.n_groups < GEMM_TARGET_WG)
-    S = std::min({GEMM_MAX_SPLIT, cdiv(GEMM_TARGET_WG, p.n_groups), std::max(1, nch / GEMM_WAVES)});
+  if (p.n_groups < 256 && nch > 4 * p.waves) S = std::min(GEMM_MAX_SPLIT, cdiv(256, p.n_groups));
   p.k_split = cdiv(nch, S) * chunk;
   p.S = cdiv(K, p.k_split);
   p.grid = p.n_groups * p.S;
@@ -230,18 +230,21 @@ namespace {
 
 // ------------------------------------------------------------------ launchers
 template <typename T, int MT, int EPI>
-void launch_gemm_mt(const GemmArgs& a, const EpiParams& e, int grid, hipStream_t st) {
-  hipLaunchKernelGGL((gemm_kernel<T, MT, GEMM_WAVES, EPI>), dim3(grid), dim3(GEMM_WAVES * 64), 0, st, a, e);
+void launch_gemm_mt(const GemmArgs& a, const EpiParams& e, int grid, int waves, hipStream_t st) {
+  if (waves == 8)
+    hipLaunchKernelGGL((gemm_kernel<T, MT, 8, EPI>), dim3(grid), dim3(8 * 64), 0, st, a, e);
+  else
+    hipLaunchKernelGGL((gemm_kernel<T, MT, 4, EPI>), dim3(grid), dim3(4 * 64), 0, st, a, e);
 }
 
 template <typename T, int EPI>
-fm_status launch_gemm_epi(const GemmArgs& a, const EpiParams& e, int grid, hipStream_t st) {
+fm_status launch_gemm_epi(const GemmArgs& a, const EpiParams& e, int grid, int waves, hipStream_t st) {
   switch (cdiv(a.M, 16)) {
-    case 1: launch_gemm_mt<T, 1, EPI>(a, e, grid, st); break;
-    case 2: launch_gemm_mt<T, 2, EPI>(a, e, grid, st); break;
-    case 3: launch_gemm_mt<T, 3, EPI>(a, e, grid, st); break;
-    case 4: launch_gemm_mt<T, 4, EPI>(a, e, grid, st); break;
-    case 5: launch_gemm_mt<T, 5, EPI>(a, e, grid, st); break;
+    case 1: launch_gemm_mt<T, 1, EPI>(a, e, grid, waves, st); break;
+    case 2: launch_gemm_mt<T, 2, EPI>(a, e, grid, waves, st); break;
+    case 3: launch_gemm_mt<T, 3, EPI>(a, e, grid, waves, st); break;
+    case 4: launch_gemm_mt<T, 4, EPI>(a, e, grid, waves, st); break;
+    case 5: launch_gemm_mt<T, 5, EPI>(a, e, grid, waves, st); break;
     default: return fail(FM_EINVAL, "contraction with %d rows exceeds 80", a.M);
   }
   FM_LAUNCHED("gemm_kernel");
@@ -268,11 +271,11 @@ fm_status gemm(fm_handle* h, int epi, const void* A, int lda, int M, const void*
   a.partial = h->at<float>(h->lay.partial);
   a.counters = h->at<uint32_t>(h->lay.counters);
   switch (epi) {
-    case EPI_F32: return launch_gemm_epi<T, EPI_F32>(a, e, p.grid, st);
-    case EPI_ACT: return launch_gemm_epi<T, EPI_ACT>(a, e, p.grid, st);
-    case EPI_GELU: return launch_gemm_epi<T, EPI_GELU>(a, e, p.grid, st);
-    case EPI_RESID: return launch_gemm_epi<T, EPI_RESID>(a, e, p.grid, st);
-    default: return launch_gemm_epi<T, EPI_QKV>(a, e, p.grid, st);
+    case EPI_F32: return launch_gemm_epi<T, EPI_F32>(a, e, p.grid, p.waves, st);
+    case EPI_ACT: return launch_gemm_epi<T, EPI_ACT>(a, e, p.grid, p.waves, st);
+    case EPI_GELU: return launch_gemm_epi<T, EPI_GELU>(a, e, p.grid, p.waves, st);
+    case EPI_RESID: return launch_gemm_epi<T, EPI_RESID>(a, e, p.grid, p.waves, st);
+    default: return launch_gemm_epi<T, EPI_QKV>(a, e, p.grid, p.waves, st);
   }
 }
 

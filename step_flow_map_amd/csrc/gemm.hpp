@@ -112,33 +112,53 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs g, EpiParams e) 
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto process = [&](const uint4 (&r)[8], int c) {
+  // Up to two row tiles, a chunk's weights and the matching A fragments are
+  // loaded together, one chunk ahead of the MFMAs, so neither latency is
+  // exposed; larger row counts (draft trees) load A at use to stay in registers.
+  constexpr bool PRE_A = MT <= 2;
+  constexpr int AF = PRE_A ? MT : 1;
+  // A values outside [k_begin, k_end) or rows >= M are zeroed at use (this also
+  // neutralises the clamped weight columns beyond the k range)
+  auto a_ok = [&](int mt, int k0, int st) { return (k0 + (4 * st + grp) * VE) < k_end && aok[mt]; };
+  auto a_load = [&](int mt, int k0, int st) -> VT {
+    const int k = k0 + (4 * st + grp) * VE;
+    return vload<T>(arow[mt] + (a_ok(mt, k0, st) ? k : 0));
+  };
+  auto load = [&](uint4 (&r)[8], VT (&af)[AF][8], int c) {
+    const int k0 = k_begin + c * KC;
+    chunk_load<T>(r, W, g.ldw, n0, g.N, k0, k_end);
+    if (PRE_A) {
+#pragma unroll
+      for (int st = 0; st < 8; ++st)
+#pragma unroll
+        for (int mt = 0; mt < AF; ++mt) af[mt][st] = a_load(mt, k0, st);
+    }
+  };
+  auto process = [&](const uint4 (&r)[8], const VT (&af)[AF][8], int c) {
     const int k0 = k_begin + c * KC;
     chunk_to_lds(r, wt);
     wave_lds_sync();
 #pragma unroll
     for (int st = 0; st < 8; ++st) {
       const VT b = as_vec<T>(chunk_frag(wt, st));
-      const int k = k0 + (4 * st + grp) * VE;
-      const bool kok = k < k_end;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const bool ok = kok && aok[mt];
-        const VT av = vload<T>(arow[mt] + (ok ? k : 0));
-        mma(acc[mt], ok ? av : vzero<VT>(), b);
+        const VT av = PRE_A ? af[PRE_A ? mt : 0][st] : a_load(mt, k0, st);
+        mma(acc[mt], a_ok(mt, k0, st) ? av : vzero<VT>(), b);
       }
     }
     wave_lds_sync();
   };
 
   uint4 r0[8], r1[8];
-  if (wave < nch) chunk_load<T>(r0, W, g.ldw, n0, g.N, k_begin + wave * KC, k_end);
+  VT a0[AF][8], a1[AF][8];
+  if (wave < nch) load(r0, a0, wave);
   for (int c = wave; c < nch; c += 2 * NW) {
-    if (c + NW < nch) chunk_load<T>(r1, W, g.ldw, n0, g.N, k_begin + (c + NW) * KC, k_end);
-    process(r0, c);
+    if (c + NW < nch) load(r1, a1, c + NW);
+    process(r0, a0, c);
     if (c + NW < nch) {
-      if (c + 2 * NW < nch) chunk_load<T>(r0, W, g.ldw, n0, g.N, k_begin + (c + 2 * NW) * KC, k_end);
-      process(r1, c + NW);
+      if (c + 2 * NW < nch) load(r0, a0, c + 2 * NW);
+      process(r1, a1, c + NW);
     }
   }
 

@@ -14,29 +14,36 @@
 
 namespace fm {
 
+// 16-byte load of data read exactly once (weights): nontemporal hint
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ldg_stream(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 template <typename T>
 struct ChunkT {
   static constexpr int VE = Vec<T>::N;
   static constexpr int KC = 32 * VE;  // k elements per chunk
 };
 
-// Load the chunk of rows n0..n0+15 (rows >= N read as zero) and columns
-// k0..k0+KC-1 (columns >= K read as zero; K is a multiple of VE).  Loads are
-// unconditional from clamped, valid addresses; the value is then selected.
+// Load the chunk of rows n0..n0+15 and columns k0..k0+KC-1.  Addresses are
+// clamped into the matrix (rows >= N read row 0, columns >= K read column 0),
+// never masked here: a select on a loaded value would make the wave wait for
+// that load right away and defeat the prefetch.  Rows >= N only feed output
+// columns that are never stored, and columns >= K meet A values that the
+// consumer zeroes, so the clamped data never reaches a result.
 template <typename T>
 __device__ __forceinline__ void chunk_load(uint4 (&r)[8], const T* W, size_t ldw, int n0, int N, int k0, int K) {
   constexpr int VE = ChunkT<T>::VE;
   const int lane = threadIdx.x & 63;
   const int half = lane >> 5, p = lane & 31;
   const int kk = k0 + p * VE;
-  const bool kok = kk < K;
+  const int kc = kk < K ? kk : 0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int row = n0 + 2 * i + half;
-    const bool ok = kok && row < N;
-    const T* ptr = W + (size_t)(ok ? row : 0) * ldw + (ok ? kk : 0);
-    const uint4 v = *reinterpret_cast<const uint4*>(ptr);
-    r[i] = ok ? v : make_uint4(0, 0, 0, 0);
+    r[i] = ldg_stream(W + (size_t)(row < N ? row : 0) * ldw + kc);
   }
 }
 

@@ -19,22 +19,46 @@ __global__ __launch_bounds__(1024) void verify_argmax_kernel(const T* logits, in
   __shared__ uint64_t wk[16];
   const T* row = logits + (size_t)blockIdx.x * V;
   const int tid = threadIdx.x;
-  // head elements up to 16-byte alignment, vector body, tail
+  // head elements up to 16-byte alignment, vector body, tail.  Each thread
+  // visits its elements in increasing index order and keeps the first maximum
+  // (strict >, and -0 == +0 compare equal); the order-preserving key is built
+  // once per thread for the cross-thread reduction.
   const uintptr_t addr = reinterpret_cast<uintptr_t>(row);
   int head = (int)(((16 - (addr & 15)) & 15) / sizeof(T));
   if (head > V) head = V;
   const int nvec = (V - head) / VE;
   const int tail0 = head + nvec * VE;
-  uint64_t best = 0ull;
-  if (tid < head) best = argmax_key(to_f32<T>(row[tid]), (uint32_t)tid);
+  float bv = -INFINITY;
+  int bi = -1;
+  auto visit = [&](float v, int idx) {
+    if (bi < 0 || v > bv) {
+      bv = v;
+      bi = idx;
+    }
+  };
+  if (tid < head) visit(to_f32<T>(row[tid]), tid);
   const VT* body = reinterpret_cast<const VT*>(row + head);
-  for (int i = tid; i < nvec; i += 1024) {
+  constexpr int U = 8;  // eight 16-byte loads in flight per thread
+  int i = tid;
+  for (; i + (U - 1) * 1024 < nvec; i += U * 1024) {
+    VT v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = body[i + u * 1024];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int base = head + (i + u * 1024) * VE;
+#pragma unroll
+      for (int e = 0; e < VE; ++e) visit(velem(v[u], e), base + e);
+    }
+  }
+  for (; i < nvec; i += 1024) {
     const VT v = body[i];
     const int base = head + i * VE;
 #pragma unroll
-    for (int e = 0; e < VE; ++e) best = umax64(best, argmax_key(velem(v, e), (uint32_t)(base + e)));
+    for (int e = 0; e < VE; ++e) visit(velem(v, e), base + e);
   }
-  if (tail0 + tid < V) best = umax64(best, argmax_key(to_f32<T>(row[tail0 + tid]), (uint32_t)(tail0 + tid)));
+  if (tail0 + tid < V) visit(to_f32<T>(row[tail0 + tid]), tail0 + tid);
+  uint64_t best = bi >= 0 ? argmax_key(bv, (uint32_t)bi) : 0ull;
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) best = umax64(best, shfl_xor_u64(best, o));
   const int lane = tid & 63, wave = tid >> 6;
