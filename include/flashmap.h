@@ -53,9 +53,10 @@ typedef enum fm_dtype {
 } fm_dtype;
 
 /* Drafter shape and capacities.  Constraints checked by fm_create:
- *   K == 16; d % 64 == 0; n_heads divides d with d / n_heads in {64, 128};
- *   mlp_mult >= 1; n_ctx_layers == 5; V >= 16 and H >= 1 with V, H and d
- *   multiples of 8 (bf16) or 4 (f32), so every row starts 16-byte aligned;
+ *   K == 16; d a multiple of 128 (bf16) or 64 (f32), at most 4096; n_heads
+ *   divides d with d / n_heads in {64, 128}; mlp_mult >= 1; n_ctx_layers == 5;
+ *   V >= 16 and H >= 1 with V and H multiples of 8 (bf16) or 4 (f32), so
+ *   every row starts 16-byte aligned;
  *   1 <= max_branches <= 4; 0 <= max_new <= 16; C_max >= 0; 1 <= max_steps <= 4. */
 typedef struct fm_config {
   int K;             /* drafted block length (16)                            */
@@ -102,9 +103,10 @@ typedef struct fm_weights {
 
 typedef struct fm_handle fm_handle;
 
-/* Bytes of device workspace a handle with this configuration needs (context
- * K/V cache [L][C_max][2][d], modulation vectors, activations, split-K
- * partials and counters).  Returns 0 for an invalid configuration. */
+/* Bytes of device workspace a handle with this configuration needs (per DiT
+ * block a key and a value cache of ceil(C_max/32)*32 + 32*max_branches
+ * positions of width d, modulation vectors, activations, split-K partials and
+ * counters).  Returns 0 for an invalid configuration. */
 size_t fm_workspace_bytes(const fm_config *cfg);
 
 /* Create a handle on `device` using the caller's workspace (device memory of

@@ -58,7 +58,6 @@ fm_status fail(fm_status st, const char* fmt, ...) {
   } while (0)
 
 constexpr int KB = 16;             // block rows per branch (K)
-constexpr int ATT_SUB = 64;        // keys per attention sub-chunk
 constexpr int ATT_MAX_RANGES = ATT_RANGES_MAX;
 constexpr int GEMM_MAX_SPLIT = GEMM_SPLIT_MAX;
 constexpr int LM_WAVES = 8;
@@ -112,17 +111,21 @@ EmbedPlan plan_embed(int V, int d, fm_dtype t) {
 }
 
 struct AttnPlan {
-  int n_ranges, range_keys;
+  int n_ranges, blocks_per_range;
 };
 
-AttnPlan plan_attention(int total_keys) {
+// n_blocks 32-key blocks of one (branch, head) over at most 8 ranges
+AttnPlan plan_attention(int n_blocks) {
   AttnPlan p;
-  const int nsub = std::max(1, cdiv(total_keys, ATT_SUB));
-  const int per = cdiv(nsub, std::min(ATT_MAX_RANGES, nsub));
-  p.n_ranges = cdiv(nsub, per);
-  p.range_keys = per * ATT_SUB;
+  const int r = std::min(ATT_MAX_RANGES, n_blocks);
+  p.blocks_per_range = cdiv(n_blocks, r);
+  p.n_ranges = cdiv(n_blocks, p.blocks_per_range);
   return p;
 }
+
+// cache positions per head: the context capacity rounded up to whole 32-key
+// blocks, then one scratch block per branch for the branch's block rows
+int cache_positions(const fm_config& c) { return cdiv(c.C_max, ATT_BLK) * ATT_BLK + ATT_BLK * c.max_branches; }
 
 struct Layout {
   size_t cache, mods, sched, h, e_state, u_pre, act_qkv, act_d, attn_o, act_f, qkv;
@@ -156,7 +159,7 @@ Layout make_layout(const fm_config& c) {
     off = align256(off + std::max<size_t>(bytes, 1));
     return o;
   };
-  L.cache = take((size_t)c.L * c.C_max * 2 * d * es);
+  L.cache = take((size_t)c.L * 2 * cache_positions(c) * d * es);  // per block: keys, then values
   L.mods = take((size_t)c.max_steps * (6 * c.L + 2) * d * 4);
   L.sched = take(((size_t)2 * c.max_steps * 256 + 3 * (size_t)c.max_steps * d) * 4);
   L.h = take(Mb * d * 4);
@@ -166,7 +169,7 @@ Layout make_layout(const fm_config& c) {
   L.act_d = take(Mb * d * es);
   L.attn_o = take(Mb * d * es);
   L.act_f = take(Mb * F * es);
-  L.qkv = take(Mb * 3 * d * es);
+  L.qkv = take(Mb * d * es);  // queries of the block rows
   L.att_po = take((size_t)c.max_branches * c.n_heads * ATT_MAX_RANGES * KB * hd * 4);
   L.att_ml = take((size_t)c.max_branches * c.n_heads * ATT_MAX_RANGES * KB * 2 * 4);
   L.partial = take(partial_bytes(c));
@@ -224,6 +227,11 @@ struct fm_handle {
   hipEvent_t probe_start = nullptr, probe_stop = nullptr;
 
   template <typename P> P* at(size_t off) { return reinterpret_cast<P*>(ws + off); }
+  // key / value cache of DiT block l
+  template <typename T> T* kcache(int l) {
+    return at<T>(lay.cache) + (size_t)l * 2 * cache_positions(cfg) * cfg.d;
+  }
+  template <typename T> T* vcache(int l) { return kcache<T>(l) + (size_t)cache_positions(cfg) * cfg.d; }
 };
 
 namespace {
@@ -334,17 +342,22 @@ template <typename T>
 fm_status attention(fm_handle* h, int l, int B, int C, hipStream_t st) {
   const fm_config& c = h->cfg;
   const int hd = c.d / c.n_heads;
-  AttnPlan p = plan_attention(C + KB);
+  const int ctx_blocks = cdiv(C, ATT_BLK);
+  AttnPlan p = plan_attention(ctx_blocks + 1);
   AttnArgs a;
-  a.qkv = h->at<T>(h->lay.qkv);
-  a.ld_qkv = 3 * c.d;
-  a.cache = h->at<T>(h->lay.cache) + (size_t)l * c.C_max * 2 * c.d;
+  a.q = h->at<T>(h->lay.qkv);
+  a.ldq = c.d;
+  a.kc = h->kcache<T>(l);
+  a.vt = h->vcache<T>(l);
+  a.P = cache_positions(c);
   a.C = C;
+  a.ctx_blocks = ctx_blocks;
+  a.scratch_blk = cdiv(c.C_max, ATT_BLK);
   a.K = KB;
   a.d = c.d;
   a.nh = c.n_heads;
   a.n_ranges = p.n_ranges;
-  a.range_keys = p.range_keys;
+  a.blocks_per_range = p.blocks_per_range;
   a.part_o = h->at<float>(h->lay.att_po);
   a.part_ml = h->at<float>(h->lay.att_ml);
   a.counters = h->at<uint32_t>(h->lay.counters);
@@ -450,6 +463,18 @@ fm_status fuse_rows(fm_handle* h, const void* feats, int n, T* out, hipStream_t 
   return ln_mod<T>(h, h->at<float>(h->lay.u_pre), n, nullptr, nullptr, out, c.d, st);
 }
 
+// cache fields of the QKV epilogue for DiT block l
+template <typename T>
+void qkv_cache_params(fm_handle* h, int l, EpiParams& e) {
+  const fm_config& c = h->cfg;
+  e.kcache = h->kcache<T>(l);
+  e.vcache = h->vcache<T>(l);
+  e.P = cache_positions(c);
+  e.hd = c.d / c.n_heads;
+  e.d = c.d;
+  e.scratch_pos0 = cdiv(c.C_max, ATT_BLK) * ATT_BLK;
+}
+
 template <typename T>
 fm_status context_append_impl(fm_handle* h, const void* feats, int n, hipStream_t st) {
   const fm_config& c = h->cfg;
@@ -463,9 +488,8 @@ fm_status context_append_impl(fm_handle* h, const void* feats, int n, hipStream_
       EpiParams e{};
       e.bias = offset_rows<T>(blk(h, l, B_BQKV), c.d);
       e.rows_block = 0;
-      e.cache = h->at<T>(h->lay.cache) + (size_t)l * c.C_max * 2 * c.d;
+      qkv_cache_params<T>(h, l, e);
       e.cache_pos0 = h->ctx_len + r0;
-      e.d = c.d;
       e.col_offset = c.d;
       FM_TRY(gemm<T>(h, EPI_QKV, stage, c.d, rows, offset_rows<T>(blk(h, l, B_WQKV), (size_t)c.d * c.d), 2 * c.d,
                      c.d, e, st));
@@ -511,11 +535,10 @@ fm_status draft_impl(fm_handle* h, const void* noise, int B, const void* new_fea
         EpiParams e{};
         e.bias = blk(h, l, B_BQKV);
         e.out_act = qkv;
-        e.ld_act = 3 * d;
+        e.ld_act = d;
         e.rows_block = Mb;
-        e.cache = h->at<T>(h->lay.cache) + (size_t)l * c.C_max * 2 * d;
+        qkv_cache_params<T>(h, l, e);
         e.cache_pos0 = h->ctx_len;
-        e.d = d;
         e.col_offset = 0;
         FM_TRY(gemm<T>(h, EPI_QKV, act_qkv, d, m_qkv, blk(h, l, B_WQKV), 3 * d, d, e, st));
       }

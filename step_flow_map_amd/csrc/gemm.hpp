@@ -15,6 +15,7 @@
 #pragma once
 #include "common.hpp"
 #include "stream.hpp"
+#include "attention.hpp"
 
 namespace fm {
 
@@ -23,7 +24,8 @@ enum EpiKind {
   EPI_ACT = 1,    // out_act[m][n] = T(v + bias[n])
   EPI_GELU = 2,   // out_act[m][n] = T(gelu(v + bias[n]))
   EPI_RESID = 3,  // out_f32[m][n] += gate[n] * (v + bias[n])   (residual stream)
-  EPI_QKV = 4     // block rows: out_act[m][n] = T(v + b); context rows: K/V to cache
+  EPI_QKV = 4     // block rows: queries to out_act, keys/values to the branch's
+                  // scratch block of the cache; context rows: keys/values to the cache
 };
 
 struct EpiParams {
@@ -33,11 +35,14 @@ struct EpiParams {
   void* out_act;        // EPI_ACT / EPI_GELU / EPI_QKV
   int ld_act;
   const float* gate;    // EPI_RESID, [N]
-  int rows_block;       // EPI_QKV: rows >= rows_block are context rows
-  void* cache;          // EPI_QKV: this block's cache base, [C_max][2][d]
-  int cache_pos0;       // EPI_QKV: context position of row rows_block
-  int d;                // EPI_QKV: width
-  int col_offset;       // EPI_QKV: logical qkv column of n = 0 (d for a K/V-only call)
+  // EPI_QKV (cache layout: attention.hpp)
+  int rows_block;       // rows < rows_block are block rows (branch m / 16), the rest context rows
+  void* kcache;         // this DiT block's key cache   [nh][P][hd]
+  void* vcache;         // this DiT block's value cache [nh][P/32][hd][32]
+  int P, hd, d;         // positions per head, head width, model width
+  int cache_pos0;       // position of context row rows_block
+  int scratch_pos0;     // position of branch 0's first block row (branch b at +32b)
+  int col_offset;       // logical qkv column of n = 0 (d for a K/V-only call)
 };
 
 constexpr int GEMM_SPLIT_MAX = 8;  // k splits per tile (= arrivals per counter)
@@ -67,14 +72,25 @@ __device__ __forceinline__ void epilogue(const EpiParams& e, int m, int n, float
     *p = *p + e.gate[n] * v;
   } else {  // EPI_QKV
     const int nn = n + e.col_offset;
+    int pos;
     if (m < e.rows_block) {
-      reinterpret_cast<T*>(e.out_act)[(size_t)m * e.ld_act + n] = from_f32<T>(v);
-    } else if (nn >= e.d) {
-      const int p = e.cache_pos0 + (m - e.rows_block);
-      const int which = nn >= 2 * e.d;  // 0: key, 1: value
-      reinterpret_cast<T*>(e.cache)[((size_t)p * 2 + which) * e.d + (nn - (1 + which) * e.d)] =
-          from_f32<T>(v);
+      if (nn < e.d) {
+        reinterpret_cast<T*>(e.out_act)[(size_t)m * e.ld_act + nn] = from_f32<T>(v);
+        return;
+      }
+      pos = e.scratch_pos0 + 32 * (m >> 4) + (m & 15);
+    } else {
+      if (nn < e.d) return;  // queries of context rows are not needed
+      pos = e.cache_pos0 + (m - e.rows_block);
     }
+    const int which = nn >= 2 * e.d;  // 0: key, 1: value
+    const int col = nn - (1 + which) * e.d;
+    const int head = col / e.hd, c = col - head * e.hd;
+    if (!which)
+      reinterpret_cast<T*>(e.kcache)[((size_t)head * e.P + pos) * e.hd + c] = from_f32<T>(v);
+    else
+      reinterpret_cast<T*>(e.vcache)[(((size_t)head * (e.P >> 5) + (pos >> 5)) * e.hd + c) * 32 +
+                                     vt_slot<T>(pos & 31)] = from_f32<T>(v);
   }
 }
 
@@ -112,10 +128,11 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs g, EpiParams e) 
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Up to two row tiles, a chunk's weights and the matching A fragments are
+  // With one row tile a chunk's weights and the matching A fragments are
   // loaded together, one chunk ahead of the MFMAs, so neither latency is
-  // exposed; larger row counts (draft trees) load A at use to stay in registers.
-  constexpr bool PRE_A = MT <= 2;
+  // exposed; more row tiles load A at use, which keeps the register count low
+  // enough for two workgroups per CU.
+  constexpr bool PRE_A = MT == 1;
   constexpr int AF = PRE_A ? MT : 1;
   // A values outside [k_begin, k_end) or rows >= M are zeroed at use (this also
   // neutralises the clamped weight columns beyond the k range)
