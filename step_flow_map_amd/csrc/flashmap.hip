@@ -76,6 +76,7 @@ int cdiv(int a, int b) { return (a + b - 1) / b; }
 
 struct GemmPlan {
   int S, k_split, n_groups, grid, waves;
+  int tg;  // > 0: tile-group kernel with tg tiles per workgroup
 };
 
 // One workgroup per (16-row tile, k split).  Without a split there is no
@@ -87,6 +88,16 @@ GemmPlan plan_gemm(int N, int K, fm_dtype t) {
   GemmPlan p;
   p.n_groups = cdiv(N, 16);
   const int nch = std::max(1, cdiv(K, chunk));
+  p.tg = 0;
+  if (p.n_groups >= 256 && nch <= 8) {
+    // wide layer, short k: two tiles per workgroup of 8 waves, one chunk per wave
+    p.tg = 2;
+    p.waves = 8;
+    p.S = 1;
+    p.k_split = nch * chunk;
+    p.grid = cdiv(p.n_groups, p.tg);
+    return p;
+  }
   p.waves = p.n_groups < 256 ? 8 : 4;
   int S = 1;
   if (p.n_groups < 256 && nch > 4 * p.waves) S = std::min(GEMM_MAX_SPLIT, cdiv(256, p.n_groups));
@@ -238,21 +249,23 @@ namespace {
 
 // ------------------------------------------------------------------ launchers
 template <typename T, int MT, int EPI>
-void launch_gemm_mt(const GemmArgs& a, const EpiParams& e, int grid, int waves, hipStream_t st) {
-  if (waves == 8)
+void launch_gemm_mt(const GemmArgs& a, const EpiParams& e, int grid, int waves, int tg, hipStream_t st) {
+  if (tg == 2)
+    hipLaunchKernelGGL((gemm_tg_kernel<T, MT, 8, 2, EPI>), dim3(grid), dim3(8 * 64), 0, st, a, e);
+  else if (waves == 8)
     hipLaunchKernelGGL((gemm_kernel<T, MT, 8, EPI>), dim3(grid), dim3(8 * 64), 0, st, a, e);
   else
     hipLaunchKernelGGL((gemm_kernel<T, MT, 4, EPI>), dim3(grid), dim3(4 * 64), 0, st, a, e);
 }
 
 template <typename T, int EPI>
-fm_status launch_gemm_epi(const GemmArgs& a, const EpiParams& e, int grid, int waves, hipStream_t st) {
+fm_status launch_gemm_epi(const GemmArgs& a, const EpiParams& e, const GemmPlan& p, hipStream_t st) {
   switch (cdiv(a.M, 16)) {
-    case 1: launch_gemm_mt<T, 1, EPI>(a, e, grid, waves, st); break;
-    case 2: launch_gemm_mt<T, 2, EPI>(a, e, grid, waves, st); break;
-    case 3: launch_gemm_mt<T, 3, EPI>(a, e, grid, waves, st); break;
-    case 4: launch_gemm_mt<T, 4, EPI>(a, e, grid, waves, st); break;
-    case 5: launch_gemm_mt<T, 5, EPI>(a, e, grid, waves, st); break;
+    case 1: launch_gemm_mt<T, 1, EPI>(a, e, p.grid, p.waves, p.tg, st); break;
+    case 2: launch_gemm_mt<T, 2, EPI>(a, e, p.grid, p.waves, p.tg, st); break;
+    case 3: launch_gemm_mt<T, 3, EPI>(a, e, p.grid, p.waves, p.tg, st); break;
+    case 4: launch_gemm_mt<T, 4, EPI>(a, e, p.grid, p.waves, p.tg, st); break;
+    case 5: launch_gemm_mt<T, 5, EPI>(a, e, p.grid, p.waves, p.tg, st); break;
     default: return fail(FM_EINVAL, "contraction with %d rows exceeds 80", a.M);
   }
   FM_LAUNCHED("gemm_kernel");
@@ -279,11 +292,11 @@ fm_status gemm(fm_handle* h, int epi, const void* A, int lda, int M, const void*
   a.partial = h->at<float>(h->lay.partial);
   a.counters = h->at<uint32_t>(h->lay.counters);
   switch (epi) {
-    case EPI_F32: return launch_gemm_epi<T, EPI_F32>(a, e, p.grid, p.waves, st);
-    case EPI_ACT: return launch_gemm_epi<T, EPI_ACT>(a, e, p.grid, p.waves, st);
-    case EPI_GELU: return launch_gemm_epi<T, EPI_GELU>(a, e, p.grid, p.waves, st);
-    case EPI_RESID: return launch_gemm_epi<T, EPI_RESID>(a, e, p.grid, p.waves, st);
-    default: return launch_gemm_epi<T, EPI_QKV>(a, e, p.grid, p.waves, st);
+    case EPI_F32: return launch_gemm_epi<T, EPI_F32>(a, e, p, st);
+    case EPI_ACT: return launch_gemm_epi<T, EPI_ACT>(a, e, p, st);
+    case EPI_GELU: return launch_gemm_epi<T, EPI_GELU>(a, e, p, st);
+    case EPI_RESID: return launch_gemm_epi<T, EPI_RESID>(a, e, p, st);
+    default: return launch_gemm_epi<T, EPI_QKV>(a, e, p, st);
   }
 }
 

@@ -230,4 +230,97 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs g, EpiParams e) 
   }
 }
 
+// Tile-group variant for wide layers (many 16-row tiles, a k range of at most
+// NW chunks): a workgroup owns TT adjacent tiles and wave w takes chunks w,
+// w+NW, ...  For a chunk it loads the A fragments first (they are consumed
+// first, and loads complete in issue order), then the TT weight chunks, and
+// applies the A fragments to all TT tiles, so A is fetched once per TT tiles.
+// The waves then reduce through LDS in wave order and run the epilogue.
+template <typename T, int MT, int NW, int TT, int EPI>
+__global__ __launch_bounds__(NW * 64) void gemm_tg_kernel(GemmArgs g, EpiParams e) {
+  typedef typename Vec<T>::type VT;
+  constexpr int VE = ChunkT<T>::VE;
+  constexpr int KC = ChunkT<T>::KC;
+  constexpr int ELEMS = TT * MT * 256;  // outputs: TT tiles x MT*16 rows x 16 columns
+  constexpr int RED_U4 = NW * ELEMS / 4;
+  constexpr int TILE_U4 = NW * 512;
+  __shared__ uint4 smem[TILE_U4 > RED_U4 ? TILE_U4 : RED_U4];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int j = lane & 15, grp = lane >> 4;
+  const int n0 = blockIdx.x * 16 * TT;
+  const int nch = (g.K + KC - 1) / KC;
+  const T* A = reinterpret_cast<const T*>(g.A);
+  const T* W = reinterpret_cast<const T*>(g.W);
+  uint4* wt = smem + wave * 512;
+
+  const T* arow[MT];
+  bool aok[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int m = mt * 16 + j;
+    aok[mt] = m < g.M;
+    arow[mt] = A + (size_t)(aok[mt] ? m : 0) * g.lda;
+  }
+  f32x4 acc[TT][MT];
+#pragma unroll
+  for (int t = 0; t < TT; ++t)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int c = wave; c < nch; c += NW) {
+    const int k0 = c * KC;
+    // A: rows >= M and columns >= K read in-range addresses and are zeroed at use
+    VT af[MT][8];
+    bool kok[8];
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      const int k = k0 + (4 * st + grp) * VE;
+      kok[st] = k < g.K;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) af[mt][st] = vload<T>(arow[mt] + (kok[st] ? k : 0));
+    }
+    uint4 r[TT][8];
+#pragma unroll
+    for (int t = 0; t < TT; ++t) chunk_load<T>(r[t], W, g.ldw, n0 + 16 * t, g.N, k0, g.K);
+#pragma unroll
+    for (int t = 0; t < TT; ++t) {
+      chunk_to_lds(r[t], wt);
+      wave_lds_sync();
+#pragma unroll
+      for (int st = 0; st < 8; ++st) {
+        const VT b = as_vec<T>(chunk_frag(wt, st));
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) mma(acc[t][mt], (kok[st] && aok[mt]) ? af[mt][st] : vzero<VT>(), b);
+      }
+      wave_lds_sync();
+    }
+  }
+
+  // ---- fixed-order reduction over the waves
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(smem);
+#pragma unroll
+  for (int t = 0; t < TT; ++t)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[wave * ELEMS + ((t * MT + mt) * 4 + i) * 64 + lane] = acc[t][mt][i];
+  __syncthreads();
+  constexpr int PER_THREAD = (ELEMS + NW * 64 - 1) / (NW * 64);
+#pragma unroll
+  for (int r = 0; r < PER_THREAD; ++r) {
+    const int el = threadIdx.x + r * NW * 64;
+    if (el >= ELEMS) break;
+    const int ln = el & 63, q = el >> 6;  // q = (t*MT + mt)*4 + i
+    const int i = q & 3, tm = q >> 2;
+    const int mt = tm % MT, t = tm / MT;
+    const int m = mt * 16 + 4 * (ln >> 4) + i, n = n0 + 16 * t + (ln & 15);
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) v += red[w * ELEMS + el];
+    if (m < g.M && n < g.N) epilogue<T, EPI>(e, m, n, v);
+  }
+}
+
 }  // namespace fm
