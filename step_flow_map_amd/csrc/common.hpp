@@ -54,6 +54,18 @@ template <typename V> __device__ __forceinline__ V vzero();
 template <> __device__ __forceinline__ uint4 vzero<uint4>() { return make_uint4(0, 0, 0, 0); }
 template <> __device__ __forceinline__ float4 vzero<float4>() { return make_float4(0.f, 0.f, 0.f, 0.f); }
 
+// VE floats rounded to the storage type and packed into a vec
+template <typename T> __device__ __forceinline__ typename Vec<T>::type pack_vec(const float (&y)[Vec<T>::N]);
+template <> __device__ __forceinline__ uint4 pack_vec<bf16_t>(const float (&y)[8]) {
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w[i] = (uint32_t)f32_to_bf16(y[2 * i]) | ((uint32_t)f32_to_bf16(y[2 * i + 1]) << 16);
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+template <> __device__ __forceinline__ float4 pack_vec<float>(const float (&y)[4]) {
+  return make_float4(y[0], y[1], y[2], y[3]);
+}
+
 template <typename T>
 __device__ __forceinline__ typename Vec<T>::type vload(const T* p) {
   return *reinterpret_cast<const typename Vec<T>::type*>(p);
@@ -180,6 +192,15 @@ constexpr int COUNTER_STRIDE = 32;
 // wave's accesses in order.  (A release fence here would also wait for every
 // outstanding global load, draining the next chunk's prefetch.)
 __device__ __forceinline__ void wave_lds_sync() {}
+
+// Workgroup barrier that orders LDS accesses only.  __syncthreads() also waits
+// for every outstanding global load of the wave, which would drain loads that
+// are meant to stay in flight across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 __device__ __forceinline__ float gelu_tanh(float x) {
   const float k0 = 0.7978845608028654f;  // sqrt(2/pi)

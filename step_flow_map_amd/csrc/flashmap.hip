@@ -251,7 +251,7 @@ namespace {
 template <typename T, int MT, int EPI>
 void launch_gemm_mt(const GemmArgs& a, const EpiParams& e, int grid, int waves, int tg, hipStream_t st) {
   if (tg == 2)
-    hipLaunchKernelGGL((gemm_tg_kernel<T, MT, 8, 2, EPI>), dim3(grid), dim3(8 * 64), 0, st, a, e);
+    hipLaunchKernelGGL((gemm_tg_kernel<T, MT, 8, 2, EPI, false>), dim3(grid), dim3(8 * 64), 0, st, a, e, LnArgs{});
   else if (waves == 8)
     hipLaunchKernelGGL((gemm_kernel<T, MT, 8, EPI>), dim3(grid), dim3(8 * 64), 0, st, a, e);
   else
@@ -298,6 +298,46 @@ fm_status gemm(fm_handle* h, int epi, const void* A, int lda, int M, const void*
     case EPI_RESID: return launch_gemm_epi<T, EPI_RESID>(a, e, p, st);
     default: return launch_gemm_epi<T, EPI_QKV>(a, e, p, st);
   }
+}
+
+// LayerNorm + modulation of the 16 residual rows x fused into the contraction's
+// A operand; A_ctx supplies M_ctx further rows (already normalised) below them.
+bool ln_fusable(const fm_config& c, int B) { return B == 1 && cdiv(c.d, gemm_chunk(c.dtype)) <= 8; }
+
+template <typename T>
+fm_status gemm_ln(fm_handle* h, int epi, const float* x, const float* shift, const float* scale, const void* A_ctx,
+                  int M_ctx, const void* W, int N, int K, const EpiParams& e, hipStream_t st) {
+  if (cdiv(K, gemm_chunk(h->cfg.dtype)) > 8) return fail(FM_EINVAL, "fused LayerNorm needs k <= 8 chunks");
+  GemmArgs a;
+  a.A = A_ctx;
+  a.lda = K;
+  a.M = KB + M_ctx;
+  a.W = W;
+  a.ldw = K;
+  a.N = N;
+  a.K = K;
+  a.S = 1;
+  a.k_split = K;
+  a.partial = nullptr;
+  a.counters = nullptr;
+  LnArgs l;
+  l.h = x;
+  l.ldh = K;
+  l.shift = shift;
+  l.scale = scale;
+  l.eps = 1e-6f;
+  const dim3 grid(cdiv(cdiv(N, 16), 2)), block(8 * 64);
+  const bool two = a.M > 16;
+  if (epi == EPI_QKV && two)
+    hipLaunchKernelGGL((gemm_tg_kernel<T, 2, 8, 2, EPI_QKV, true>), grid, block, 0, st, a, e, l);
+  else if (epi == EPI_QKV)
+    hipLaunchKernelGGL((gemm_tg_kernel<T, 1, 8, 2, EPI_QKV, true>), grid, block, 0, st, a, e, l);
+  else if (epi == EPI_GELU && !two)
+    hipLaunchKernelGGL((gemm_tg_kernel<T, 1, 8, 2, EPI_GELU, true>), grid, block, 0, st, a, e, l);
+  else
+    return fail(FM_EINVAL, "no fused LayerNorm variant for this contraction");
+  FM_LAUNCHED("gemm_tg_kernel");
+  return FM_OK;
 }
 
 template <typename T>
@@ -517,6 +557,7 @@ fm_status draft_impl(fm_handle* h, const void* noise, int B, const void* new_fea
   const fm_config& c = h->cfg;
   const int d = c.d, F = c.mlp_mult * c.d, Mb = B * KB, L = c.L;
   const int C = h->ctx_len + n_new;
+  const bool fuse_ln = ln_fusable(c, B);
   T* act_qkv = h->at<T>(h->lay.act_qkv);
   T* act_d = h->at<T>(h->lay.act_d);
   T* act_f = h->at<T>(h->lay.act_f);
@@ -543,7 +584,6 @@ fm_status draft_impl(fm_handle* h, const void* noise, int B, const void* new_fea
     const int m_qkv = Mb + (j == 0 ? n_new : 0);
     for (int l = 0; l < L; ++l) {
       const float* mv = mods + (size_t)6 * l * d;  // shift1 scale1 gate1 shift2 scale2 gate2
-      FM_TRY(ln_mod<T>(h, hres, Mb, mv + 0 * d, mv + 1 * d, act_qkv, d, st));
       {
         EpiParams e{};
         e.bias = blk(h, l, B_BQKV);
@@ -553,7 +593,13 @@ fm_status draft_impl(fm_handle* h, const void* noise, int B, const void* new_fea
         qkv_cache_params<T>(h, l, e);
         e.cache_pos0 = h->ctx_len;
         e.col_offset = 0;
-        FM_TRY(gemm<T>(h, EPI_QKV, act_qkv, d, m_qkv, blk(h, l, B_WQKV), 3 * d, d, e, st));
+        if (fuse_ln) {
+          FM_TRY(gemm_ln<T>(h, EPI_QKV, hres, mv + 0 * d, mv + 1 * d, act_qkv + (size_t)Mb * d, m_qkv - Mb,
+                            blk(h, l, B_WQKV), 3 * d, d, e, st));
+        } else {
+          FM_TRY(ln_mod<T>(h, hres, Mb, mv + 0 * d, mv + 1 * d, act_qkv, d, st));
+          FM_TRY(gemm<T>(h, EPI_QKV, act_qkv, d, m_qkv, blk(h, l, B_WQKV), 3 * d, d, e, st));
+        }
       }
       FM_TRY(attention<T>(h, l, B, C, st));
       {
@@ -564,16 +610,22 @@ fm_status draft_impl(fm_handle* h, const void* noise, int B, const void* new_fea
         e.gate = mv + 2 * d;
         FM_TRY(gemm<T>(h, EPI_RESID, attn_o, d, Mb, blk(h, l, B_WO), d, d, e, st));
       }
-      FM_TRY(ln_mod<T>(h, hres, Mb, mv + 3 * d, mv + 4 * d, act_d, d, st));
       {
         EpiParams e{};
         e.bias = blk(h, l, B_B1);
         e.out_act = act_f;
         e.ld_act = F;
         const int pk = (j == 0 && l == 0) ? FM_PROBE_FC1 : -1;
-        FM_TRY(probe_begin(h, pk, st));
-        FM_TRY(gemm<T>(h, EPI_GELU, act_d, d, Mb, blk(h, l, B_W1), F, d, e, st));
-        FM_TRY(probe_end(h, pk, st));
+        if (fuse_ln) {
+          FM_TRY(probe_begin(h, pk, st));
+          FM_TRY(gemm_ln<T>(h, EPI_GELU, hres, mv + 3 * d, mv + 4 * d, nullptr, 0, blk(h, l, B_W1), F, d, e, st));
+          FM_TRY(probe_end(h, pk, st));
+        } else {
+          FM_TRY(ln_mod<T>(h, hres, Mb, mv + 3 * d, mv + 4 * d, act_d, d, st));
+          FM_TRY(probe_begin(h, pk, st));
+          FM_TRY(gemm<T>(h, EPI_GELU, act_d, d, Mb, blk(h, l, B_W1), F, d, e, st));
+          FM_TRY(probe_end(h, pk, st));
+        }
       }
       {
         EpiParams e{};

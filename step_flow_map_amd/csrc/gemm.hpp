@@ -230,23 +230,52 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs g, EpiParams e) 
   }
 }
 
+// LayerNorm fused into the A operand (tile-group kernel): rows 0..15 of the
+// contraction are LN(h[r]) * (1 + scale) + shift rounded to the storage type,
+// computed inside the kernel from the float32 residual rows; rows 16.. come
+// from GemmArgs::A as usual (context rows, already normalised).
+struct LnArgs {
+  const float* h;      // [16][ldh] float32
+  int ldh;
+  const float* shift;  // [K]
+  const float* scale;  // [K]
+  float eps;
+};
+
 // Tile-group variant for wide layers (many 16-row tiles, a k range of at most
 // NW chunks): a workgroup owns TT adjacent tiles and wave w takes chunks w,
-// w+NW, ...  For a chunk it loads the A fragments first (they are consumed
-// first, and loads complete in issue order), then the TT weight chunks, and
-// applies the A fragments to all TT tiles, so A is fetched once per TT tiles.
-// The waves then reduce through LDS in wave order and run the epilogue.
-template <typename T, int MT, int NW, int TT, int EPI>
-__global__ __launch_bounds__(NW * 64) void gemm_tg_kernel(GemmArgs g, EpiParams e) {
+// w+NW, ...  For a chunk it loads the A operand first (it is consumed first,
+// and loads complete in issue order), then the TT weight chunks, and applies
+// the A fragments to all TT tiles, so A is fetched once per TT tiles.  The
+// waves then reduce through LDS in wave order and run the epilogue.
+//
+// With LN the k range is at most NW chunks, so each wave holds one chunk of
+// the 16 residual rows; it computes the mean and the sum of squared deviations
+// of its columns per row, the workgroup combines the waves' pairs in wave
+// order (pairwise update of Chan, Golub and LeVeque), and every wave then
+// normalises, modulates and rounds its own fragments.
+template <typename T, int MT, int NW, int TT, int EPI, bool LN>
+__global__ __launch_bounds__(NW * 64) void gemm_tg_kernel(GemmArgs g, EpiParams e, LnArgs ln) {
   typedef typename Vec<T>::type VT;
   constexpr int VE = ChunkT<T>::VE;
   constexpr int KC = ChunkT<T>::KC;
   constexpr int ELEMS = TT * MT * 256;  // outputs: TT tiles x MT*16 rows x 16 columns
   constexpr int RED_U4 = NW * ELEMS / 4;
   constexpr int TILE_U4 = NW * 512;
+  constexpr int KMAX = NW * KC;                            // LN: longest k range
+  constexpr int MODQ = LN ? (KMAX / 4 + NW * 64 - 1) / (NW * 64) : 1;  // float4 of scale (and shift) per thread
+  constexpr int HQ = VE / 4;                               // float4 per fragment of residual
+  constexpr int SHIFT_OFF = MODQ * NW * 64 * 4;
   __shared__ uint4 smem[TILE_U4 > RED_U4 ? TILE_U4 : RED_U4];
+  __shared__ __align__(16) float smod[LN ? 2 * MODQ * NW * 64 * 4 : 1];  // scale, then shift at SHIFT_OFF
+  __shared__ float sstat[LN ? NW : 1][16][2];              // per wave and row: mean, M2
+  // LN with context rows: their fragments wait in LDS (wave-private) rather
+  // than in registers while the weights are in flight
+  static_assert(!LN || MT <= 2, "fused LayerNorm supports at most 16 further rows");
+  constexpr bool CTX_LDS = LN && MT == 2;
+  __shared__ uint4 sctx[CTX_LDS ? NW : 1][CTX_LDS ? 8 : 1][64];
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int j = lane & 15, grp = lane >> 4;
   const int n0 = blockIdx.x * 16 * TT;
   const int nch = (g.K + KC - 1) / KC;
@@ -254,13 +283,15 @@ __global__ __launch_bounds__(NW * 64) void gemm_tg_kernel(GemmArgs g, EpiParams 
   const T* W = reinterpret_cast<const T*>(g.W);
   uint4* wt = smem + wave * 512;
 
+  // rows of A: with LN, row tile 0 is computed and tiles 1.. read A rows 0..
+  constexpr int MT0 = LN ? 1 : 0;
   const T* arow[MT];
   bool aok[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int m = mt * 16 + j;
     aok[mt] = m < g.M;
-    arow[mt] = A + (size_t)(aok[mt] ? m : 0) * g.lda;
+    arow[mt] = A + (size_t)(aok[mt] && mt >= MT0 ? m - 16 * MT0 : 0) * g.lda;
   }
   f32x4 acc[TT][MT];
 #pragma unroll
@@ -268,21 +299,114 @@ __global__ __launch_bounds__(NW * 64) void gemm_tg_kernel(GemmArgs g, EpiParams 
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int c = wave; c < nch; c += NW) {
+  for (int c = wave; LN ? c == wave : c < nch; c += NW) {
+    const bool has = c < nch;  // LN: every wave takes part in the statistics
     const int k0 = c * KC;
-    // A: rows >= M and columns >= K read in-range addresses and are zeroed at use
-    VT af[MT][8];
     bool kok[8];
 #pragma unroll
-    for (int st = 0; st < 8; ++st) {
-      const int k = k0 + (4 * st + grp) * VE;
-      kok[st] = k < g.K;
+    for (int st = 0; st < 8; ++st) kok[st] = has && k0 + (4 * st + grp) * VE < g.K;
+    // ---- issue: residual rows, modulation, A rows, weights.  Addresses are
+    // clamped in range and nothing here is conditional, so no load waits for
+    // another one before the statistics need the residual rows.
+    float4 hv[LN ? 8 : 1][HQ];
+    float4 mv[MODQ], mv2[MODQ];
+    if constexpr (LN) {
+      const float* hr = ln.h + (size_t)j * ln.ldh;
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) af[mt][st] = vload<T>(arow[mt] + (kok[st] ? k : 0));
+      for (int st = 0; st < 8; ++st) {
+        const int k = kok[st] ? k0 + (4 * st + grp) * VE : 0;
+#pragma unroll
+        for (int q = 0; q < HQ; ++q) hv[st][q] = *reinterpret_cast<const float4*>(hr + k + 4 * q);
+      }
+      const int kq = g.K / 4;
+#pragma unroll
+      for (int q = 0; q < MODQ; ++q) {
+        const int idx = min(tid + q * NW * 64, kq - 1);
+        mv[q] = reinterpret_cast<const float4*>(ln.scale)[idx];
+        mv2[q] = reinterpret_cast<const float4*>(ln.shift)[idx];
+      }
+    }
+    VT af[MT][8];
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      const int k = kok[st] ? k0 + (4 * st + grp) * VE : 0;
+#pragma unroll
+      for (int mt = MT0; mt < MT; ++mt) af[mt][st] = vload<T>(arow[mt] + k);
     }
     uint4 r[TT][8];
 #pragma unroll
     for (int t = 0; t < TT; ++t) chunk_load<T>(r[t], W, g.ldw, n0 + 16 * t, g.N, k0, g.K);
+    if constexpr (LN) {
+      // every load above is issued before the statistics consume the first one
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (CTX_LDS) {
+#pragma unroll
+        for (int st = 0; st < 8; ++st) sctx[wave][st][lane] = __builtin_bit_cast(uint4, af[1][st]);
+      }
+      // smod holds exactly MODQ float4 of each per thread: entries past K are never read
+#pragma unroll
+      for (int q = 0; q < MODQ; ++q) {
+        *reinterpret_cast<float4*>(&smod[4 * (tid + q * NW * 64)]) = mv[q];
+        *reinterpret_cast<float4*>(&smod[SHIFT_OFF + 4 * (tid + q * NW * 64)]) = mv2[q];
+      }
+      // this wave's columns of row j: mean and sum of squared deviations
+      const int nw = has ? min(KC, g.K - k0) : 0;
+      float sum = 0.f;
+#pragma unroll
+      for (int st = 0; st < 8; ++st) {
+        const float mk = kok[st] ? 1.f : 0.f;
+#pragma unroll
+        for (int q = 0; q < HQ; ++q) sum += mk * ((hv[st][q].x + hv[st][q].y) + (hv[st][q].z + hv[st][q].w));
+      }
+      sum += __shfl_xor(sum, 16, 64);
+      sum += __shfl_xor(sum, 32, 64);
+      const float mw = sum / (float)max(nw, 1);
+      float m2 = 0.f;
+#pragma unroll
+      for (int st = 0; st < 8; ++st) {
+        const float mk = kok[st] ? 1.f : 0.f;
+#pragma unroll
+        for (int q = 0; q < HQ; ++q) {
+          const float a = hv[st][q].x - mw, b = hv[st][q].y - mw, cc = hv[st][q].z - mw, d = hv[st][q].w - mw;
+          m2 += mk * ((a * a + b * b) + (cc * cc + d * d));
+        }
+      }
+      m2 += __shfl_xor(m2, 16, 64);
+      m2 += __shfl_xor(m2, 32, 64);
+      if (grp == 0) {
+        sstat[wave][j][0] = mw;
+        sstat[wave][j][1] = m2;
+      }
+      lds_barrier();  // the weight loads stay in flight
+      float mean = 0.f, M2 = 0.f, n = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float nb = (float)max(0, min(KC, g.K - w * KC));
+        const float mb = sstat[w][j][0], m2b = sstat[w][j][1];
+        const float nn = n + nb, delta = mb - mean;
+        const float f = nb > 0.f ? nb / nn : 0.f;
+        mean += delta * f;
+        M2 += nb > 0.f ? m2b + delta * delta * (n * f) : 0.f;
+        n = nn;
+      }
+      const float rstd = 1.f / sqrtf(M2 / (float)g.K + ln.eps);
+#pragma unroll
+      for (int st = 0; st < 8; ++st) {
+        const int k = kok[st] ? k0 + (4 * st + grp) * VE : 0;
+        float y[VE];
+#pragma unroll
+        for (int q = 0; q < HQ; ++q) {
+          const float4 sc = *reinterpret_cast<const float4*>(&smod[k + 4 * q]);
+          const float4 sh = *reinterpret_cast<const float4*>(&smod[SHIFT_OFF + k + 4 * q]);
+          y[4 * q + 0] = ((hv[st][q].x - mean) * rstd) * (1.f + sc.x) + sh.x;
+          y[4 * q + 1] = ((hv[st][q].y - mean) * rstd) * (1.f + sc.y) + sh.y;
+          y[4 * q + 2] = ((hv[st][q].z - mean) * rstd) * (1.f + sc.z) + sh.z;
+          y[4 * q + 3] = ((hv[st][q].w - mean) * rstd) * (1.f + sc.w) + sh.w;
+        }
+        af[0][st] = pack_vec<T>(y);
+      }
+    }
+    if (!has) break;
 #pragma unroll
     for (int t = 0; t < TT; ++t) {
       chunk_to_lds(r[t], wt);
@@ -291,7 +415,10 @@ __global__ __launch_bounds__(NW * 64) void gemm_tg_kernel(GemmArgs g, EpiParams 
       for (int st = 0; st < 8; ++st) {
         const VT b = as_vec<T>(chunk_frag(wt, st));
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) mma(acc[t][mt], (kok[st] && aok[mt]) ? af[mt][st] : vzero<VT>(), b);
+        for (int mt = 0; mt < MT; ++mt) {
+          const VT a = (CTX_LDS && mt == 1) ? as_vec<T>(sctx[wave][st][lane]) : af[mt][st];
+          mma(acc[t][mt], (kok[st] && aok[mt]) ? a : vzero<VT>(), b);
+        }
       }
       wave_lds_sync();
     }
@@ -310,12 +437,12 @@ __global__ __launch_bounds__(NW * 64) void gemm_tg_kernel(GemmArgs g, EpiParams 
   constexpr int PER_THREAD = (ELEMS + NW * 64 - 1) / (NW * 64);
 #pragma unroll
   for (int r = 0; r < PER_THREAD; ++r) {
-    const int el = threadIdx.x + r * NW * 64;
+    const int el = tid + r * NW * 64;
     if (el >= ELEMS) break;
-    const int ln = el & 63, q = el >> 6;  // q = (t*MT + mt)*4 + i
+    const int ln_ = el & 63, q = el >> 6;  // q = (t*MT + mt)*4 + i
     const int i = q & 3, tm = q >> 2;
     const int mt = tm % MT, t = tm / MT;
-    const int m = mt * 16 + 4 * (ln >> 4) + i, n = n0 + 16 * t + (ln & 15);
+    const int m = mt * 16 + 4 * (ln_ >> 4) + i, n = n0 + 16 * t + (ln_ & 15);
     float v = 0.f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) v += red[w * ELEMS + el];

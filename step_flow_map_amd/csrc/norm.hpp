@@ -27,17 +27,21 @@ __device__ __forceinline__ float block_sum(float v, float* sh) {
 template <typename T, int PER>
 __global__ __launch_bounds__(256) void ln_mod_kernel(const float* x, int ldx, int d, const float* shift,
                                                      const float* scale, T* out, int ldo, float eps) {
-  __shared__ float sh[4];
+  __shared__ float red[4];
   const float* row = x + (size_t)blockIdx.x * ldx;
-  float v[PER];
+  float v[PER], sc[PER], sh[PER];
   float s = 0.f;
+  // the modulation is loaded together with the row, not after the reductions
 #pragma unroll
   for (int p = 0; p < PER; ++p) {
     const int c = threadIdx.x + p * 256;
-    v[p] = c < d ? row[c] : 0.f;
+    const int cc = c < d ? c : 0;
+    v[p] = c < d ? row[cc] : 0.f;
+    sc[p] = scale ? scale[cc] : 0.f;
+    sh[p] = scale ? shift[cc] : 0.f;
     s += v[p];
   }
-  const float mean = block_sum<T, 256>(s, sh) / (float)d;
+  const float mean = block_sum<T, 256>(s, red) / (float)d;
   float q = 0.f;
 #pragma unroll
   for (int p = 0; p < PER; ++p) {
@@ -45,7 +49,7 @@ __global__ __launch_bounds__(256) void ln_mod_kernel(const float* x, int ldx, in
     const float dv = c < d ? v[p] - mean : 0.f;
     q += dv * dv;
   }
-  const float var = block_sum<T, 256>(q, sh) / (float)d;
+  const float var = block_sum<T, 256>(q, red) / (float)d;
   const float rstd = 1.f / sqrtf(var + eps);
   T* o = out + (size_t)blockIdx.x * ldo;
 #pragma unroll
@@ -53,7 +57,7 @@ __global__ __launch_bounds__(256) void ln_mod_kernel(const float* x, int ldx, in
     const int c = threadIdx.x + p * 256;
     if (c < d) {
       float y = (v[p] - mean) * rstd;
-      if (scale) y = y * (1.f + scale[c]) + shift[c];
+      if (scale) y = y * (1.f + sc[p]) + sh[p];
       o[c] = from_f32<T>(y);
     }
   }

@@ -17,6 +17,10 @@ TINY = synth.CONFIGS["tiny"]
 # bf16 with ragged vocabulary (1000 = 62.5 column tiles, 31.25 row chunks) and
 # a context width whose fused length 5*520 = 2600 is not a multiple of the chunk
 SMALL_BF16 = TINY.with_(name="small_bf16", dtype="bf16", V=1000, H=520)
+# width 384 = one and a half weight chunks (a ragged k range in every
+# contraction and in the fused LayerNorm), head width 128, and a context of 308
+# rows = 10 key blocks (the last one partial) spread over several ranges
+MID_BF16 = TINY.with_(name="mid_bf16", dtype="bf16", V=2000, d=384, nh=3, H=520, c_prefill=300)
 
 
 def _case(cfg, variant="random", B=1, seed_noise=None):
@@ -26,7 +30,7 @@ def _case(cfg, variant="random", B=1, seed_noise=None):
     return w, feats, noise
 
 
-@pytest.mark.parametrize("cfg", [TINY, SMALL_BF16], ids=["tiny_f32", "small_bf16"])
+@pytest.mark.parametrize("cfg", [TINY, SMALL_BF16, MID_BF16], ids=["tiny_f32", "small_bf16", "mid_bf16"])
 @pytest.mark.parametrize("variant", ["random", "unit_gate", "gate_zero"])
 def test_draft_matches_oracle(cfg, variant):
     print(f"[draft parity] {cfg.name} {variant}", flush=True)
@@ -110,7 +114,7 @@ def test_errors_enqueue_nothing():
     assert e.value.status == fm.FM_ECAPACITY
 
 
-@pytest.mark.parametrize("cfg", [TINY, SMALL_BF16], ids=["tiny_f32", "small_bf16"])
+@pytest.mark.parametrize("cfg", [TINY, SMALL_BF16, MID_BF16], ids=["tiny_f32", "small_bf16", "mid_bf16"])
 def test_two_step_schedule(cfg):
     cfg = cfg.with_(times=(0.0, 0.5, 1.0))
     w, feats, noise = _case(cfg)
@@ -121,7 +125,7 @@ def test_two_step_schedule(cfg):
     print(f"  2-step {cfg.name}: logit error {rel:.2e}, near-ties {ties}")
 
 
-@pytest.mark.parametrize("cfg", [TINY, SMALL_BF16], ids=["tiny_f32", "small_bf16"])
+@pytest.mark.parametrize("cfg", [TINY, SMALL_BF16, MID_BF16], ids=["tiny_f32", "small_bf16", "mid_bf16"])
 def test_draft_tree_of_four(cfg):
     cfg = cfg.with_(B=4)
     w, feats, noise = _case(cfg, B=4)
