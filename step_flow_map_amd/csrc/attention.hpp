@@ -19,9 +19,11 @@
 // hi + lo bf16 parts, two MFMAs per tile, which keeps P to 16 significant bits
 // (float32 accumulation throughout); float storage multiplies in float32.
 //
-// Work split: a workgroup (4 waves) per (branch, head, block range); waves take
-// the range's blocks round-robin with the next block's loads in flight while
-// the current one is computed, then merge their (max, sum, output) through LDS.
+// Work split: a workgroup (NW waves) per (branch, head, block range); waves
+// take the range's blocks round-robin with the next block's loads in flight
+// while the current one is computed, then merge their (max, sum, output)
+// through LDS.  Short contexts use a single range, so no merge crosses
+// workgroups.
 // With several ranges per (branch, head) each publishes its merged state with
 // coherent stores and the last to arrive (at most 8) merges them in range order.
 // Results never depend on scheduling.
@@ -59,8 +61,8 @@ struct AttnArgs {
   float scale;         // 1/sqrt(hd)
 };
 
-template <typename T, int HD>
-__global__ __launch_bounds__(256) void attention_kernel(AttnArgs g) {
+template <typename T, int HD, int NW>
+__global__ __launch_bounds__(NW * 64) void attention_kernel(AttnArgs g) {
   typedef typename Vec<T>::type VT;
   constexpr int KB = 16;              // block rows (queries) per branch
   constexpr int VE = Vec<T>::N;
@@ -68,8 +70,8 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnArgs g) {
   constexpr int OT = HD / 16;         // 16-dim output tiles
   constexpr int PS = 32 / (4 * VE);   // P.V steps per block: bf16 1, float 2
   constexpr bool BF = sizeof(T) == 2;
-  __shared__ float so[4][KB][HD + 4];
-  __shared__ float sm[4][KB], sl[4][KB];
+  __shared__ float so[NW][KB][HD + 4];
+  __shared__ float sm[NW][KB], sl[NW][KB];
   __shared__ int flag;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -213,20 +215,20 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnArgs g) {
     }
   };
 
-  // blocks blo + wave, +4, ... with the next block's loads in flight
+  // blocks blo + wave, +NW, ... with the next block's loads in flight
   Tile t0, t1;
   int bi = blo + wave;
   if (bi < bhi) load(t0, bi);
-  for (; bi < bhi; bi += 8) {
-    if (bi + 4 < bhi) load(t1, bi + 4);
+  for (; bi < bhi; bi += 2 * NW) {
+    if (bi + NW < bhi) load(t1, bi + NW);
     process(t0, bi);
-    if (bi + 4 < bhi) {
-      if (bi + 8 < bhi) load(t0, bi + 8);
-      process(t1, bi + 4);
+    if (bi + NW < bhi) {
+      if (bi + 2 * NW < bhi) load(t0, bi + 2 * NW);
+      process(t1, bi + NW);
     }
   }
 
-  // ---- merge the four waves (fixed order) through LDS
+  // ---- merge the waves (fixed order) through LDS
 #pragma unroll
   for (int ot = 0; ot < OT; ++ot)
     *reinterpret_cast<float4*>(&so[wave][j][16 * ot + 4 * grp]) = make_float4(o[ot][0], o[ot][1], o[ot][2], o[ot][3]);
@@ -235,16 +237,16 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnArgs g) {
     sl[wave][j] = l_run;
   }
   __syncthreads();
-  constexpr int CPT = KB * HD / 256;  // output columns per thread (8 or 4)
+  constexpr int CPT = KB * HD / (NW * 64);  // output columns per thread
   const int row = tid / (HD / CPT), c0 = (tid % (HD / CPT)) * CPT;
   float M = -INFINITY;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) M = fmaxf(M, sm[w][row]);
+  for (int w = 0; w < NW; ++w) M = fmaxf(M, sm[w][row]);
   float Lsum = 0.f, acc[CPT];
 #pragma unroll
   for (int c = 0; c < CPT; ++c) acc[c] = 0.f;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
+  for (int w = 0; w < NW; ++w) {
     const float wt = expf(sm[w][row] - M);  // 0 for waves without blocks
     Lsum += wt * sl[w][row];
 #pragma unroll

@@ -59,6 +59,7 @@ fm_status fail(fm_status st, const char* fmt, ...) {
 
 constexpr int KB = 16;             // block rows per branch (K)
 constexpr int ATT_MAX_RANGES = ATT_RANGES_MAX;
+constexpr int ATT_WAVES = 8;  // waves per attention workgroup
 constexpr int GEMM_MAX_SPLIT = GEMM_SPLIT_MAX;
 constexpr int LM_WAVES = 8;
 constexpr int LM_GRID = 256;
@@ -98,6 +99,16 @@ GemmPlan plan_gemm(int N, int K, fm_dtype t) {
     p.grid = cdiv(p.n_groups, p.tg);
     return p;
   }
+  if (p.n_groups < 256 && nch >= 16 && nch <= 4 * GEMM_MAX_SPLIT) {
+    // narrow layer, long k: one tile and four chunks (one a wave) per workgroup
+    // of 4 waves, up to 8 splits of k summed by the last split to arrive
+    p.tg = 1;
+    p.waves = 4;
+    p.S = cdiv(nch, 4);
+    p.k_split = 4 * chunk;
+    p.grid = p.n_groups * p.S;
+    return p;
+  }
   p.waves = p.n_groups < 256 ? 8 : 4;
   int S = 1;
   if (p.n_groups < 256 && nch > 4 * p.waves) S = std::min(GEMM_MAX_SPLIT, cdiv(256, p.n_groups));
@@ -125,10 +136,12 @@ struct AttnPlan {
   int n_ranges, blocks_per_range;
 };
 
-// n_blocks 32-key blocks of one (branch, head) over at most 8 ranges
+// n_blocks 32-key blocks of one (branch, head) over at most 8 ranges of a
+// workgroup of ATT_WAVES waves: one range while no wave takes more than three
+// blocks (no merge across workgroups), else ranges of about two blocks a wave
 AttnPlan plan_attention(int n_blocks) {
   AttnPlan p;
-  const int r = std::min(ATT_MAX_RANGES, n_blocks);
+  const int r = n_blocks <= 3 * ATT_WAVES ? 1 : std::min(ATT_MAX_RANGES, cdiv(n_blocks, 2 * ATT_WAVES));
   p.blocks_per_range = cdiv(n_blocks, r);
   p.n_ranges = cdiv(n_blocks, p.blocks_per_range);
   return p;
@@ -252,6 +265,8 @@ template <typename T, int MT, int EPI>
 void launch_gemm_mt(const GemmArgs& a, const EpiParams& e, int grid, int waves, int tg, hipStream_t st) {
   if (tg == 2)
     hipLaunchKernelGGL((gemm_tg_kernel<T, MT, 8, 2, EPI, false>), dim3(grid), dim3(8 * 64), 0, st, a, e, LnArgs{});
+  else if (tg == 1)
+    hipLaunchKernelGGL((gemm_tg_kernel<T, MT, 4, 1, EPI, false>), dim3(grid), dim3(4 * 64), 0, st, a, e, LnArgs{});
   else if (waves == 8)
     hipLaunchKernelGGL((gemm_kernel<T, MT, 8, EPI>), dim3(grid), dim3(8 * 64), 0, st, a, e);
   else
@@ -418,9 +433,9 @@ fm_status attention(fm_handle* h, int l, int B, int C, hipStream_t st) {
   a.scale = 1.0f / std::sqrt((float)hd);
   const int grid = B * c.n_heads * p.n_ranges;
   if (hd == 128)
-    hipLaunchKernelGGL((attention_kernel<T, 128>), dim3(grid), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((attention_kernel<T, 128, ATT_WAVES>), dim3(grid), dim3(ATT_WAVES * 64), 0, st, a);
   else
-    hipLaunchKernelGGL((attention_kernel<T, 64>), dim3(grid), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((attention_kernel<T, 64, ATT_WAVES>), dim3(grid), dim3(ATT_WAVES * 64), 0, st, a);
   FM_LAUNCHED("attention_kernel");
   return FM_OK;
 }

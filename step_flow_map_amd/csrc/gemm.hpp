@@ -277,8 +277,11 @@ __global__ __launch_bounds__(NW * 64) void gemm_tg_kernel(GemmArgs g, EpiParams 
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int j = lane & 15, grp = lane >> 4;
-  const int n0 = blockIdx.x * 16 * TT;
-  const int nch = (g.K + KC - 1) / KC;
+  const int group = blockIdx.x / g.S, split = blockIdx.x % g.S;
+  const int n0 = group * 16 * TT;
+  const int k_begin = split * g.k_split;
+  const int k_end = min(g.K, k_begin + g.k_split);
+  const int nch = k_end > k_begin ? (k_end - k_begin + KC - 1) / KC : 0;
   const T* A = reinterpret_cast<const T*>(g.A);
   const T* W = reinterpret_cast<const T*>(g.W);
   uint4* wt = smem + wave * 512;
@@ -301,10 +304,10 @@ __global__ __launch_bounds__(NW * 64) void gemm_tg_kernel(GemmArgs g, EpiParams 
 
   for (int c = wave; LN ? c == wave : c < nch; c += NW) {
     const bool has = c < nch;  // LN: every wave takes part in the statistics
-    const int k0 = c * KC;
+    const int k0 = k_begin + c * KC;
     bool kok[8];
 #pragma unroll
-    for (int st = 0; st < 8; ++st) kok[st] = has && k0 + (4 * st + grp) * VE < g.K;
+    for (int st = 0; st < 8; ++st) kok[st] = has && k0 + (4 * st + grp) * VE < k_end;
     // ---- issue: residual rows, modulation, A rows, weights.  Addresses are
     // clamped in range and nothing here is conditional, so no load waits for
     // another one before the statistics need the residual rows.
@@ -335,7 +338,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_tg_kernel(GemmArgs g, EpiParams 
     }
     uint4 r[TT][8];
 #pragma unroll
-    for (int t = 0; t < TT; ++t) chunk_load<T>(r[t], W, g.ldw, n0 + 16 * t, g.N, k0, g.K);
+    for (int t = 0; t < TT; ++t) chunk_load<T>(r[t], W, g.ldw, n0 + 16 * t, g.N, k0, k_end);
     if constexpr (LN) {
       // every load above is issued before the statistics consume the first one
       __builtin_amdgcn_sched_barrier(0);
@@ -435,18 +438,46 @@ __global__ __launch_bounds__(NW * 64) void gemm_tg_kernel(GemmArgs g, EpiParams 
       for (int i = 0; i < 4; ++i) red[wave * ELEMS + ((t * MT + mt) * 4 + i) * 64 + lane] = acc[t][mt][i];
   __syncthreads();
   constexpr int PER_THREAD = (ELEMS + NW * 64 - 1) / (NW * 64);
+  float val[PER_THREAD];
+  int em[PER_THREAD], en[PER_THREAD];
 #pragma unroll
   for (int r = 0; r < PER_THREAD; ++r) {
     const int el = tid + r * NW * 64;
-    if (el >= ELEMS) break;
     const int ln_ = el & 63, q = el >> 6;  // q = (t*MT + mt)*4 + i
     const int i = q & 3, tm = q >> 2;
     const int mt = tm % MT, t = tm / MT;
-    const int m = mt * 16 + 4 * (ln_ >> 4) + i, n = n0 + 16 * t + (ln_ & 15);
+    em[r] = el < ELEMS ? mt * 16 + 4 * (ln_ >> 4) + i : g.M;
+    en[r] = n0 + 16 * t + (ln_ & 15);
+    float v = 0.f;
+    if (el < ELEMS) {
+#pragma unroll
+      for (int w = 0; w < NW; ++w) v += red[w * ELEMS + el];
+    }
+    val[r] = v;
+  }
+  if (g.S == 1) {
+#pragma unroll
+    for (int r = 0; r < PER_THREAD; ++r)
+      if (em[r] < g.M && en[r] < g.N) epilogue<T, EPI>(e, em[r], en[r], val[r]);
+    return;
+  }
+  // ---- split k: publish, the last split of the tile group sums in split order
+  __shared__ int flag;
+#pragma unroll
+  for (int r = 0; r < PER_THREAD; ++r)
+    if (em[r] < g.M && en[r] < g.N) st_coh(&g.partial[((size_t)split * g.M + em[r]) * g.N + en[r]], val[r]);
+  if (!arrive(&g.counters[group * COUNTER_STRIDE], (uint32_t)g.S, &flag)) return;
+#pragma unroll
+  for (int r = 0; r < PER_THREAD; ++r) {
+    const bool ok = em[r] < g.M && en[r] < g.N;
+    float pv[GEMM_SPLIT_MAX];
+#pragma unroll
+    for (int ss = 0; ss < GEMM_SPLIT_MAX; ++ss)
+      pv[ss] = (ok && ss < g.S) ? ld_coh(&g.partial[((size_t)ss * g.M + em[r]) * g.N + en[r]]) : 0.f;
     float v = 0.f;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) v += red[w * ELEMS + el];
-    if (m < g.M && n < g.N) epilogue<T, EPI>(e, m, n, v);
+    for (int ss = 0; ss < GEMM_SPLIT_MAX; ++ss) v += pv[ss];
+    if (ok) epilogue<T, EPI>(e, em[r], en[r], v);
   }
 }
 
