@@ -66,6 +66,17 @@ template <> __device__ __forceinline__ float4 pack_vec<float>(const float (&y)[4
   return make_float4(y[0], y[1], y[2], y[3]);
 }
 
+// v if keep, else zero, without a branch or a select on the vector
+__device__ __forceinline__ uint4 vkeep(uint4 v, bool keep) {
+  const uint32_t m = keep ? ~0u : 0u;
+  return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
+}
+__device__ __forceinline__ float4 vkeep(float4 v, bool keep) {
+  const uint32_t m = keep ? ~0u : 0u;
+  return make_float4(__uint_as_float(__float_as_uint(v.x) & m), __uint_as_float(__float_as_uint(v.y) & m),
+                     __uint_as_float(__float_as_uint(v.z) & m), __uint_as_float(__float_as_uint(v.w) & m));
+}
+
 template <typename T>
 __device__ __forceinline__ typename Vec<T>::type vload(const T* p) {
   return *reinterpret_cast<const typename Vec<T>::type*>(p);
@@ -94,6 +105,8 @@ __device__ __forceinline__ float velem(float4 v, int e) {
 
 // Transpose a VxV block held as V row vectors in[r] (r = k index, element t =
 // column) into V column vectors out[t] (element r = k index).
+// Each output word takes one bf16 from each of two input words: one byte
+// permute (v_perm_b32: bytes 0-3 of the second operand, 4-7 of the first).
 __device__ __forceinline__ void transpose_block(const uint4 (&in)[8], uint4 (&out)[8]) {
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
@@ -104,7 +117,8 @@ __device__ __forceinline__ void transpose_block(const uint4 (&in)[8], uint4 (&ou
       const uint4& b = in[2 * p + 1];
       uint32_t wa = (t >> 1) == 0 ? a.x : (t >> 1) == 1 ? a.y : (t >> 1) == 2 ? a.z : a.w;
       uint32_t wb = (t >> 1) == 0 ? b.x : (t >> 1) == 1 ? b.y : (t >> 1) == 2 ? b.z : b.w;
-      w[p] = (t & 1) ? ((wa >> 16) | (wb & 0xFFFF0000u)) : ((wa & 0xFFFFu) | (wb << 16));
+      // even t: low halves (wa.lo, wb.lo); odd t: high halves (wa.hi, wb.hi)
+      w[p] = __builtin_amdgcn_perm(wb, wa, (t & 1) ? 0x07060302u : 0x05040100u);
     }
     out[t] = make_uint4(w[0], w[1], w[2], w[3]);
   }

@@ -108,12 +108,14 @@ __global__ __launch_bounds__(NW * 64) void embed_kernel(EmbedArgs g) {
   };
   auto compute = [&](const VT (&in)[VE], const VT (&a)[MT], int v0) {
     const bool ok = v0 + grp * VE < v_end;
-    VT bt[VE];
+    VT bt[VE], am[MT];
     transpose_block(in, bt);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) am[mt] = vkeep(a[mt], ok && xok[mt]);
 #pragma unroll
     for (int t = 0; t < VE; ++t)
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) mma(acc[mt][t], (ok && xok[mt]) ? a[mt] : vzero<VT>(), bt[t]);
+      for (int mt = 0; mt < MT; ++mt) mma(acc[mt][t], am[mt], bt[t]);
   };
 
   VT in0[VE], in1[VE], a0[MT], a1[MT];

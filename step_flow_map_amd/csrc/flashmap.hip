@@ -64,7 +64,6 @@ constexpr int GEMM_MAX_SPLIT = GEMM_SPLIT_MAX;
 constexpr int LM_WAVES = 8;
 constexpr int LM_GRID = 256;
 constexpr int EMB_WAVES = 8;
-constexpr int EMB_S1 = EMB_LEVEL_MAX, EMB_S2 = EMB_LEVEL_MAX;  // 16 splits of V, two levels of 4
 constexpr int MAX_PREFILL_ROWS = 16;
 constexpr int N_COUNTER_SLOTS = 1024;  // counters, COUNTER_STRIDE words apart
 constexpr int SOFTMAX_CHUNK = 4096;
@@ -119,15 +118,18 @@ GemmPlan plan_gemm(int N, int K, fm_dtype t) {
 }
 
 struct EmbedPlan {
-  int S, rows_split, n_cb, grid;
+  int MT, n_cb, S, S1, S2, grid;
 };
 
-EmbedPlan plan_embed(int V, int d, fm_dtype t) {
-  const int ve = vec_elems(t), rch = 4 * ve;
+// Column blocks of 16*VE columns and S = S1*S2 = 16 splits of V (a multiple of
+// 8 for the XCD placement); splits without rows still arrive.
+EmbedPlan plan_embed(int d, fm_dtype t, int M) {
   EmbedPlan p;
-  p.n_cb = d / (16 * ve);
-  p.S = EMB_S1 * EMB_S2;  // a multiple of 8 (XCD placement); empty splits still arrive
-  p.rows_split = cdiv(cdiv(V, p.S), rch) * rch;
+  p.MT = cdiv(M, 16);
+  p.n_cb = d / (16 * vec_elems(t));
+  p.S1 = EMB_LEVEL_MAX;
+  p.S2 = EMB_LEVEL_MAX;
+  p.S = p.S1 * p.S2;
   p.grid = p.n_cb * p.S;
   return p;
 }
@@ -168,8 +170,10 @@ size_t partial_bytes(const fm_config& c) {
     GemmPlan p = plan_gemm(s.N, s.K, c.dtype);
     if (p.S > 1) mx = std::max(mx, (size_t)p.S * s.M * s.N * 4);
   }
-  EmbedPlan e = plan_embed(c.V, c.d, c.dtype);
-  mx = std::max(mx, (size_t)(e.S + EMB_S2) * Mb * d * 4);
+  for (int M = 16; M <= Mb; M += 16) {
+    EmbedPlan e = plan_embed(c.d, c.dtype, M);
+    mx = std::max(mx, (size_t)(e.S + e.S2) * M * d * 4);
+  }
   return mx;
 }
 
@@ -374,7 +378,8 @@ fm_status ln_mod(fm_handle* h, const float* x, int rows, const float* shift, con
 template <typename T>
 fm_status embed(fm_handle* h, const void* x, int ldx, int M, float alpha, float beta, hipStream_t st) {
   const fm_config& c = h->cfg;
-  EmbedPlan p = plan_embed(c.V, c.d, c.dtype);
+  if (M > 64) return fail(FM_EINVAL, "embedding contraction with %d rows exceeds 64", M);
+  EmbedPlan p = plan_embed(c.d, c.dtype, M);
   EmbedArgs a;
   a.x = x;
   a.ldx = ldx;
@@ -382,9 +387,9 @@ fm_status embed(fm_handle* h, const void* x, int ldx, int M, float alpha, float 
   a.V = c.V;
   a.E = h->w.E;
   a.d = c.d;
-  a.S1 = EMB_S1;
-  a.S2 = EMB_S2;
-  a.rows_split = p.rows_split;
+  a.S1 = p.S1;
+  a.S2 = p.S2;
+  a.rows_split = cdiv(cdiv(c.V, p.S), 4 * vec_elems(c.dtype)) * 4 * vec_elems(c.dtype);
   a.partial = h->at<float>(h->lay.partial);
   a.gpartial = a.partial + (size_t)p.S * M * c.d;
   a.counters = h->at<uint32_t>(h->lay.counters);
@@ -395,12 +400,11 @@ fm_status embed(fm_handle* h, const void* x, int ldx, int M, float alpha, float 
   a.K = KB;
   a.use_pos = 1;
   const dim3 grid(p.grid), block(EMB_WAVES * 64);
-  switch (cdiv(M, 16)) {
+  switch (p.MT) {
     case 1: hipLaunchKernelGGL((embed_kernel<T, 1, EMB_WAVES>), grid, block, 0, st, a); break;
     case 2: hipLaunchKernelGGL((embed_kernel<T, 2, EMB_WAVES>), grid, block, 0, st, a); break;
     case 3: hipLaunchKernelGGL((embed_kernel<T, 3, EMB_WAVES>), grid, block, 0, st, a); break;
-    case 4: hipLaunchKernelGGL((embed_kernel<T, 4, EMB_WAVES>), grid, block, 0, st, a); break;
-    default: return fail(FM_EINVAL, "embedding contraction with %d rows exceeds 64", M);
+    default: hipLaunchKernelGGL((embed_kernel<T, 4, EMB_WAVES>), grid, block, 0, st, a); break;
   }
   FM_LAUNCHED("embed_kernel");
   return FM_OK;
