@@ -138,12 +138,13 @@ struct AttnPlan {
   int n_ranges, blocks_per_range;
 };
 
-// n_blocks 32-key blocks of one (branch, head) over at most 8 ranges of a
-// workgroup of ATT_WAVES waves: one range while no wave takes more than three
-// blocks (no merge across workgroups), else ranges of about two blocks a wave
+// n_blocks 32-key blocks of one (branch, head) over ranges of a workgroup of
+// ATT_WAVES waves: about one block a wave (all of a wave's loads in flight at
+// once), but at most 6 ranges, since every further arrival at the merge costs
+// more than a second block per wave (measured at 18 and 66 blocks)
 AttnPlan plan_attention(int n_blocks) {
   AttnPlan p;
-  const int r = n_blocks <= 3 * ATT_WAVES ? 1 : std::min(ATT_MAX_RANGES, cdiv(n_blocks, 2 * ATT_WAVES));
+  const int r = std::min(std::min(6, ATT_MAX_RANGES), cdiv(n_blocks, ATT_WAVES));
   p.blocks_per_range = cdiv(n_blocks, r);
   p.n_ranges = cdiv(n_blocks, p.blocks_per_range);
   return p;
