@@ -123,6 +123,9 @@ def main():
     ap.add_argument("--config", default="qwen3_8b", choices=sorted(synth.CONFIGS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="time eager calls instead of graph replays")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="only copy this many bytes device to device five times and exit (the plain copy "
+                         "kernel that calibrates the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the drafting step runs on the GPU that holds the "
@@ -130,6 +133,15 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_bytes:
+        src = torch.full((args.copy_bytes,), 1, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": args.copy_bytes, "launches": 5}))
+        return
     import step_flow_map_amd as fm
 
     def to_dev(a):
