@@ -62,7 +62,7 @@ constexpr int ATT_MAX_RANGES = ATT_RANGES_MAX;
 constexpr int ATT_WAVES = 8;  // waves per attention workgroup
 constexpr int GEMM_MAX_SPLIT = GEMM_SPLIT_MAX;
 constexpr int LM_WAVES = 8;
-constexpr int LM_GRID = 256;
+constexpr int LM_GRID = 512;  // most LM head workgroups (keys per row)
 constexpr int EMB_WAVES = 8;
 constexpr int MAX_PREFILL_ROWS = 16;
 constexpr int N_COUNTER_SLOTS = 1024;  // counters, COUNTER_STRIDE words apart
@@ -456,23 +456,39 @@ fm_status lm_head(fm_handle* h, const void* z, int M, float* logits, int32_t* to
   a.V = c.V;
   a.logits = logits;
   a.partial = h->at<uint64_t>(h->lay.lm_part);
-  const int grid = std::min(LM_GRID, cdiv(cdiv(c.V, 16), LM_WAVES));
+  // k split over the waves with z held in registers (at most four 16-row x
+  // 512-byte fragment sets per lane); with 16 rows, 512 workgroups (a second
+  // dispatch round fills the CUs that finish first) even out the finish times
+  const int mt = cdiv(M, 16), cpw = cdiv(cdiv(c.d, 32 * vec_elems(c.dtype)), LM_WAVES);
+  if (mt < 1 || mt > 4) return fail(FM_EINVAL, "LM head with %d rows (1..64)", M);
+  const bool ks = mt * cpw <= 4;
+  const int grid = ks ? std::min(mt == 1 ? LM_GRID : LM_GRID / 2, cdiv(c.V, 16))
+                      : std::min(LM_GRID / 2, cdiv(cdiv(c.V, 16), LM_WAVES));
   const dim3 block(LM_WAVES * 64);
-  const bool zlds = M <= 16 && 16 * (c.d / vec_elems(c.dtype)) <= LM_ZLDS_U4;
-  if (zlds) {
-    hipLaunchKernelGGL((lmhead_kernel<T, 1, LM_WAVES, true>), dim3(grid), block, 0, st, a);
-  } else {
-    switch (cdiv(M, 16)) {
-      case 1: hipLaunchKernelGGL((lmhead_kernel<T, 1, LM_WAVES, false>), dim3(grid), block, 0, st, a); break;
-      case 2: hipLaunchKernelGGL((lmhead_kernel<T, 2, LM_WAVES, false>), dim3(grid), block, 0, st, a); break;
-      case 3: hipLaunchKernelGGL((lmhead_kernel<T, 3, LM_WAVES, false>), dim3(grid), block, 0, st, a); break;
-      case 4: hipLaunchKernelGGL((lmhead_kernel<T, 4, LM_WAVES, false>), dim3(grid), block, 0, st, a); break;
-      default: return fail(FM_EINVAL, "LM head with %d rows exceeds 64", M);
+  if (ks) {
+    switch (mt * 8 + cpw) {
+      case 9: hipLaunchKernelGGL((lmhead_ks_kernel<T, 1, LM_WAVES, 1>), dim3(grid), block, 0, st, a); break;
+      case 10: hipLaunchKernelGGL((lmhead_ks_kernel<T, 1, LM_WAVES, 2>), dim3(grid), block, 0, st, a); break;
+      case 11: hipLaunchKernelGGL((lmhead_ks_kernel<T, 1, LM_WAVES, 3>), dim3(grid), block, 0, st, a); break;
+      case 12: hipLaunchKernelGGL((lmhead_ks_kernel<T, 1, LM_WAVES, 4>), dim3(grid), block, 0, st, a); break;
+      case 17: hipLaunchKernelGGL((lmhead_ks_kernel<T, 2, LM_WAVES, 1>), dim3(grid), block, 0, st, a); break;
+      case 18: hipLaunchKernelGGL((lmhead_ks_kernel<T, 2, LM_WAVES, 2>), dim3(grid), block, 0, st, a); break;
+      case 25: hipLaunchKernelGGL((lmhead_ks_kernel<T, 3, LM_WAVES, 1>), dim3(grid), block, 0, st, a); break;
+      case 33: hipLaunchKernelGGL((lmhead_ks_kernel<T, 4, LM_WAVES, 1>), dim3(grid), block, 0, st, a); break;
+      default: return fail(FM_EINVAL, "LM head plan: %d row tiles x %d chunks per wave", mt, cpw);
     }
+    FM_LAUNCHED("lmhead_ks_kernel");
+  } else {
+    switch (mt) {
+      case 1: hipLaunchKernelGGL((lmhead_kernel<T, 1, LM_WAVES>), dim3(grid), block, 0, st, a); break;
+      case 2: hipLaunchKernelGGL((lmhead_kernel<T, 2, LM_WAVES>), dim3(grid), block, 0, st, a); break;
+      case 3: hipLaunchKernelGGL((lmhead_kernel<T, 3, LM_WAVES>), dim3(grid), block, 0, st, a); break;
+      default: hipLaunchKernelGGL((lmhead_kernel<T, 4, LM_WAVES>), dim3(grid), block, 0, st, a); break;
+    }
+    FM_LAUNCHED("lmhead_kernel");
   }
-  FM_LAUNCHED("lmhead_kernel");
   if (tokens) {
-    hipLaunchKernelGGL(argmax_finalize_kernel, dim3(1), dim3(256), 0, st, a.partial, grid, M, tokens);
+    hipLaunchKernelGGL(argmax_finalize_kernel, dim3(1), dim3(FIN_THREADS), 0, st, a.partial, grid, M, tokens);
     FM_LAUNCHED("argmax_finalize_kernel");
   }
   return FM_OK;

@@ -21,6 +21,10 @@ SMALL_BF16 = TINY.with_(name="small_bf16", dtype="bf16", V=1000, H=520)
 # contraction and in the fused LayerNorm), head width 128, and a context of 308
 # rows = 10 key blocks (the last one partial) spread over several ranges
 MID_BF16 = TINY.with_(name="mid_bf16", dtype="bf16", V=2000, d=384, nh=3, H=520, c_prefill=300)
+# float32 width 1152 = nine 128-column chunks: two chunks for the first wave of
+# the k-split LM head and one for the rest, the LayerNorm left unfused, and a
+# four-branch tree whose z no longer fits in registers (whole-tile LM head)
+WIDE_F32 = TINY.with_(name="wide_f32", V=1000, d=1152, nh=9)
 
 
 def _case(cfg, variant="random", B=1, seed_noise=None):
@@ -30,7 +34,8 @@ def _case(cfg, variant="random", B=1, seed_noise=None):
     return w, feats, noise
 
 
-@pytest.mark.parametrize("cfg", [TINY, SMALL_BF16, MID_BF16], ids=["tiny_f32", "small_bf16", "mid_bf16"])
+@pytest.mark.parametrize("cfg", [TINY, SMALL_BF16, MID_BF16, WIDE_F32],
+                         ids=["tiny_f32", "small_bf16", "mid_bf16", "wide_f32"])
 @pytest.mark.parametrize("variant", ["random", "unit_gate", "gate_zero"])
 def test_draft_matches_oracle(cfg, variant):
     print(f"[draft parity] {cfg.name} {variant}", flush=True)
@@ -125,7 +130,8 @@ def test_two_step_schedule(cfg):
     print(f"  2-step {cfg.name}: logit error {rel:.2e}, near-ties {ties}")
 
 
-@pytest.mark.parametrize("cfg", [TINY, SMALL_BF16, MID_BF16], ids=["tiny_f32", "small_bf16", "mid_bf16"])
+@pytest.mark.parametrize("cfg", [TINY, SMALL_BF16, MID_BF16, WIDE_F32],
+                         ids=["tiny_f32", "small_bf16", "mid_bf16", "wide_f32"])
 def test_draft_tree_of_four(cfg):
     cfg = cfg.with_(B=4)
     w, feats, noise = _case(cfg, B=4)
