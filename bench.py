@@ -65,6 +65,9 @@ def alg_bytes(cfg) -> dict:
         "mod_vectors": n * (6 * L + 2) * d * 4,
         "softmax_round_trip": (n - 1) * Mb * V * (4 + 4 + es + es),
     }
+    if cfg.temperature > 0:   # sampled: the draft's float32 logits out, read back by verify
+        parts["draft_logits_write"] = Mb * V * 4
+        parts["draft_logits_read"] = Mb * V * 4
     parts["total"] = sum(parts.values())
     return parts
 
@@ -72,8 +75,8 @@ def alg_bytes(cfg) -> dict:
 def kernel_alg_bytes(cfg, kernel: str) -> int:
     es = 2 if cfg.dtype == "bf16" else 4
     Mb = cfg.B * cfg.K
-    if kernel.startswith("lmhead"):    # W_lm, z in, tokens out
-        return cfg.V * cfg.d * es + Mb * cfg.d * es + Mb * 4
+    if kernel.startswith("lmhead"):    # W_lm, z in, tokens out (sampled: float32 logits out)
+        return cfg.V * cfg.d * es + Mb * cfg.d * es + Mb * 4 + (Mb * cfg.V * 4 if cfg.temperature > 0 else 0)
     if kernel == "embed_kernel":       # E, x in, e and h out (float32)
         return cfg.V * cfg.d * es + Mb * cfg.V * es + 2 * Mb * cfg.d * 4
     raise KeyError(kernel)
@@ -112,7 +115,12 @@ def cpu_baseline(cfg, w, noise, feats, T):
     t0 = time.perf_counter()
     while True:   # whole steps until about 10 s of CPU work
         ref = oracle.draft(W, cfg, noise[0], feats)
-        oracle.verify(T[0], ref["tokens"])
+        if cfg.temperature > 0:
+            d = oracle.sampling.sample_draft(ref["logits"], cfg.temperature, synth.SAMPLE_SEEDS[0])
+            oracle.sampling.verify_sample(synth.values(T[0]), ref["logits"], d, cfg.temperature,
+                                          synth.SAMPLE_SEEDS[0])
+        else:
+            oracle.verify(T[0], ref["tokens"])
         steps += 1
         dt = time.perf_counter() - t0
         if dt >= 10.0 or steps >= 1000:
@@ -192,36 +200,53 @@ def main():
     best = torch.empty(1, dtype=torch.int32, device=dev)
     torch.cuda.synchronize()
 
-    # draft once to learn the tokens when the oracle did not run
-    dr.truncate(cfg.c_prefill)
-    dr.draft(x, new_feats=new, tokens=tokens)
-    gpu_tokens = tokens.cpu().numpy()
-    plant_from = ref_tokens[None] if ref_tokens is not None else gpu_tokens
-    planted = synth.PLANTED_ACCEPT_TREE if cfg.B > 1 else synth.PLANTED_ACCEPT
-    sets = []
-    if cfg.B > 1:
-        src = np.stack([synth.plant(T_raw[b], gpu_tokens[b], planted[b]) for b in range(cfg.B)])
-        sets.append((to_dev(src), list(planted)))
-    else:
-        for n in planted:
-            sets.append((to_dev(synth.plant(T_raw[0], plant_from[0], n)[None]), [n]))
+    temp = cfg.temperature
+    logits_q = lse_q = None
+    if temp > 0:
+        logits_q = torch.empty(cfg.B, cfg.K, cfg.V, dtype=torch.float32, device=dev)
+        lse_q = torch.empty(cfg.B, cfg.K, dtype=torch.float32, device=dev)
 
-    def step(T):
+    def draft_and_verify(T, seed):
+        if temp > 0:
+            fm.fm_draft_sample(dr.handle, x, temp, seed, tokens, logits_q, lse_q, new_feats=new)
+            fm.fm_verify_sample(dr.handle, T, logits_q, lse_q, tokens, temp, seed, emitted, accept)
+        else:
+            dr.draft(x, new_feats=new, tokens=tokens)
+            fm.fm_verify(T, tokens, emitted, accept, best)
+
+    sets = []   # (target logits, seed, planted accept lengths or None)
+    if temp > 0:
+        # sampled steps: the unplanted target logits, one seed per replayed step
+        T_dev = to_dev(T_raw)
+        sets = [(T_dev, s, None) for s in synth.SAMPLE_SEEDS]
+    else:
+        # draft once to learn the tokens when the oracle did not run
         dr.truncate(cfg.c_prefill)
         dr.draft(x, new_feats=new, tokens=tokens)
-        fm.fm_verify(T, tokens, emitted, accept, best)
+        gpu_tokens = tokens.cpu().numpy()
+        plant_from = ref_tokens[None] if ref_tokens is not None else gpu_tokens
+        planted = synth.PLANTED_ACCEPT_TREE if cfg.B > 1 else synth.PLANTED_ACCEPT
+        if cfg.B > 1:
+            src = np.stack([synth.plant(T_raw[b], gpu_tokens[b], planted[b]) for b in range(cfg.B)])
+            sets.append((to_dev(src), 0, list(planted)))
+        else:
+            for n in planted:
+                sets.append((to_dev(synth.plant(T_raw[0], plant_from[0], n)[None]), 0, [n]))
+
+    def step(T, seed):
+        dr.truncate(cfg.c_prefill)
+        draft_and_verify(T, seed)
 
     stream = torch.cuda.current_stream()
     graphs = []
     if not args.eager:
-        for T, _ in sets:
-            step(T)   # warm the path outside capture
+        for T, seed, _ in sets:
+            step(T, seed)   # warm the path outside capture
             torch.cuda.synchronize()
             g = torch.cuda.CUDAGraph()
             dr.truncate(cfg.c_prefill)
             with torch.cuda.graph(g):
-                dr.draft(x, new_feats=new, tokens=tokens)
-                fm.fm_verify(T, tokens, emitted, accept, best)
+                draft_and_verify(T, seed)
             graphs.append(g)
         torch.cuda.synchronize()
 
@@ -229,7 +254,7 @@ def main():
         if graphs:
             graphs[i % len(graphs)].replay()
         else:
-            step(sets[i % len(sets)][0])
+            step(*sets[i % len(sets)][:2])
 
     # accept lengths of every planted set (checks the planted workload)
     accepts = []
@@ -261,7 +286,7 @@ def main():
         fm.fm_set_probe(dr.handle, probe, a, b)
         durs = []
         for i in range(20):
-            step(sets[i % len(sets)][0])
+            step(*sets[i % len(sets)][:2])
             torch.cuda.synchronize()
             durs.append(a.elapsed_time(b))
         fm.fm_set_probe(dr.handle, fm.FM_PROBE_NONE)
@@ -284,11 +309,14 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": cfg.dtype,
-        "data": "synthetic (seeded random weights ~N(0,0.02), features/noise/target logits ~N(0,1); "
-                "target logits planted for accept lengths 7,7,7,7,7,7,7,6,6,6)",
+        "data": "synthetic (seeded random weights ~N(0,0.02), features/noise/target logits ~N(0,1); " + (
+                f"sampled at temperature {cfg.temperature} with seeds {list(synth.SAMPLE_SEEDS)}, target "
+                "logits not planted)" if cfg.temperature > 0 else
+                "target logits planted for accept lengths 7,7,7,7,7,7,7,6,6,6)"),
         "config": {"workload": cfg.name, "K": cfg.K, "V": cfg.V, "d": cfg.d, "L": cfg.L,
                    "heads": cfg.nh, "H": cfg.H, "context": cfg.C, "new_rows_per_step": cfg.n_new,
-                   "branches": cfg.B, "schedule": list(cfg.times), "replay": "eager" if args.eager else "hipgraph"},
+                   "branches": cfg.B, "schedule": list(cfg.times), "temperature": cfg.temperature,
+                   "replay": "eager" if args.eager else "hipgraph"},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": kd["gbs"], "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": kd["gbs"] / HBM_PEAK_GBS, "traffic": traffic,
                      "alg_bytes_per_launch": kd["alg_bytes"], "us_per_launch": kd["us"]},

@@ -176,6 +176,24 @@ int fm_context_length(const fm_handle *h);
 fm_status fm_draft(fm_handle *h, const void *noise, int B, const void *new_feats, int n_new,
                    int32_t *tokens, float *logits, float *hidden, void *stream);
 
+/* Drafting at temperature > 0 (feinterview.poetries.top, deployment list of
+ * the last section, and wire.sakhanda.co, "Как развернуть FlashMap?": a
+ * separate probabilistic draft-sampling mode for requests sampled at
+ * temperature above 0).  The same step as fm_draft, except that row i of
+ * branch b is SAMPLED from q = softmax(logits_i / temperature) instead of
+ * taking the argmax: token = argmax_v (logits_iv / temperature + G), G the
+ * Gumbel noise -log(-log U) of the Philox4x32-10 counter (v, i, b, 0) under
+ * the key `seed` (low word, high word), U = (x + 0.5) / 2^32 for the draw x,
+ * lowest index on ties.
+ *   temperature  > 0 and finite (host value)
+ *   seed         64-bit key (host value); the same seed gives the same draft
+ *   logits       [B][K][V] float32 output, required (fm_verify_sample reads it)
+ *   lse          [B][K] float32 output: log sum_v exp(logits_iv / temperature)
+ * Other arguments and errors as fm_draft (hidden is not offered here). */
+fm_status fm_draft_sample(fm_handle *h, const void *noise, int B, const void *new_feats, int n_new,
+                          float temperature, uint64_t seed, int32_t *tokens, float *logits, float *lse,
+                          void *stream);
+
 /* Greedy verification (feinterview.poetries.top, first section;
  * wire.sakhanda.co, "Что такое FlashMap?"; alphasignal.ai, "Why drafting
  * still costs time").  Stateless; needs no handle.
@@ -190,6 +208,31 @@ fm_status fm_draft(fm_handle *h, const void *noise, int B, const void *new_feats
 fm_status fm_verify(const void *target_logits, fm_dtype dtype, int B, int K, int V,
                     const int32_t *draft, int32_t *emitted, int32_t *accept, int32_t *best,
                     void *stream);
+
+/* Probabilistic verification at temperature > 0 (alphasignal.ai, "Why
+ * drafting still costs time": lossless = the target's output distribution is
+ * kept under the same sampling settings).  The speculative-sampling rule, with
+ * p_j = softmax(target_logits_j / temperature) and q_i the drafter's
+ * distribution (draft_logits_i / temperature normalised by draft_lse_i):
+ *   draft i is accepted while u_i * q_i(d_i) < p_i(d_i), u_i the uniform of
+ *   Philox counter (0, i, b, 2); n = accepted prefix; row n emits a sample of
+ *   max(0, p_n - q_n) (renormalised) if n < K, of p_K if n = K, drawn by
+ *   Gumbel-max with counters (v, n, b, 1) (lowest index on ties; a residual
+ *   that is zero on every token in float32 falls back to p_n).
+ *   target_logits [B][K+1][V] (dtype), draft_logits [B][K][V] and draft_lse
+ *             [B][K] as written by fm_draft_sample, draft [B][K] int32 tokens
+ *             in [0, V) (others give unspecified results)
+ *   emitted   [B][K+1] int32 output: draft[0..n-1], the sample, then -1
+ *   accept    [B] int32 output: n
+ * Branches are verified independently (no branch selection: choosing among
+ * sampled branches would change the output distribution).  K and V are the
+ * handle's; scratch lives in the handle's workspace, so calls on one handle
+ * must not overlap.  Errors: FM_EINVAL, FM_ECAPACITY (B > max_branches),
+ * FM_EHIP. */
+fm_status fm_verify_sample(fm_handle *h, const void *target_logits, fm_dtype dtype, int B,
+                           const float *draft_logits, const float *draft_lse, const int32_t *draft,
+                           float temperature, uint64_t seed, int32_t *emitted, int32_t *accept,
+                           void *stream);
 
 /* Kernels a probe can bracket. */
 typedef enum fm_probe_kernel {

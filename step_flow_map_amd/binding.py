@@ -78,6 +78,11 @@ def lib() -> ctypes.CDLL:
     L.fm_draft.restype = st
     L.fm_verify.argtypes = [vp, i, i, i, i, vp, vp, vp, vp, vp]
     L.fm_verify.restype = st
+    f32, u64 = ctypes.c_float, ctypes.c_uint64
+    L.fm_draft_sample.argtypes = [vp, vp, i, vp, i, f32, u64, vp, vp, vp, vp]
+    L.fm_draft_sample.restype = st
+    L.fm_verify_sample.argtypes = [vp, vp, i, i, vp, vp, vp, f32, u64, vp, vp, vp]
+    L.fm_verify_sample.restype = st
     L.fm_set_probe.argtypes = [vp, i, vp, vp]
     L.fm_set_probe.restype = st
     L.fm_last_error.argtypes = []
@@ -182,6 +187,27 @@ def fm_draft(h, noise, tokens, new_feats=None, logits=None, hidden=None, stream=
                           _ptr(tokens), _ptr(logits), _ptr(hidden), _stream(stream)))
 
 
+def fm_draft_sample(h, noise, temperature, seed, tokens, logits, lse, new_feats=None, stream=None):
+    """Temperature > 0 draft: tokens [B][K] int32, logits [B][K][V] float32
+    and lse [B][K] float32 outputs."""
+    n_new = 0 if new_feats is None else int(new_feats.shape[0])
+    _check(lib().fm_draft_sample(h, _ptr(noise), int(noise.shape[0]), _ptr(new_feats), n_new,
+                                 float(temperature), int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(tokens),
+                                 _ptr(logits), _ptr(lse), _stream(stream)))
+
+
+def fm_verify_sample(h, target_logits, draft_logits, draft_lse, draft, temperature, seed, emitted, accept,
+                     stream=None):
+    """Probabilistic verify: target_logits [B][K+1][V] (bf16 or float32),
+    draft_logits [B][K][V] and draft_lse [B][K] float32, draft [B][K] int32;
+    outputs emitted [B][K+1] and accept [B] int32."""
+    B = int(target_logits.shape[0])
+    _check(lib().fm_verify_sample(h, _ptr(target_logits), dtype_code(target_logits.dtype), B,
+                                  _ptr(draft_logits), _ptr(draft_lse), _ptr(draft), float(temperature),
+                                  int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(emitted), _ptr(accept),
+                                  _stream(stream)))
+
+
 def fm_verify(target_logits, draft, emitted, accept, best, stream=None):
     """target_logits [B][K+1][V] (bf16 or float32); draft [B][K] int32; outputs
     emitted [B][K+1], accept [B], best [1] int32."""
@@ -239,6 +265,24 @@ class Drafter:
             tokens = torch.empty(noise.shape[0], noise.shape[1], dtype=torch.int32, device=self.device)
         fm_draft(self.handle, noise, tokens, new_feats, logits, hidden, stream)
         return tokens
+
+    def draft_sample(self, noise, temperature, seed, new_feats=None, stream=None):
+        """Returns (tokens, logits, lse) of a temperature > 0 draft."""
+        B, K, V = (int(x) for x in noise.shape)
+        tokens = torch.empty(B, K, dtype=torch.int32, device=self.device)
+        logits = torch.empty(B, K, V, dtype=torch.float32, device=self.device)
+        lse = torch.empty(B, K, dtype=torch.float32, device=self.device)
+        fm_draft_sample(self.handle, noise, temperature, seed, tokens, logits, lse, new_feats, stream)
+        return tokens, logits, lse
+
+    def verify_sample(self, target_logits, draft_logits, draft_lse, draft, temperature, seed, stream=None):
+        """Returns (emitted, accept) of probabilistic verification."""
+        B, K1, _ = target_logits.shape
+        emitted = torch.empty(B, K1, dtype=torch.int32, device=self.device)
+        accept = torch.empty(B, dtype=torch.int32, device=self.device)
+        fm_verify_sample(self.handle, target_logits, draft_logits, draft_lse, draft, temperature, seed,
+                         emitted, accept, stream)
+        return emitted, accept
 
     def close(self):
         if self.handle is not None:

@@ -63,6 +63,7 @@ constexpr int ATT_WAVES = 8;  // waves per attention workgroup
 constexpr int GEMM_MAX_SPLIT = GEMM_SPLIT_MAX;
 constexpr int LM_WAVES = 8;
 constexpr int LM_GRID = 512;  // most LM head workgroups (keys per row)
+constexpr int VS_MAX_SLICES = 64;  // vocabulary slices of the probabilistic verifier
 constexpr int EMB_WAVES = 8;
 constexpr int MAX_PREFILL_ROWS = 16;
 constexpr int N_COUNTER_SLOTS = 1024;  // counters, COUNTER_STRIDE words apart
@@ -156,7 +157,7 @@ int cache_positions(const fm_config& c) { return cdiv(c.C_max, ATT_BLK) * ATT_BL
 
 struct Layout {
   size_t cache, mods, sched, h, e_state, u_pre, act_qkv, act_d, attn_o, act_f, qkv;
-  size_t att_po, att_ml, partial, lm_part, counters, dsoft, logits_tmp, sm_part, total;
+  size_t att_po, att_ml, partial, lm_part, lm_lse, counters, dsoft, logits_tmp, sm_part, vs_stats, vs_keys, total;
 };
 
 int max_rows(const fm_config& c) { return c.max_branches * KB; }
@@ -203,6 +204,9 @@ Layout make_layout(const fm_config& c) {
   L.att_ml = take((size_t)c.max_branches * c.n_heads * ATT_MAX_RANGES * KB * 2 * 4);
   L.partial = take(partial_bytes(c));
   L.lm_part = take((size_t)LM_GRID * Mb * 8);
+  L.lm_lse = take((size_t)LM_GRID * Mb * 8);
+  L.vs_stats = take((size_t)c.max_branches * (KB + 1) * VS_MAX_SLICES * 8);
+  L.vs_keys = take((size_t)c.max_branches * (KB + 1) * VS_MAX_SLICES * 16);
   L.counters = take((size_t)N_COUNTER_SLOTS * COUNTER_STRIDE * 4);
   if (c.max_steps > 1) {
     L.dsoft = take(Mb * (size_t)c.V * es);
@@ -445,10 +449,24 @@ fm_status attention(fm_handle* h, int l, int B, int C, hipStream_t st) {
   return FM_OK;
 }
 
+// Temperature > 0 drafting: tokens are sampled from softmax(logits / tau) and
+// the per-row log-normalisers are written to lse.
+struct Sampling {
+  float tau;
+  uint64_t seed;
+  float* lse;  // [M]
+};
+
 template <typename T>
-fm_status lm_head(fm_handle* h, const void* z, int M, float* logits, int32_t* tokens, hipStream_t st) {
+fm_status lm_head(fm_handle* h, const void* z, int M, float* logits, int32_t* tokens, hipStream_t st,
+                  const Sampling* smp = nullptr) {
   const fm_config& c = h->cfg;
-  LmArgs a;
+  LmArgs a{};
+  a.tau = smp ? smp->tau : 0.f;
+  a.seed_lo = smp ? (uint32_t)(smp->seed & 0xFFFFFFFFu) : 0u;
+  a.seed_hi = smp ? (uint32_t)(smp->seed >> 32) : 0u;
+  a.K = KB;
+  a.lse_part = smp ? h->at<float2>(h->lay.lm_lse) : nullptr;
   a.z = z;
   a.M = M;
   a.d = c.d;
@@ -488,7 +506,8 @@ fm_status lm_head(fm_handle* h, const void* z, int M, float* logits, int32_t* to
     FM_LAUNCHED("lmhead_kernel");
   }
   if (tokens) {
-    hipLaunchKernelGGL(argmax_finalize_kernel, dim3(1), dim3(FIN_THREADS), 0, st, a.partial, grid, M, tokens);
+    hipLaunchKernelGGL(argmax_finalize_kernel, dim3(1), dim3(FIN_THREADS), 0, st, a.partial, grid, M, tokens,
+                       a.lse_part, smp ? smp->lse : nullptr);
     FM_LAUNCHED("argmax_finalize_kernel");
   }
   return FM_OK;
@@ -589,7 +608,7 @@ fm_status context_append_impl(fm_handle* h, const void* feats, int n, hipStream_
 
 template <typename T>
 fm_status draft_impl(fm_handle* h, const void* noise, int B, const void* new_feats, int n_new, int32_t* tokens,
-                     float* logits, float* hidden, hipStream_t st) {
+                     float* logits, float* hidden, hipStream_t st, const Sampling* smp = nullptr) {
   const fm_config& c = h->cfg;
   const int d = c.d, F = c.mlp_mult * c.d, Mb = B * KB, L = c.L;
   const int C = h->ctx_len + n_new;
@@ -677,7 +696,7 @@ fm_status draft_impl(fm_handle* h, const void* noise, int B, const void* new_fea
     FM_TRY(ln_mod<T>(h, hres, Mb, fin, fin + d, act_d, d, st));
     if (t == 1.f) {
       FM_TRY(probe_begin(h, FM_PROBE_LM_HEAD, st));
-      FM_TRY(lm_head<T>(h, act_d, Mb, logits, tokens, st));
+      FM_TRY(lm_head<T>(h, act_d, Mb, logits, tokens, st, smp));
       FM_TRY(probe_end(h, FM_PROBE_LM_HEAD, st));
     } else {
       FM_TRY(lm_head<T>(h, act_d, Mb, h->at<float>(h->lay.logits_tmp), nullptr, st));
@@ -729,6 +748,38 @@ fm_status verify_impl(const void* tl, int B, int K, int V, const int32_t* draft,
   FM_LAUNCHED("verify_argmax_kernel");
   hipLaunchKernelGGL(verify_prefix_kernel, dim3(1), dim3(64), 0, st, draft, B, K, emitted, accept, best);
   FM_LAUNCHED("verify_prefix_kernel");
+  return FM_OK;
+}
+
+template <typename T>
+fm_status verify_sample_impl(fm_handle* h, const void* tl, int B, const float* Q, const float* lseQ,
+                             const int32_t* draft, float tau, uint64_t seed, int32_t* emitted, int32_t* accept,
+                             hipStream_t st) {
+  const fm_config& c = h->cfg;
+  VsArgs a{};
+  a.T = tl;
+  a.Q = Q;
+  a.lseQ = lseQ;
+  a.draft = draft;
+  a.B = B;
+  a.K = KB;
+  a.V = c.V;
+  a.S = std::min(VS_MAX_SLICES, cdiv(c.V, 4096));
+  a.slice = cdiv(c.V, a.S);
+  a.tau = tau;
+  a.seed_lo = (uint32_t)(seed & 0xFFFFFFFFu);
+  a.seed_hi = (uint32_t)(seed >> 32);
+  a.stats = h->at<float2>(h->lay.vs_stats);
+  a.keys = h->at<uint64_t>(h->lay.vs_keys);
+  a.emitted = emitted;
+  a.accept = accept;
+  const dim3 grid(a.S, B * (KB + 1));
+  hipLaunchKernelGGL((vs_stats_kernel<T>), grid, dim3(VS_THREADS), 0, st, a);
+  FM_LAUNCHED("vs_stats_kernel");
+  hipLaunchKernelGGL((vs_keys_kernel<T>), grid, dim3(VS_THREADS), 0, st, a);
+  FM_LAUNCHED("vs_keys_kernel");
+  hipLaunchKernelGGL((vs_final_kernel<T>), dim3(B), dim3(64), 0, st, a);
+  FM_LAUNCHED("vs_final_kernel");
   return FM_OK;
 }
 
@@ -852,9 +903,8 @@ fm_status fm_context_truncate(fm_handle* h, int new_len) {
 
 int fm_context_length(const fm_handle* h) { return h ? h->ctx_len : -1; }
 
-fm_status fm_draft(fm_handle* h, const void* noise, int B, const void* new_feats, int n_new, int32_t* tokens,
-                   float* logits, float* hidden, void* stream) {
-  g_err.clear();
+static fm_status draft_checked(fm_handle* h, const void* noise, int B, const void* new_feats, int n_new,
+                               int32_t* tokens, float* logits, float* hidden, void* stream, const Sampling* smp) {
   if (!h) return fail(FM_EINVAL, "handle is NULL");
   const fm_config& c = h->cfg;
   if (!noise || !tokens) return fail(FM_EINVAL, "noise and tokens must not be NULL");
@@ -870,13 +920,30 @@ fm_status fm_draft(fm_handle* h, const void* noise, int B, const void* new_feats
   if (!h->has_weights) return fail(FM_ESTATE, "fm_draft before fm_set_weights");
   if (h->n_steps < 1) return fail(FM_ESTATE, "fm_draft before fm_set_schedule");
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  fm_status s = c.dtype == FM_BF16 ? draft_impl<bf16_t>(h, noise, B, new_feats, n_new, tokens, logits, hidden, st)
-                                   : draft_impl<float>(h, noise, B, new_feats, n_new, tokens, logits, hidden, st);
+  fm_status s = c.dtype == FM_BF16 ? draft_impl<bf16_t>(h, noise, B, new_feats, n_new, tokens, logits, hidden, st, smp)
+                                   : draft_impl<float>(h, noise, B, new_feats, n_new, tokens, logits, hidden, st, smp);
   if (s == FM_OK) {
     h->ctx_len += n_new;
     h->ctx_high = std::max(h->ctx_high, h->ctx_len);
   }
   return s;
+}
+
+fm_status fm_draft(fm_handle* h, const void* noise, int B, const void* new_feats, int n_new, int32_t* tokens,
+                   float* logits, float* hidden, void* stream) {
+  g_err.clear();
+  return draft_checked(h, noise, B, new_feats, n_new, tokens, logits, hidden, stream, nullptr);
+}
+
+fm_status fm_draft_sample(fm_handle* h, const void* noise, int B, const void* new_feats, int n_new,
+                          float temperature, uint64_t seed, int32_t* tokens, float* logits, float* lse,
+                          void* stream) {
+  g_err.clear();
+  if (!(temperature > 0.f) || !std::isfinite(temperature))
+    return fail(FM_EINVAL, "temperature must be finite and > 0");
+  if (!logits || !lse) return fail(FM_EINVAL, "logits and lse must not be NULL when sampling");
+  const Sampling smp{temperature, seed, lse};
+  return draft_checked(h, noise, B, new_feats, n_new, tokens, logits, nullptr, stream, &smp);
 }
 
 fm_status fm_verify(const void* target_logits, fm_dtype dtype, int B, int K, int V, const int32_t* draft,
@@ -893,6 +960,28 @@ fm_status fm_verify(const void* target_logits, fm_dtype dtype, int B, int K, int
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   return dtype == FM_BF16 ? verify_impl<bf16_t>(target_logits, B, K, V, draft, emitted, accept, best, st)
                           : verify_impl<float>(target_logits, B, K, V, draft, emitted, accept, best, st);
+}
+
+fm_status fm_verify_sample(fm_handle* h, const void* target_logits, fm_dtype dtype, int B, const float* draft_logits,
+                           const float* draft_lse, const int32_t* draft, float temperature, uint64_t seed,
+                           int32_t* emitted, int32_t* accept, void* stream) {
+  g_err.clear();
+  if (!h) return fail(FM_EINVAL, "handle is NULL");
+  if (!target_logits || !draft_logits || !draft_lse || !draft || !emitted || !accept)
+    return fail(FM_EINVAL, "a pointer argument is NULL");
+  if (dtype != FM_BF16 && dtype != FM_F32) return fail(FM_EINVAL, "dtype must be FM_BF16 or FM_F32");
+  if (B < 1) return fail(FM_EINVAL, "B must be >= 1");
+  if (B > h->cfg.max_branches) return fail(FM_ECAPACITY, "B %d exceeds max_branches %d", B, h->cfg.max_branches);
+  if (!(temperature > 0.f) || !std::isfinite(temperature))
+    return fail(FM_EINVAL, "temperature must be finite and > 0");
+  if (reinterpret_cast<uintptr_t>(target_logits) % esize(dtype) || reinterpret_cast<uintptr_t>(draft_logits) % 4 ||
+      reinterpret_cast<uintptr_t>(draft_lse) % 4)
+    return fail(FM_EINVAL, "a logits array is not aligned to its element size");
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  return dtype == FM_BF16 ? verify_sample_impl<bf16_t>(h, target_logits, B, draft_logits, draft_lse, draft,
+                                                       temperature, seed, emitted, accept, st)
+                          : verify_sample_impl<float>(h, target_logits, B, draft_logits, draft_lse, draft,
+                                                      temperature, seed, emitted, accept, st);
 }
 
 fm_status fm_set_probe(fm_handle* h, fm_probe_kernel kernel, void* ev_start, void* ev_stop) {

@@ -12,8 +12,15 @@
 // key (value, then lower index), so lanes, waves and workgroups combine with a
 // plain max in any order; each workgroup writes its keys and
 // argmax_finalize_kernel reduces them.
+//
+// Temperature tau > 0 (draft sampling): the key of logit l at (row m, token
+// v) is l / tau + G, G the Gumbel noise of Philox counter (v, m % K, m / K,
+// stream 0), so the row's winner is a sample of softmax(l / tau); each
+// workgroup also writes the row's (max, sum of exp(l / tau - max)) and the
+// finalize kernel merges them into log sum_v exp(l_v / tau).
 #pragma once
 #include "common.hpp"
+#include "philox.hpp"
 #include "stream.hpp"
 
 namespace fm {
@@ -25,7 +32,51 @@ struct LmArgs {
   int V;
   float* logits;      // [M][V] or null
   uint64_t* partial;  // [gridDim.x][M]
+  float tau;          // 0: greedy argmax; > 0: sampling at this temperature
+  uint32_t seed_lo, seed_hi;
+  int K;              // rows per branch
+  float2* lse_part;   // [gridDim.x][M] (tau > 0)
 };
+
+// Online log-sum-exp state (m, s): sum of exp(x - m) over the values seen.
+__device__ __forceinline__ void lse_add(float& m, float& s, float x) {
+  if (x > m) {
+    s = s * expf(m - x) + 1.f;  // m = -inf at the start: s = 0 * 0 + 1
+    m = x;
+  } else {
+    s += expf(x - m);
+  }
+}
+__device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
+  if (m2 == -INFINITY) return;
+  if (m == -INFINITY) {
+    m = m2;
+    s = s2;
+    return;
+  }
+  const float mm = fmaxf(m, m2);
+  s = s * expf(m - mm) + s2 * expf(m2 - mm);
+  m = mm;
+}
+__device__ __forceinline__ void lse_shfl_merge(float& m, float& s, int o) {
+  const float m2 = __shfl_xor(m, o, 64), s2 = __shfl_xor(s, o, 64);
+  lse_merge(m, s, m2, s2);
+}
+
+// One finished logit v at (row m, token n): running key, log-sum-exp state,
+// optional dump.
+__device__ __forceinline__ void lm_visit(const LmArgs& g, float v, int m, int n, uint64_t& best, float& lm,
+                                         float& ls) {
+  float key = v;
+  if (g.tau > 0.f) {
+    const float x = v / g.tau;
+    lse_add(lm, ls, x);
+    key = x + gumbel_of(philox_x0((uint32_t)n, (uint32_t)(m % g.K), (uint32_t)(m / g.K), RNG_DRAFT, g.seed_lo,
+                                  g.seed_hi));
+  }
+  best = umax64(best, argmax_key(key, (uint32_t)n));
+  if (g.logits) g.logits[(size_t)m * g.V + n] = v;
+}
 
 template <typename T, int MT, int NW>
 __global__ __launch_bounds__(NW * 64) void lmhead_kernel(LmArgs g) {
@@ -34,6 +85,7 @@ __global__ __launch_bounds__(NW * 64) void lmhead_kernel(LmArgs g) {
   constexpr int KC = ChunkT<T>::KC;
   __shared__ uint4 wtiles[NW * 512];
   __shared__ uint64_t wbest[NW][MT * 16];
+  __shared__ float2 wlse[NW][MT * 16];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int j = lane & 15, grp = lane >> 4;
@@ -49,10 +101,15 @@ __global__ __launch_bounds__(NW * 64) void lmhead_kernel(LmArgs g) {
     zrow[mt] = Z + (size_t)(zok[mt] ? m : 0) * g.d;
   }
   uint64_t best[MT][4];
+  float lm[MT][4], ls[MT][4];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) best[mt][i] = 0ull;
+    for (int i = 0; i < 4; ++i) {
+      best[mt][i] = 0ull;
+      lm[mt][i] = -INFINITY;
+      ls[mt][i] = 0.f;
+    }
 
   const int ntiles = (g.V + 15) / 16, nch = (g.d + KC - 1) / KC;
   const int gw = blockIdx.x * NW + wave, nw = gridDim.x * NW;
@@ -92,11 +149,7 @@ __global__ __launch_bounds__(NW * 64) void lmhead_kernel(LmArgs g) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int m = mt * 16 + 4 * grp + i;
-          if (n < g.V && m < g.M) {
-            const float v = acc[mt][i];
-            best[mt][i] = umax64(best[mt][i], argmax_key(v, (uint32_t)n));
-            if (g.logits) g.logits[(size_t)m * g.V + n] = v;
-          }
+          if (n < g.V && m < g.M) lm_visit(g, acc[mt][i], m, n, best[mt][i], lm[mt][i], ls[mt][i]);
         }
         acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
@@ -120,16 +173,28 @@ __global__ __launch_bounds__(NW * 64) void lmhead_kernel(LmArgs g) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       uint64_t k = best[mt][i];
+      float a = lm[mt][i], b = ls[mt][i];
 #pragma unroll
-      for (int o = 1; o < 16; o <<= 1) k = umax64(k, shfl_xor_u64(k, o));
-      if (j == 0) wbest[wave][mt * 16 + 4 * grp + i] = k;
+      for (int o = 1; o < 16; o <<= 1) {
+        k = umax64(k, shfl_xor_u64(k, o));
+        lse_shfl_merge(a, b, o);
+      }
+      if (j == 0) {
+        wbest[wave][mt * 16 + 4 * grp + i] = k;
+        wlse[wave][mt * 16 + 4 * grp + i] = make_float2(a, b);
+      }
     }
   __syncthreads();
   for (int m = threadIdx.x; m < g.M; m += NW * 64) {
     uint64_t k = 0ull;
+    float a = -INFINITY, b = 0.f;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) k = umax64(k, wbest[w][m]);
+    for (int w = 0; w < NW; ++w) {
+      k = umax64(k, wbest[w][m]);
+      lse_merge(a, b, wlse[w][m].x, wlse[w][m].y);
+    }
     g.partial[(size_t)blockIdx.x * g.M + m] = k;
+    if (g.tau > 0.f) g.lse_part[(size_t)blockIdx.x * g.M + m] = make_float2(a, b);
   }
 }
 
@@ -178,8 +243,13 @@ __global__ __launch_bounds__(NW * 64) void lmhead_ks_kernel(LmArgs g) {
         zf[u][mt][st] = vkeep(vload<T>(Z + (size_t)(ok ? m : 0) * g.d + (ok ? k : 0)), ok);
       }
   uint64_t best[PER];
+  float lm[PER], ls[PER];
 #pragma unroll
-  for (int r = 0; r < PER; ++r) best[r] = 0ull;
+  for (int r = 0; r < PER; ++r) {
+    best[r] = 0ull;
+    lm[r] = -INFINITY;
+    ls[r] = 0.f;
+  }
 
   // chunks of tile it (of this workgroup); tiles past the end read row 0
   auto load = [&](uint4 (&rb)[CPW][8], int it) {
@@ -222,10 +292,7 @@ __global__ __launch_bounds__(NW * 64) void lmhead_ks_kernel(LmArgs g) {
         float v = 0.f;
 #pragma unroll
         for (int w = 0; w < NW; ++w) v += rd[w * ELEMS + el];
-        if (n < g.V && m < g.M) {
-          best[r] = umax64(best[r], argmax_key(v, (uint32_t)n));
-          if (g.logits) g.logits[(size_t)m * g.V + n] = v;
-        }
+        if (n < g.V && m < g.M) lm_visit(g, v, m, n, best[r], lm[r], ls[r]);
       }
     }
   };
@@ -246,38 +313,62 @@ __global__ __launch_bounds__(NW * 64) void lmhead_ks_kernel(LmArgs g) {
   for (int r = 0; r < PER; ++r) {
     const int el = tid + r * NW * 64;
     uint64_t k = best[r];
+    float a = lm[r], b = ls[r];
 #pragma unroll
-    for (int o = 1; o < 16; o <<= 1) k = umax64(k, shfl_xor_u64(k, o));
+    for (int o = 1; o < 16; o <<= 1) {
+      k = umax64(k, shfl_xor_u64(k, o));
+      lse_shfl_merge(a, b, o);
+    }
     const int ln = el & 63, q = el >> 6;
     const int m = (q >> 2) * 16 + 4 * (ln >> 4) + (q & 3);
-    if (el < ELEMS && (ln & 15) == 0 && m < g.M) g.partial[(size_t)blockIdx.x * g.M + m] = k;
+    if (el < ELEMS && (ln & 15) == 0 && m < g.M) {
+      g.partial[(size_t)blockIdx.x * g.M + m] = k;
+      if (g.tau > 0.f) g.lse_part[(size_t)blockIdx.x * g.M + m] = make_float2(a, b);
+    }
   }
 }
 
-// tokens[m] = index of max over G workgroup keys.  1024 threads, tpr threads
-// per row on consecutive lanes of one wave (M <= 64); each thread keeps eight loads in
-// flight at once, so G = 512 costs one memory latency for up to 16 rows.
+// tokens[m] = index of max over G workgroup keys, and with lse_part given
+// lse[m] = log-sum-exp merged from the G workgroup states.  1024 threads, tpr
+// threads per row on consecutive lanes of one wave (M <= 64); each thread
+// keeps eight loads in flight at once, so G = 512 costs one memory latency for
+// up to 16 rows.  The merge order is fixed, so results are reproducible.
 constexpr int FIN_THREADS = 1024;
 __global__ __launch_bounds__(FIN_THREADS) void argmax_finalize_kernel(const uint64_t* partial, int G, int M,
-                                                                     int32_t* tokens) {
+                                                                     int32_t* tokens, const float2* lse_part,
+                                                                     float* lse) {
   int mp = 16;
   while (mp < M) mp <<= 1;
   const int tpr = FIN_THREADS / mp;
   const int m = threadIdx.x / tpr, sub = threadIdx.x % tpr;
   const int mr = m < M ? m : 0;
   uint64_t k = 0ull;
+  float a = -INFINITY, b = 0.f;
   for (int b0 = sub; b0 < G; b0 += 8 * tpr) {
     uint64_t v[8];
+    float2 e[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int b = b0 + u * tpr;
-      v[u] = partial[(size_t)(b < G ? b : 0) * M + mr];
+      const int gi = b0 + u * tpr;
+      const size_t at = (size_t)(gi < G ? gi : 0) * M + mr;
+      v[u] = partial[at];
+      if (lse_part) e[u] = lse_part[at];
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) k = umax64(k, b0 + u * tpr < G ? v[u] : 0ull);
+    for (int u = 0; u < 8; ++u) {
+      const bool in = b0 + u * tpr < G;
+      k = umax64(k, in ? v[u] : 0ull);
+      if (lse_part && in) lse_merge(a, b, e[u].x, e[u].y);
+    }
   }
-  for (int o = 1; o < tpr; o <<= 1) k = umax64(k, shfl_xor_u64(k, o));  // tpr <= 64
-  if (m < M && sub == 0) tokens[m] = (int32_t)argmax_key_index(k);
+  for (int o = 1; o < tpr; o <<= 1) {  // tpr <= 64
+    k = umax64(k, shfl_xor_u64(k, o));
+    if (lse_part) lse_shfl_merge(a, b, o);
+  }
+  if (m < M && sub == 0) {
+    tokens[m] = (int32_t)argmax_key_index(k);
+    if (lse_part) lse[m] = a + logf(b);
+  }
 }
 
 }  // namespace fm

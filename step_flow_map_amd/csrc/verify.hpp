@@ -9,6 +9,8 @@
 // buffer (it has exactly B*(K+1) slots), the second turns it into the result.
 #pragma once
 #include "common.hpp"
+#include "lmhead.hpp"
+#include "philox.hpp"
 
 namespace fm {
 
@@ -94,6 +96,151 @@ __global__ __launch_bounds__(64) void verify_prefix_kernel(const int32_t* draft,
       if (ns[i] > ns[bi]) bi = i;
     best[0] = bi;
   }
+}
+
+
+// ------------------------------------------------------------ temperature > 0
+// Probabilistic verification (speculative sampling) of B branches:
+//   p_j = softmax(T_j / tau) for target rows j = 0..K, q_i = softmax(Q_i / tau)
+//   the drafter's distribution of row i (its log-normaliser lseQ_i comes with
+//   the draft).  Draft i is accepted while u_i * q_i(d_i) < p_i(d_i), u_i the
+//   uniform of Philox counter (0, i, b, stream 2); n = accepted prefix.  Row n
+//   emits the Gumbel-max sample (counters (v, n, b, stream 1)) of the residual
+//   max(0, p_n - q_n) when n < K, of p_K when n = K; a residual that is zero
+//   everywhere (p = q in float32) falls back to p_n.
+// Three launches over a [B*(K+1)] x S grid of vocabulary slices: the target
+// rows' (max, sum of exp) per slice; every row's residual and fallback keys
+// per slice (all rows, so no launch waits on n); then one wave per branch
+// finds n and merges row n's keys.  Merge orders are fixed.
+struct VsArgs {
+  const void* T;          // [B][K+1][V] target logits
+  const float* Q;         // [B][K][V] drafter logits of the last jump
+  const float* lseQ;      // [B][K] log sum_v exp(Q / tau)
+  const int32_t* draft;   // [B][K]
+  int B, K, V, S, slice;  // S vocabulary slices of `slice` tokens
+  float tau;
+  uint32_t seed_lo, seed_hi;
+  float2* stats;          // [B*(K+1)][S]
+  uint64_t* keys;         // [B*(K+1)][S][2]: residual (or bonus) key, fallback key
+  int32_t* emitted;       // [B][K+1]
+  int32_t* accept;        // [B]
+};
+
+constexpr int VS_THREADS = 256;
+
+// Block-wide max of two keys; thread 0 ends with the results.
+__device__ __forceinline__ void block_max2(uint64_t& a, uint64_t& b) {
+  __shared__ uint64_t sk[2][VS_THREADS / 64];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    a = umax64(a, shfl_xor_u64(a, o));
+    b = umax64(b, shfl_xor_u64(b, o));
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) {
+    sk[0][wave] = a;
+    sk[1][wave] = b;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0)
+    for (int w = 1; w < VS_THREADS / 64; ++w) {
+      a = umax64(a, sk[0][w]);
+      b = umax64(b, sk[1][w]);
+    }
+}
+
+template <typename T>
+__global__ __launch_bounds__(VS_THREADS) void vs_stats_kernel(VsArgs g) {
+  __shared__ float2 sw[VS_THREADS / 64];
+  const int s = blockIdx.x, r = blockIdx.y;
+  const T* row = reinterpret_cast<const T*>(g.T) + (size_t)r * g.V;
+  const int v0 = s * g.slice, v1 = min(g.V, v0 + g.slice);
+  float m = -INFINITY, sum = 0.f;
+  for (int v = v0 + (int)threadIdx.x; v < v1; v += VS_THREADS) lse_add(m, sum, to_f32<T>(row[v]) / g.tau);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) lse_shfl_merge(m, sum, o);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) sw[wave] = make_float2(m, sum);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < VS_THREADS / 64; ++w) lse_merge(m, sum, sw[w].x, sw[w].y);
+    g.stats[(size_t)r * g.S + s] = make_float2(m, sum);
+  }
+}
+
+// log-normaliser of target row r from its S slice states (fixed order)
+__device__ __forceinline__ float vs_row_lse(const VsArgs& g, int r) {
+  float m = -INFINITY, sum = 0.f;
+  for (int s = 0; s < g.S; ++s) {
+    const float2 e = g.stats[(size_t)r * g.S + s];
+    lse_merge(m, sum, e.x, e.y);
+  }
+  return m + logf(sum);
+}
+
+template <typename T>
+__global__ __launch_bounds__(VS_THREADS) void vs_keys_kernel(VsArgs g) {
+  __shared__ float s_lse;
+  const int s = blockIdx.x, r = blockIdx.y;
+  const int b = r / (g.K + 1), j = r % (g.K + 1);
+  if (threadIdx.x == 0) s_lse = vs_row_lse(g, r);
+  __syncthreads();
+  const float lseP = s_lse;
+  const T* row = reinterpret_cast<const T*>(g.T) + (size_t)r * g.V;
+  const bool bonus = j == g.K;
+  const float* qrow = bonus ? nullptr : g.Q + ((size_t)b * g.K + j) * g.V;
+  const float lseQ = bonus ? 0.f : g.lseQ[b * g.K + j];
+  const int v0 = s * g.slice, v1 = min(g.V, v0 + g.slice);
+  uint64_t k1 = 0ull, k2 = 0ull;
+  for (int v = v0 + (int)threadIdx.x; v < v1; v += VS_THREADS) {
+    const float lp = to_f32<T>(row[v]) / g.tau - lseP;
+    const float G = gumbel_of(philox_x0((uint32_t)v, (uint32_t)j, (uint32_t)b, RNG_CORRECT, g.seed_lo, g.seed_hi));
+    k2 = umax64(k2, argmax_key(lp + G, (uint32_t)v));
+    if (bonus) {
+      k1 = umax64(k1, argmax_key(lp + G, (uint32_t)v));
+    } else {
+      const float w = expf(lp) - expf(qrow[v] / g.tau - lseQ);
+      if (w > 0.f) k1 = umax64(k1, argmax_key(logf(w) + G, (uint32_t)v));
+    }
+  }
+  block_max2(k1, k2);
+  if (threadIdx.x == 0) {
+    g.keys[((size_t)r * g.S + s) * 2 + 0] = k1;
+    g.keys[((size_t)r * g.S + s) * 2 + 1] = k2;
+  }
+}
+
+// one wave per branch; lane i tests draft i (K <= 64), lanes merge row n's
+// slice keys (S <= 64)
+template <typename T>
+__global__ __launch_bounds__(64) void vs_final_kernel(VsArgs g) {
+  const int b = blockIdx.x, lane = threadIdx.x;
+  const T* Tb = reinterpret_cast<const T*>(g.T) + (size_t)b * (g.K + 1) * g.V;
+  bool reject = false;
+  if (lane < g.K) {
+    const int d = min(max(g.draft[b * g.K + lane], 0), g.V - 1);  // memory safety only
+    const float lp = to_f32<T>(Tb[(size_t)lane * g.V + d]) / g.tau - vs_row_lse(g, b * (g.K + 1) + lane);
+    const float lq = g.Q[((size_t)b * g.K + lane) * g.V + d] / g.tau - g.lseQ[b * g.K + lane];
+    const float u = uniform_of(philox_x0(0u, (uint32_t)lane, (uint32_t)b, RNG_ACCEPT, g.seed_lo, g.seed_hi));
+    reject = !(u * expf(lq) < expf(lp));
+  }
+  const uint64_t rej = __ballot(reject);
+  const int n = rej ? (int)__builtin_ctzll(rej) : g.K;
+  const int r = b * (g.K + 1) + n;
+  uint64_t k1 = 0ull, k2 = 0ull;
+  if (lane < g.S) {
+    k1 = g.keys[((size_t)r * g.S + lane) * 2 + 0];
+    k2 = g.keys[((size_t)r * g.S + lane) * 2 + 1];
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    k1 = umax64(k1, shfl_xor_u64(k1, o));
+    k2 = umax64(k2, shfl_xor_u64(k2, o));
+  }
+  const int y = (int)argmax_key_index(k1 ? k1 : k2);
+  for (int i = lane; i <= g.K; i += 64)
+    g.emitted[(size_t)b * (g.K + 1) + i] = i < n ? g.draft[b * g.K + i] : (i == n ? y : -1);
+  if (lane == 0) g.accept[b] = n;
 }
 
 }  // namespace fm

@@ -52,6 +52,7 @@ class Config:
     times: tuple = (0.0, 1.0)   # flow-map schedule s_0=0 < ... < s_n=1
     mlp_mult: int = 4
     c_max: int = 0  # context capacity (0: c_prefill + n_new)
+    temperature: float = 0.0    # 0: greedy drafting and verification; > 0: sampled
 
     @property
     def hd(self) -> int:
@@ -97,7 +98,12 @@ CONFIGS = {
                               times=(0.0, 0.5, 1.0)),
     # tree of 4 noise branches sharing one context of 4096
     "qwen3_8b_tree4": _qwen8b(name="qwen3_8b_tree4", c_prefill=4088, B=4),
+    # as qwen3_8b, sampled at temperature 1 (probabilistic drafting + verify)
+    "qwen3_8b_t1": _qwen8b(name="qwen3_8b_t1", temperature=1.0),
 }
+
+# seeds of the random streams of sampled steps (one per replayed step)
+SAMPLE_SEEDS = tuple(range(1, 11))
 
 
 # --------------------------------------------------------------------------

@@ -9,6 +9,8 @@ import oracle
 import step_flow_map_amd as fm
 import synth
 
+S = oracle.sampling
+
 # logits: per row, max |gpu - ref| <= LOGIT_RTOL * max |ref|   (norm-wise relative)
 LOGIT_RTOL = 2e-2
 # residual stream after every block, same norm-wise measure
@@ -101,3 +103,71 @@ def check_draft(cfg, w, noise, feats, prefill, tok, logits, hidden=None, times=N
                 e = rowwise_rel_err(hidden[j, 0, b], jt["h0"])
                 assert e.max() <= HIDDEN_RTOL, f"jump {j} embedding error {e.max():.3e}"
     return rel_max, all_ties
+
+
+# ------------------------------------------------------------ temperature > 0
+
+# float32 evaluation of a key l / tau + G (division, two logarithms): relative
+KEY_EPS = 2e-6
+# acceptance u q < p in float32 with a 24-bit uniform
+ACCEPT_EPS = 2e-6
+
+
+def _sample_keys(logits_row, tau, seed, row, branch):
+    V = logits_row.shape[0]
+    return logits_row.astype(np.float64) / tau + S.gumbel(np.arange(V), row, branch, S.STREAM_DRAFT, seed)
+
+
+def check_sampled_tokens(tok, logits_gpu, ref_logits, tau, seed):
+    """tok [B][K]; logits [B][K][V]; returns the near-ties."""
+    ties = []
+    B, K, _ = logits_gpu.shape
+    for b in range(B):
+        for i in range(K):
+            own = _sample_keys(logits_gpu[b, i], tau, seed, i, b)
+            t = int(tok[b, i])
+            eps = KEY_EPS * (1.0 + np.abs(own).max())
+            assert own[t] >= own.max() - eps, (b, i, t, int(own.argmax()), own.max() - own[t])
+            ref = _sample_keys(ref_logits[b][i], tau, seed, i, b)
+            r = int(np.flatnonzero(ref == ref.max())[0])
+            if t != r:
+                err = np.abs(logits_gpu[b, i].astype(np.float64) - ref_logits[b][i]).max() / tau
+                gap = ref[r] - ref[t]
+                assert gap <= NEAR_TIE_FACTOR * err + eps, (b, i, t, r, gap, err)
+                ties.append((b, i, float(gap)))
+    return ties
+
+
+def ref_verify_sample(T, Q, d, tau, seed):
+    B, K = d.shape
+    em = np.full((B, K + 1), -1, dtype=np.int64)
+    acc = np.zeros(B, dtype=np.int64)
+    rs = []
+    for b in range(B):
+        r = S.verify_sample(T[b], Q[b], d[b], tau, seed, b)
+        em[b, :r["n"] + 1] = r["emitted"]
+        acc[b] = r["n"]
+        rs.append(r)
+    return em, acc, rs
+
+
+def is_near_tie(T, Q, d, tau, seed, b, n_gpu, r):
+    """A disagreement is a near-tie when an acceptance margin up to the
+    earlier stop is within rounding, or the emitted row's two best keys are."""
+    logq = S.log_softmax_rows(Q[b], tau)
+    logp = S.log_softmax_rows(T[b], tau)
+    stop = min(n_gpu, r["n"])
+    for i, m in enumerate(r["margins"][:stop + 1]):
+        q = np.exp(logq[i, int(d[b, i])])
+        if abs(m) <= ACCEPT_EPS * max(q, 1e-30):
+            return True
+    if n_gpu == r["n"]:
+        n = r["n"]
+        K = Q.shape[1]
+        p = np.exp(logp[n])
+        wgt = np.maximum(p - np.exp(logq[n]), 0.0) if n < K else p
+        with np.errstate(divide="ignore"):
+            key = np.log(wgt) + S.gumbel(np.arange(T.shape[2]), n, b, S.STREAM_CORRECT, seed)
+        top = np.sort(key[np.isfinite(key)])[-2:]
+        return len(top) == 2 and top[1] - top[0] <= 1e-4 * (1 + abs(top[1]))
+    return False

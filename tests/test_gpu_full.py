@@ -54,3 +54,43 @@ def test_full_size_draft_and_verify(name):
     assert int(best.cpu()[0]) == rbest
     if not ties:
         assert [n for n, _ in res] == list(planted)
+
+
+def test_full_size_sampled_draft_and_verify():
+    """Qwen3-8B-shaped step at temperature 1 in the launch configuration
+    bench.py times (fm_draft_sample, then fm_verify_sample on the unplanted
+    target logits): logits within 2e-2, sampled tokens and the verifier's
+    outcome equal to the oracle's except reported near-ties."""
+    from gpu_util import check_sampled_tokens, is_near_tie, ref_verify_sample
+    cfg = synth.CONFIGS["qwen3_8b_t1"]
+    tau = cfg.temperature
+    print("[full parity] qwen3_8b_t1", flush=True)
+    w = synth.make_weights(cfg)
+    feats = synth.make_features(cfg)
+    noise = synth.make_noise(cfg)
+    dr = make_drafter(cfg, w, max_new=max(cfg.n_new, 1))
+    dr.set_schedule(cfg.times)
+    dr.append(to_dev(feats[:cfg.c_prefill]))
+    T = synth.make_target_logits(cfg)
+    T_dev = to_dev(T)
+    outcomes = []
+    for seed in synth.SAMPLE_SEEDS[:3]:
+        dr.truncate(cfg.c_prefill)
+        tok, logits, lse = dr.draft_sample(to_dev(noise), tau, seed, new_feats=to_dev(feats[cfg.c_prefill:]))
+        e, a = dr.verify_sample(T_dev, logits, lse, tok, tau, seed)
+        torch.cuda.synchronize()
+        outcomes.append((seed, tok.cpu().numpy(), logits.cpu().numpy(), e.cpu().numpy(), a.cpu().numpy()))
+    del dr
+    W = oracle.Weights.from_storage(w)
+    ref_logits = oracle.draft(W, cfg, noise[0], feats)["logits"]
+    del W
+    Tv = synth.values(T).astype(np.float64)
+    for seed, tok, logits, e, a in outcomes:
+        rel = rowwise_rel_err(logits[0], ref_logits)
+        assert rel.max() <= LOGIT_RTOL, rel.max()
+        ties = check_sampled_tokens(tok, logits, [ref_logits], tau, seed)
+        re, ra, rs = ref_verify_sample(Tv, logits.astype(np.float64), tok, tau, seed)
+        if a[0] != ra[0] or not np.array_equal(e[0], re[0]):
+            assert is_near_tie(Tv, logits.astype(np.float64), tok, tau, seed, 0, int(a[0]), rs[0])
+            ties.append(("verify", seed))
+        print(f"  seed {seed}: logit error {rel.max():.2e}, accepted {int(a[0])}, near-ties {ties}", flush=True)
