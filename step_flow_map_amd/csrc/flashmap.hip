@@ -63,7 +63,8 @@ constexpr int ATT_WAVES = 8;  // waves per attention workgroup
 constexpr int GEMM_MAX_SPLIT = GEMM_SPLIT_MAX;
 constexpr int LM_WAVES = 8;
 constexpr int LM_GRID = 512;  // most LM head workgroups (keys per row)
-constexpr int VS_MAX_SLICES = 64;  // vocabulary slices of the probabilistic verifier
+constexpr int VS_MAX_SLICES = VS_THREADS;  // vocabulary slices of the probabilistic verifier
+constexpr int VS_SLICE = 1024;             // tokens per slice (at least)
 constexpr int EMB_WAVES = 8;
 constexpr int MAX_PREFILL_ROWS = 16;
 constexpr int N_COUNTER_SLOTS = 1024;  // counters, COUNTER_STRIDE words apart
@@ -157,7 +158,8 @@ int cache_positions(const fm_config& c) { return cdiv(c.C_max, ATT_BLK) * ATT_BL
 
 struct Layout {
   size_t cache, mods, sched, h, e_state, u_pre, act_qkv, act_d, attn_o, act_f, qkv;
-  size_t att_po, att_ml, partial, lm_part, lm_lse, counters, dsoft, logits_tmp, sm_part, vs_stats, vs_keys, total;
+  size_t att_po, att_ml, partial, lm_part, lm_lse, counters, dsoft, logits_tmp, sm_part, vs_stats, vs_lse, vs_n,
+      vs_keys, total;
 };
 
 int max_rows(const fm_config& c) { return c.max_branches * KB; }
@@ -206,7 +208,9 @@ Layout make_layout(const fm_config& c) {
   L.lm_part = take((size_t)LM_GRID * Mb * 8);
   L.lm_lse = take((size_t)LM_GRID * Mb * 8);
   L.vs_stats = take((size_t)c.max_branches * (KB + 1) * VS_MAX_SLICES * 8);
-  L.vs_keys = take((size_t)c.max_branches * (KB + 1) * VS_MAX_SLICES * 16);
+  L.vs_lse = take((size_t)c.max_branches * (KB + 1) * 4);
+  L.vs_n = take((size_t)c.max_branches * 4);
+  L.vs_keys = take((size_t)c.max_branches * VS_MAX_SLICES * 16);
   L.counters = take((size_t)N_COUNTER_SLOTS * COUNTER_STRIDE * 4);
   if (c.max_steps > 1) {
     L.dsoft = take(Mb * (size_t)c.V * es);
@@ -764,21 +768,24 @@ fm_status verify_sample_impl(fm_handle* h, const void* tl, int B, const float* Q
   a.B = B;
   a.K = KB;
   a.V = c.V;
-  a.S = std::min(VS_MAX_SLICES, cdiv(c.V, 4096));
+  a.S = std::min(VS_MAX_SLICES, cdiv(c.V, VS_SLICE));
   a.slice = cdiv(c.V, a.S);
   a.tau = tau;
   a.seed_lo = (uint32_t)(seed & 0xFFFFFFFFu);
   a.seed_hi = (uint32_t)(seed >> 32);
   a.stats = h->at<float2>(h->lay.vs_stats);
+  a.lse_rows = h->at<float>(h->lay.vs_lse);
+  a.n_acc = h->at<int32_t>(h->lay.vs_n);
   a.keys = h->at<uint64_t>(h->lay.vs_keys);
   a.emitted = emitted;
   a.accept = accept;
-  const dim3 grid(a.S, B * (KB + 1));
-  hipLaunchKernelGGL((vs_stats_kernel<T>), grid, dim3(VS_THREADS), 0, st, a);
+  hipLaunchKernelGGL((vs_stats_kernel<T>), dim3(a.S, B * (KB + 1)), dim3(VS_THREADS), 0, st, a);
   FM_LAUNCHED("vs_stats_kernel");
-  hipLaunchKernelGGL((vs_keys_kernel<T>), grid, dim3(VS_THREADS), 0, st, a);
+  hipLaunchKernelGGL((vs_accept_kernel<T, KB + 1>), dim3(B), dim3(VS_THREADS), 0, st, a);
+  FM_LAUNCHED("vs_accept_kernel");
+  hipLaunchKernelGGL((vs_keys_kernel<T>), dim3(a.S, B), dim3(VS_THREADS), 0, st, a);
   FM_LAUNCHED("vs_keys_kernel");
-  hipLaunchKernelGGL((vs_final_kernel<T>), dim3(B), dim3(64), 0, st, a);
+  hipLaunchKernelGGL(vs_final_kernel, dim3(B), dim3(64), 0, st, a);
   FM_LAUNCHED("vs_final_kernel");
   return FM_OK;
 }

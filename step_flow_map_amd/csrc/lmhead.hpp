@@ -329,10 +329,11 @@ __global__ __launch_bounds__(NW * 64) void lmhead_ks_kernel(LmArgs g) {
 }
 
 // tokens[m] = index of max over G workgroup keys, and with lse_part given
-// lse[m] = log-sum-exp merged from the G workgroup states.  1024 threads, tpr
-// threads per row on consecutive lanes of one wave (M <= 64); each thread
-// keeps eight loads in flight at once, so G = 512 costs one memory latency for
-// up to 16 rows.  The merge order is fixed, so results are reproducible.
+// lse[m] = M + log(sum_g s_g exp(m_g - M)) over the G workgroup states (M the
+// largest m_g; each thread rescales its partial sum once to the row's M).  1024 threads, tpr threads per row on consecutive lanes of
+// one wave (M <= 64); each thread keeps eight loads in flight at once, so
+// G = 512 costs one memory latency for up to 16 rows.  Reductions run over
+// fixed trees, so results are reproducible.
 constexpr int FIN_THREADS = 1024;
 __global__ __launch_bounds__(FIN_THREADS) void argmax_finalize_kernel(const uint64_t* partial, int G, int M,
                                                                      int32_t* tokens, const float2* lse_part,
@@ -343,7 +344,7 @@ __global__ __launch_bounds__(FIN_THREADS) void argmax_finalize_kernel(const uint
   const int m = threadIdx.x / tpr, sub = threadIdx.x % tpr;
   const int mr = m < M ? m : 0;
   uint64_t k = 0ull;
-  float a = -INFINITY, b = 0.f;
+  float mx = -INFINITY, sum = 0.f;  // this thread's states: sum of s_g exp(m_g - mx)
   for (int b0 = sub; b0 < G; b0 += 8 * tpr) {
     uint64_t v[8];
     float2 e[8];
@@ -354,21 +355,33 @@ __global__ __launch_bounds__(FIN_THREADS) void argmax_finalize_kernel(const uint
       v[u] = partial[at];
       if (lse_part) e[u] = lse_part[at];
     }
+    float bm = mx;
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const bool in = b0 + u * tpr < G;
       k = umax64(k, in ? v[u] : 0ull);
-      if (lse_part && in) lse_merge(a, b, e[u].x, e[u].y);
+      if (lse_part && in) bm = fmaxf(bm, e[u].x);
+    }
+    if (lse_part) {
+      float bs = mx == -INFINITY ? 0.f : sum * expf(mx - bm);
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (b0 + u * tpr < G) bs += e[u].y * expf(e[u].x - bm);
+      mx = bm;
+      sum = bs;
     }
   }
+  float gm = mx;
   for (int o = 1; o < tpr; o <<= 1) {  // tpr <= 64
     k = umax64(k, shfl_xor_u64(k, o));
-    if (lse_part) lse_shfl_merge(a, b, o);
+    if (lse_part) gm = fmaxf(gm, __shfl_xor(gm, o, 64));
   }
-  if (m < M && sub == 0) {
-    tokens[m] = (int32_t)argmax_key_index(k);
-    if (lse_part) lse[m] = a + logf(b);
+  if (lse_part) {
+    float t = mx == -INFINITY ? 0.f : sum * expf(mx - gm);
+    for (int o = 1; o < tpr; o <<= 1) t += __shfl_xor(t, o, 64);
+    if (m < M && sub == 0) lse[m] = gm + logf(t);
   }
+  if (m < M && sub == 0) tokens[m] = (int32_t)argmax_key_index(k);
 }
 
 }  // namespace fm

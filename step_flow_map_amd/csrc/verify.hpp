@@ -108,10 +108,11 @@ __global__ __launch_bounds__(64) void verify_prefix_kernel(const int32_t* draft,
 //   emits the Gumbel-max sample (counters (v, n, b, stream 1)) of the residual
 //   max(0, p_n - q_n) when n < K, of p_K when n = K; a residual that is zero
 //   everywhere (p = q in float32) falls back to p_n.
-// Three launches over a [B*(K+1)] x S grid of vocabulary slices: the target
-// rows' (max, sum of exp) per slice; every row's residual and fallback keys
-// per slice (all rows, so no launch waits on n); then one wave per branch
-// finds n and merges row n's keys.  Merge orders are fixed.
+// Four launches: the target rows' (max, sum of exp) per vocabulary slice
+// ([B*(K+1)] x S workgroups); per branch the rows' log-normalisers and the
+// accepted prefix n; row n's residual and fallback keys per slice (B x S);
+// per branch the merge of row n's keys into the emitted tokens.  Merge orders
+// are fixed, so results are reproducible.
 struct VsArgs {
   const void* T;          // [B][K+1][V] target logits
   const float* Q;         // [B][K][V] drafter logits of the last jump
@@ -121,12 +122,109 @@ struct VsArgs {
   float tau;
   uint32_t seed_lo, seed_hi;
   float2* stats;          // [B*(K+1)][S]
-  uint64_t* keys;         // [B*(K+1)][S][2]: residual (or bonus) key, fallback key
+  float* lse_rows;        // [B*(K+1)] log sum_v exp(T / tau) of every target row
+  int32_t* n_acc;         // [B] accepted prefix
+  uint64_t* keys;         // [B][S][2]: row n's residual (or bonus) key, fallback key
   int32_t* emitted;       // [B][K+1]
   int32_t* accept;        // [B]
 };
 
 constexpr int VS_THREADS = 256;
+constexpr int VS_UNROLL = 4;  // loads in flight per thread
+
+template <typename T>
+__global__ __launch_bounds__(VS_THREADS) void vs_stats_kernel(VsArgs g) {
+  __shared__ float2 sw[VS_THREADS / 64];
+  const int s = blockIdx.x, r = blockIdx.y;
+  const T* row = reinterpret_cast<const T*>(g.T) + (size_t)r * g.V;
+  const int v0 = s * g.slice, v1 = min(g.V, v0 + g.slice);
+  float m = -INFINITY, sum = 0.f;
+  for (int base = v0 + (int)threadIdx.x; base < v1; base += VS_UNROLL * VS_THREADS) {
+    float x[VS_UNROLL];
+#pragma unroll
+    for (int u = 0; u < VS_UNROLL; ++u) {
+      const int v = base + u * VS_THREADS;
+      x[u] = to_f32<T>(row[v < v1 ? v : v0]);
+    }
+#pragma unroll
+    for (int u = 0; u < VS_UNROLL; ++u)
+      if (base + u * VS_THREADS < v1) lse_add(m, sum, x[u] / g.tau);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) lse_shfl_merge(m, sum, o);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) sw[wave] = make_float2(m, sum);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < VS_THREADS / 64; ++w) lse_merge(m, sum, sw[w].x, sw[w].y);
+    g.stats[(size_t)r * g.S + s] = make_float2(m, sum);
+  }
+}
+
+// One workgroup per branch: thread t holds slice t of every row (S <= 256;
+// all R = K + 1 loads in flight at once).  A row's log-normaliser is M +
+// log(sum_t s_t exp(m_t - M)) with M the largest slice maximum: a max
+// reduction, one exponential per slice and a sum, each over a fixed tree.
+// Lane i of wave 0 then tests draft i.
+template <typename T, int R>
+__global__ __launch_bounds__(VS_THREADS) void vs_accept_kernel(VsArgs g) {
+  static_assert(R <= 65, "K <= 64");
+  constexpr int NWV = VS_THREADS / 64;
+  __shared__ float smax[R][NWV], ssum[R][NWV];
+  __shared__ float slse[R];
+  const int b = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  // the drafted token's target and drafter logits, loaded up front
+  const bool tester = wave == 0 && lane < g.K;
+  float t_d = 0.f, q_d = 0.f, lseq = 0.f;
+  if (tester) {
+    const int d = min(max(g.draft[b * g.K + lane], 0), g.V - 1);  // memory safety only
+    const T* Tb = reinterpret_cast<const T*>(g.T) + (size_t)b * R * g.V;
+    t_d = to_f32<T>(Tb[(size_t)lane * g.V + d]);
+    q_d = g.Q[((size_t)b * g.K + lane) * g.V + d];
+    lseq = g.lseQ[b * g.K + lane];
+  }
+  float2 e[R];
+#pragma unroll
+  for (int j = 0; j < R; ++j)
+    e[j] = t < g.S ? g.stats[((size_t)b * R + j) * g.S + t] : make_float2(-INFINITY, 0.f);
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    const float m = warp_max(e[j].x);
+    if (lane == 0) smax[j][wave] = m;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    float M = smax[j][0];
+#pragma unroll
+    for (int w = 1; w < NWV; ++w) M = fmaxf(M, smax[j][w]);
+    const float v = t < g.S ? e[j].y * expf(e[j].x - M) : 0.f;
+    const float sum = warp_sum(v);
+    if (lane == 0) ssum[j][wave] = sum;
+  }
+  __syncthreads();
+  for (int j = t; j < R; j += VS_THREADS) {
+    float M = smax[j][0], sum = ssum[j][0];
+    for (int w = 1; w < NWV; ++w) {
+      M = fmaxf(M, smax[j][w]);
+      sum += ssum[j][w];
+    }
+    slse[j] = M + logf(sum);
+    g.lse_rows[b * R + j] = slse[j];
+  }
+  __syncthreads();
+  if (wave == 0) {
+    bool reject = false;
+    if (tester) {
+      const float lp = t_d / g.tau - slse[lane];
+      const float lq = q_d / g.tau - lseq;
+      const float u = uniform_of(philox_x0(0u, (uint32_t)lane, (uint32_t)b, RNG_ACCEPT, g.seed_lo, g.seed_hi));
+      reject = !(u * expf(lq) < expf(lp));
+    }
+    const uint64_t rej = __ballot(reject);
+    if (lane == 0) g.n_acc[b] = rej ? (int)__builtin_ctzll(rej) : g.K;
+  }
+}
 
 // Block-wide max of two keys; thread 0 ends with the results.
 __device__ __forceinline__ void block_max2(uint64_t& a, uint64_t& b) {
@@ -149,88 +247,58 @@ __device__ __forceinline__ void block_max2(uint64_t& a, uint64_t& b) {
     }
 }
 
-template <typename T>
-__global__ __launch_bounds__(VS_THREADS) void vs_stats_kernel(VsArgs g) {
-  __shared__ float2 sw[VS_THREADS / 64];
-  const int s = blockIdx.x, r = blockIdx.y;
-  const T* row = reinterpret_cast<const T*>(g.T) + (size_t)r * g.V;
-  const int v0 = s * g.slice, v1 = min(g.V, v0 + g.slice);
-  float m = -INFINITY, sum = 0.f;
-  for (int v = v0 + (int)threadIdx.x; v < v1; v += VS_THREADS) lse_add(m, sum, to_f32<T>(row[v]) / g.tau);
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) lse_shfl_merge(m, sum, o);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (lane == 0) sw[wave] = make_float2(m, sum);
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    for (int w = 1; w < VS_THREADS / 64; ++w) lse_merge(m, sum, sw[w].x, sw[w].y);
-    g.stats[(size_t)r * g.S + s] = make_float2(m, sum);
-  }
-}
-
-// log-normaliser of target row r from its S slice states (fixed order)
-__device__ __forceinline__ float vs_row_lse(const VsArgs& g, int r) {
-  float m = -INFINITY, sum = 0.f;
-  for (int s = 0; s < g.S; ++s) {
-    const float2 e = g.stats[(size_t)r * g.S + s];
-    lse_merge(m, sum, e.x, e.y);
-  }
-  return m + logf(sum);
-}
-
+// Row n of branch b, slice s: the residual (bonus) key and the fallback key.
 template <typename T>
 __global__ __launch_bounds__(VS_THREADS) void vs_keys_kernel(VsArgs g) {
-  __shared__ float s_lse;
-  const int s = blockIdx.x, r = blockIdx.y;
-  const int b = r / (g.K + 1), j = r % (g.K + 1);
-  if (threadIdx.x == 0) s_lse = vs_row_lse(g, r);
-  __syncthreads();
-  const float lseP = s_lse;
+  const int s = blockIdx.x, b = blockIdx.y;
+  const int n = g.n_acc[b];
+  const int r = b * (g.K + 1) + n;
+  const float lseP = g.lse_rows[r];
   const T* row = reinterpret_cast<const T*>(g.T) + (size_t)r * g.V;
-  const bool bonus = j == g.K;
-  const float* qrow = bonus ? nullptr : g.Q + ((size_t)b * g.K + j) * g.V;
-  const float lseQ = bonus ? 0.f : g.lseQ[b * g.K + j];
+  const bool bonus = n == g.K;
+  const float* qrow = g.Q + ((size_t)b * g.K + (bonus ? 0 : n)) * g.V;
+  const float lseQ = bonus ? 0.f : g.lseQ[b * g.K + n];
   const int v0 = s * g.slice, v1 = min(g.V, v0 + g.slice);
   uint64_t k1 = 0ull, k2 = 0ull;
-  for (int v = v0 + (int)threadIdx.x; v < v1; v += VS_THREADS) {
-    const float lp = to_f32<T>(row[v]) / g.tau - lseP;
-    const float G = gumbel_of(philox_x0((uint32_t)v, (uint32_t)j, (uint32_t)b, RNG_CORRECT, g.seed_lo, g.seed_hi));
-    k2 = umax64(k2, argmax_key(lp + G, (uint32_t)v));
-    if (bonus) {
-      k1 = umax64(k1, argmax_key(lp + G, (uint32_t)v));
-    } else {
-      const float w = expf(lp) - expf(qrow[v] / g.tau - lseQ);
-      if (w > 0.f) k1 = umax64(k1, argmax_key(logf(w) + G, (uint32_t)v));
+  for (int base = v0 + (int)threadIdx.x; base < v1; base += VS_UNROLL * VS_THREADS) {
+    float x[VS_UNROLL], q[VS_UNROLL];
+#pragma unroll
+    for (int u = 0; u < VS_UNROLL; ++u) {
+      const int v = base + u * VS_THREADS < v1 ? base + u * VS_THREADS : v0;
+      x[u] = to_f32<T>(row[v]);
+      q[u] = qrow[v];
+    }
+#pragma unroll
+    for (int u = 0; u < VS_UNROLL; ++u) {
+      const int v = base + u * VS_THREADS;
+      if (v >= v1) continue;
+      const float lp = x[u] / g.tau - lseP;
+      const float G = gumbel_of(philox_x0((uint32_t)v, (uint32_t)n, (uint32_t)b, RNG_CORRECT, g.seed_lo, g.seed_hi));
+      k2 = umax64(k2, argmax_key(lp + G, (uint32_t)v));
+      if (bonus) {
+        k1 = umax64(k1, argmax_key(lp + G, (uint32_t)v));
+      } else {
+        const float w = expf(lp) - expf(q[u] / g.tau - lseQ);
+        if (w > 0.f) k1 = umax64(k1, argmax_key(logf(w) + G, (uint32_t)v));
+      }
     }
   }
   block_max2(k1, k2);
   if (threadIdx.x == 0) {
-    g.keys[((size_t)r * g.S + s) * 2 + 0] = k1;
-    g.keys[((size_t)r * g.S + s) * 2 + 1] = k2;
+    g.keys[((size_t)b * g.S + s) * 2 + 0] = k1;
+    g.keys[((size_t)b * g.S + s) * 2 + 1] = k2;
   }
 }
 
-// one wave per branch; lane i tests draft i (K <= 64), lanes merge row n's
-// slice keys (S <= 64)
-template <typename T>
+// one wave per branch: merge row n's slice keys (S <= VS_THREADS), write the
+// emitted tokens
 __global__ __launch_bounds__(64) void vs_final_kernel(VsArgs g) {
   const int b = blockIdx.x, lane = threadIdx.x;
-  const T* Tb = reinterpret_cast<const T*>(g.T) + (size_t)b * (g.K + 1) * g.V;
-  bool reject = false;
-  if (lane < g.K) {
-    const int d = min(max(g.draft[b * g.K + lane], 0), g.V - 1);  // memory safety only
-    const float lp = to_f32<T>(Tb[(size_t)lane * g.V + d]) / g.tau - vs_row_lse(g, b * (g.K + 1) + lane);
-    const float lq = g.Q[((size_t)b * g.K + lane) * g.V + d] / g.tau - g.lseQ[b * g.K + lane];
-    const float u = uniform_of(philox_x0(0u, (uint32_t)lane, (uint32_t)b, RNG_ACCEPT, g.seed_lo, g.seed_hi));
-    reject = !(u * expf(lq) < expf(lp));
-  }
-  const uint64_t rej = __ballot(reject);
-  const int n = rej ? (int)__builtin_ctzll(rej) : g.K;
-  const int r = b * (g.K + 1) + n;
+  const int n = g.n_acc[b];
   uint64_t k1 = 0ull, k2 = 0ull;
-  if (lane < g.S) {
-    k1 = g.keys[((size_t)r * g.S + lane) * 2 + 0];
-    k2 = g.keys[((size_t)r * g.S + lane) * 2 + 1];
+  for (int t = lane; t < g.S; t += 64) {
+    k1 = umax64(k1, g.keys[((size_t)b * g.S + t) * 2 + 0]);
+    k2 = umax64(k2, g.keys[((size_t)b * g.S + t) * 2 + 1]);
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
