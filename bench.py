@@ -40,7 +40,7 @@ def lm_kernel_name(cfg) -> str:
     """The LM head kernel the library plans for this shape: k split over the
     8 waves when z fits in registers (row tiles x chunks per wave <= 4)."""
     ve = 8 if cfg.dtype == "bf16" else 4
-    mt = -(-cfg.B * cfg.K // 16)
+    mt = -(-cfg.B * cfg.requests * cfg.K // 16)
     cpw = -(-(-(-cfg.d // (32 * ve))) // 8)
     return "lmhead_ks_kernel" if mt * cpw <= 4 else "lmhead_kernel"
 
@@ -49,7 +49,9 @@ def alg_bytes(cfg) -> dict:
     """Algorithmic bytes of one step: every weight read once, the context K/V
     read once, inputs and outputs once (adaLN vectors are precomputed)."""
     es = 2 if cfg.dtype == "bf16" else 4
-    d, F, V, L, K, B = cfg.d, cfg.F, cfg.V, cfg.L, cfg.K, cfg.B
+    d, F, V, L, K = cfg.d, cfg.F, cfg.V, cfg.L, cfg.K
+    B = cfg.B * cfg.requests   # row blocks: branches of one request or requests of a batch
+    R = cfg.requests           # contexts
     n = cfg.num_steps
     Mb = B * K
     parts = {
@@ -57,10 +59,10 @@ def alg_bytes(cfg) -> dict:
         "W_lm": n * V * d * es,
         "blocks": n * L * ((3 * d * d + d * d + F * d + d * F) + (3 * d + d + F + d)) * es,
         "fusion": (d * 5 * cfg.H + d) * es,
-        "ctx_kv_read": n * L * cfg.C * 2 * d * es,
-        "ctx_kv_write": L * cfg.n_new * 2 * d * es,
+        "ctx_kv_read": n * L * R * cfg.C * 2 * d * es,
+        "ctx_kv_write": L * R * cfg.n_new * 2 * d * es,
         "noise": Mb * V * es,
-        "feats": cfg.n_new * 5 * cfg.H * es,
+        "feats": R * cfg.n_new * 5 * cfg.H * es,
         "target_logits": B * (K + 1) * V * es,
         "mod_vectors": n * (6 * L + 2) * d * 4,
         "softmax_round_trip": (n - 1) * Mb * V * (4 + 4 + es + es),
@@ -74,7 +76,7 @@ def alg_bytes(cfg) -> dict:
 
 def kernel_alg_bytes(cfg, kernel: str) -> int:
     es = 2 if cfg.dtype == "bf16" else 4
-    Mb = cfg.B * cfg.K
+    Mb = cfg.B * cfg.requests * cfg.K
     if kernel.startswith("lmhead"):    # W_lm, z in, tokens out (sampled: float32 logits out)
         return cfg.V * cfg.d * es + Mb * cfg.d * es + Mb * 4 + (Mb * cfg.V * 4 if cfg.temperature > 0 else 0)
     if kernel == "embed_kernel":       # E, x in, e and h out (float32)
@@ -114,6 +116,8 @@ def cpu_baseline(cfg, w, noise, feats, T):
     steps = 0
     t0 = time.perf_counter()
     while True:   # whole steps until about 10 s of CPU work
+        for r in range(1, cfg.requests):   # the other requests of a batch (own contexts)
+            oracle.draft(W, cfg, noise[r], synth.make_features(cfg, request=r))
         ref = oracle.draft(W, cfg, noise[0], feats)
         if cfg.temperature > 0:
             d = oracle.sampling.sample_draft(ref["logits"], cfg.temperature, synth.SAMPLE_SEEDS[0])
@@ -174,8 +178,8 @@ def main():
     t_gen = time.perf_counter()
     w = synth.make_weights(cfg)
     feats = synth.make_features(cfg)
-    noise = synth.make_noise(cfg)
-    T_raw = synth.make_target_logits(cfg)
+    noise = synth.make_noise(cfg, cfg.B * cfg.requests)
+    T_raw = synth.make_target_logits(cfg, cfg.B * cfg.requests)
     print(f"[bench] inputs generated in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
 
     baseline = None
@@ -185,18 +189,22 @@ def main():
         print(f"[bench] oracle {baseline['sample']}", file=sys.stderr, flush=True)
 
     dev = torch.device("cuda", 0)
+    R = cfg.requests
+    NB = cfg.B * R   # row blocks
     c = fm.make_config(K=cfg.K, V=cfg.V, d=cfg.d, L=cfg.L, n_heads=cfg.nh, H=cfg.H, C_max=cfg.capacity,
-                       dtype=cfg.dtype, max_branches=cfg.B, max_new=max(cfg.n_new, 1),
-                       max_steps=cfg.num_steps)
+                       dtype=cfg.dtype, max_branches=cfg.B, max_new=max(R * cfg.n_new, 1),
+                       max_steps=cfg.num_steps, max_requests=R)
     dr = fm.Drafter(c, binding_weights(w))
     dr.set_schedule(cfg.times)
+    req_feats = [feats] + [synth.make_features(cfg, request=r) for r in range(1, R)]
     if cfg.c_prefill:
-        dr.append(to_dev(feats[:cfg.c_prefill]))
+        for r in range(R):
+            dr.append_req(r, to_dev(req_feats[r][:cfg.c_prefill]))
     x = to_dev(noise)
-    new = to_dev(feats[cfg.c_prefill:]) if cfg.n_new else None
-    tokens = torch.empty(cfg.B, cfg.K, dtype=torch.int32, device=dev)
-    emitted = torch.empty(cfg.B, cfg.K + 1, dtype=torch.int32, device=dev)
-    accept = torch.empty(cfg.B, dtype=torch.int32, device=dev)
+    new = to_dev(np.concatenate([f[cfg.c_prefill:] for f in req_feats])) if cfg.n_new else None
+    tokens = torch.empty(NB, cfg.K, dtype=torch.int32, device=dev)
+    emitted = torch.empty(NB, cfg.K + 1, dtype=torch.int32, device=dev)
+    accept = torch.empty(NB, dtype=torch.int32, device=dev)
     best = torch.empty(1, dtype=torch.int32, device=dev)
     torch.cuda.synchronize()
 
@@ -207,7 +215,10 @@ def main():
         lse_q = torch.empty(cfg.B, cfg.K, dtype=torch.float32, device=dev)
 
     def draft_and_verify(T, seed):
-        if temp > 0:
+        if R > 1:
+            dr.draft_batch(x, new_feats=new, n_new=[cfg.n_new] * R, tokens=tokens)
+            fm.fm_verify(T, tokens, emitted, accept, best)
+        elif temp > 0:
             fm.fm_draft_sample(dr.handle, x, temp, seed, tokens, logits_q, lse_q, new_feats=new)
             fm.fm_verify_sample(dr.handle, T, logits_q, lse_q, tokens, temp, seed, emitted, accept)
         else:
@@ -221,12 +232,20 @@ def main():
         sets = [(T_dev, s, None) for s in synth.SAMPLE_SEEDS]
     else:
         # draft once to learn the tokens when the oracle did not run
-        dr.truncate(cfg.c_prefill)
-        dr.draft(x, new_feats=new, tokens=tokens)
+        for r in range(R):
+            dr.truncate_req(r, cfg.c_prefill)
+        draft_and_verify(to_dev(T_raw), 0)
         gpu_tokens = tokens.cpu().numpy()
         plant_from = ref_tokens[None] if ref_tokens is not None else gpu_tokens
         planted = synth.PLANTED_ACCEPT_TREE if cfg.B > 1 else synth.PLANTED_ACCEPT
-        if cfg.B > 1:
+        if R > 1:   # every request planted with the same accept length, one set per length
+            plant_from = gpu_tokens
+            if ref_tokens is not None:
+                plant_from = np.concatenate([ref_tokens[None], gpu_tokens[1:]])
+            for n in planted:
+                src = np.stack([synth.plant(T_raw[r], plant_from[r], n) for r in range(R)])
+                sets.append((to_dev(src), 0, [n] * R))
+        elif cfg.B > 1:
             src = np.stack([synth.plant(T_raw[b], gpu_tokens[b], planted[b]) for b in range(cfg.B)])
             sets.append((to_dev(src), 0, list(planted)))
         else:
@@ -234,7 +253,8 @@ def main():
                 sets.append((to_dev(synth.plant(T_raw[0], plant_from[0], n)[None]), 0, [n]))
 
     def step(T, seed):
-        dr.truncate(cfg.c_prefill)
+        for r in range(R):
+            dr.truncate_req(r, cfg.c_prefill)
         draft_and_verify(T, seed)
 
     stream = torch.cuda.current_stream()
@@ -244,7 +264,8 @@ def main():
             step(T, seed)   # warm the path outside capture
             torch.cuda.synchronize()
             g = torch.cuda.CUDAGraph()
-            dr.truncate(cfg.c_prefill)
+            for r in range(R):
+                dr.truncate_req(r, cfg.c_prefill)
             with torch.cuda.graph(g):
                 draft_and_verify(T, seed)
             graphs.append(g)
@@ -315,7 +336,8 @@ def main():
                 "target logits planted for accept lengths 7,7,7,7,7,7,7,6,6,6)"),
         "config": {"workload": cfg.name, "K": cfg.K, "V": cfg.V, "d": cfg.d, "L": cfg.L,
                    "heads": cfg.nh, "H": cfg.H, "context": cfg.C, "new_rows_per_step": cfg.n_new,
-                   "branches": cfg.B, "schedule": list(cfg.times), "temperature": cfg.temperature,
+                   "branches": cfg.B, "requests": R, "schedule": list(cfg.times),
+                   "temperature": cfg.temperature,
                    "replay": "eager" if args.eager else "hipgraph"},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": kd["gbs"], "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": kd["gbs"] / HBM_PEAK_GBS, "traffic": traffic,

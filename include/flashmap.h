@@ -57,7 +57,8 @@ typedef enum fm_dtype {
  *   divides d with d / n_heads in {64, 128}; mlp_mult >= 1; n_ctx_layers == 5;
  *   V >= 16 and H >= 1 with V and H multiples of 8 (bf16) or 4 (f32), so
  *   every row starts 16-byte aligned;
- *   1 <= max_branches <= 4; 0 <= max_new <= 16; C_max >= 0; 1 <= max_steps <= 4. */
+ *   1 <= max_branches <= 4; 0 <= max_new <= 16; C_max >= 0; 1 <= max_steps <= 4;
+ *   1 <= max_requests <= 4, and max_branches == 1 when max_requests > 1. */
 typedef struct fm_config {
   int K;             /* drafted block length (16)                            */
   int V;             /* vocabulary size (151936 for Qwen3)                    */
@@ -72,6 +73,8 @@ typedef struct fm_config {
   int max_new;       /* context rows a single fm_draft call may append        */
   int max_steps;     /* flow-map jumps per draft (1, or 2 for num_steps = 2)  */
   fm_dtype dtype;    /* storage type of weights, features, noise              */
+  int max_requests;  /* independent requests, each with its own context of up
+                        to C_max rows (1, or up to 4 for batched drafting)     */
 } fm_config;
 
 /* Weights of one DiT block, all row-major [out][in], dtype = cfg.dtype:
@@ -104,9 +107,9 @@ typedef struct fm_weights {
 typedef struct fm_handle fm_handle;
 
 /* Bytes of device workspace a handle with this configuration needs (per DiT
- * block a key and a value cache of ceil(C_max/32)*32 + 32*max_branches
- * positions of width d, modulation vectors, activations, split-K partials and
- * counters).  Returns 0 for an invalid configuration. */
+ * block and request a key and a value cache of ceil(C_max/32)*32 +
+ * 32*max_branches positions of width d, modulation vectors, activations,
+ * split-K partials and counters).  Returns 0 for an invalid configuration. */
 size_t fm_workspace_bytes(const fm_config *cfg);
 
 /* Create a handle on `device` using the caller's workspace (device memory of
@@ -153,6 +156,13 @@ fm_status fm_context_truncate(fm_handle *h, int new_len);
 /* Current context length (rows), or -1 for a NULL handle. */
 int fm_context_length(const fm_handle *h);
 
+/* The same three calls for request `req` (0 <= req < max_requests) of a
+ * handle that holds several requests; the calls above act on request 0.
+ * Errors as above, plus FM_EINVAL for req out of range (length: -1). */
+fm_status fm_context_append_req(fm_handle *h, int req, const void *feats, int n, void *stream);
+fm_status fm_context_truncate_req(fm_handle *h, int req, int new_len);
+int fm_context_length_req(const fm_handle *h, int req);
+
 /* One drafting step (feinterview.poetries.top, first section: the same noise
  * decides every position of the block jointly; wire.sakhanda.co, "Что такое
  * FlashMap?": K proposals from Gaussian noise in one step).
@@ -193,6 +203,25 @@ fm_status fm_draft(fm_handle *h, const void *noise, int B, const void *new_feats
 fm_status fm_draft_sample(fm_handle *h, const void *noise, int B, const void *new_feats, int n_new,
                           float temperature, uint64_t seed, int32_t *tokens, float *logits, float *lse,
                           void *stream);
+
+/* One drafting step for R independent requests at once (serving with more
+ * than one concurrent request; the pages measure concurrency 1 only,
+ * feinterview.poetries.top, results section).  Row block r (16 rows) is
+ * request r: it attends to request r's context plus its own block, exactly as
+ * fm_draft with B = 1 on that request alone; the contractions stream every
+ * weight once for all R * 16 rows.
+ *   noise     [R][K][V]  one noise block per request
+ *   R         1 <= R <= max_requests
+ *   new_feats [sum n_new][n_ctx_layers][H] context rows appended first, the
+ *             rows of request 0, then request 1, ... (NULL when no rows)
+ *   n_new     HOST array of R counts (NULL: none), sum <= max_new
+ *   tokens    [R][K] int32 output; logits [R][K][V] float32 output or NULL
+ * Each request's context advances by its n_new.  fm_verify with B = R then
+ * verifies the requests independently (its best output is meaningless here).
+ * Errors: FM_EINVAL, FM_ECAPACITY (R > max_requests, a request's context over
+ * C_max, sum n_new > max_new), FM_ESTATE, FM_EHIP. */
+fm_status fm_draft_batch(fm_handle *h, const void *noise, int R, const void *new_feats, const int *n_new,
+                         int32_t *tokens, float *logits, void *stream);
 
 /* Greedy verification (feinterview.poetries.top, first section;
  * wire.sakhanda.co, "Что такое FlashMap?"; alphasignal.ai, "Why drafting

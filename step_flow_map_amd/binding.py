@@ -28,7 +28,7 @@ TOP_FIELDS = ("E", "W_lm", "W_f", "b_f", "te_s_W1", "te_s_b1", "te_s_W2", "te_s_
 class fm_config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int) for n in
                 ("K", "V", "d", "L", "n_heads", "mlp_mult", "H", "n_ctx_layers", "C_max",
-                 "max_branches", "max_new", "max_steps", "dtype")]
+                 "max_branches", "max_new", "max_steps", "dtype", "max_requests")]
 
 
 class fm_block_weights(ctypes.Structure):
@@ -74,6 +74,14 @@ def lib() -> ctypes.CDLL:
     L.fm_context_truncate.restype = st
     L.fm_context_length.argtypes = [vp]
     L.fm_context_length.restype = i
+    L.fm_context_append_req.argtypes = [vp, i, vp, i, vp]
+    L.fm_context_append_req.restype = st
+    L.fm_context_truncate_req.argtypes = [vp, i, i]
+    L.fm_context_truncate_req.restype = st
+    L.fm_context_length_req.argtypes = [vp, i]
+    L.fm_context_length_req.restype = i
+    L.fm_draft_batch.argtypes = [vp, vp, i, vp, ctypes.POINTER(ctypes.c_int), vp, vp, vp]
+    L.fm_draft_batch.restype = st
     L.fm_draft.argtypes = [vp, vp, i, vp, i, vp, vp, vp, vp]
     L.fm_draft.restype = st
     L.fm_verify.argtypes = [vp, i, i, i, i, vp, vp, vp, vp, vp]
@@ -123,11 +131,11 @@ def dtype_code(t: torch.dtype) -> int:
 
 
 def make_config(*, K=16, V, d, L, n_heads, H, C_max, dtype="bf16", mlp_mult=4, n_ctx_layers=5,
-                max_branches=1, max_new=16, max_steps=2) -> fm_config:
+                max_branches=1, max_new=16, max_steps=2, max_requests=1) -> fm_config:
     return fm_config(K=K, V=V, d=d, L=L, n_heads=n_heads, mlp_mult=mlp_mult, H=H,
                      n_ctx_layers=n_ctx_layers, C_max=C_max, max_branches=max_branches,
                      max_new=max_new, max_steps=max_steps,
-                     dtype=FM_BF16 if dtype in ("bf16", FM_BF16) else FM_F32)
+                     dtype=FM_BF16 if dtype in ("bf16", FM_BF16) else FM_F32, max_requests=max_requests)
 
 
 # ----------------------------------------------------------------- C entry points
@@ -177,6 +185,30 @@ def fm_context_truncate(h, new_len: int):
 
 def fm_context_length(h) -> int:
     return int(lib().fm_context_length(h))
+
+
+def fm_context_append_req(h, req: int, feats, stream=None):
+    n = 0 if feats is None else int(feats.shape[0])
+    _check(lib().fm_context_append_req(h, int(req), _ptr(feats), n, _stream(stream)))
+
+
+def fm_context_truncate_req(h, req: int, new_len: int):
+    _check(lib().fm_context_truncate_req(h, int(req), int(new_len)))
+
+
+def fm_context_length_req(h, req: int) -> int:
+    return int(lib().fm_context_length_req(h, int(req)))
+
+
+def fm_draft_batch(h, noise, tokens, new_feats=None, n_new=None, logits=None, stream=None):
+    """noise [R][K][V]; tokens [R][K] int32 out; new_feats [sum n_new][5][H] or
+    None; n_new: R counts (host) or None; logits [R][K][V] float32 or None."""
+    R = int(noise.shape[0])
+    counts = None
+    if n_new is not None:
+        counts = (ctypes.c_int * R)(*[int(x) for x in n_new])
+    _check(lib().fm_draft_batch(h, _ptr(noise), R, _ptr(new_feats), counts, _ptr(tokens), _ptr(logits),
+                                _stream(stream)))
 
 
 def fm_draft(h, noise, tokens, new_feats=None, logits=None, hidden=None, stream=None):
@@ -255,6 +287,21 @@ class Drafter:
 
     def truncate(self, n):
         fm_context_truncate(self.handle, n)
+
+    def append_req(self, req, feats, stream=None):
+        fm_context_append_req(self.handle, req, feats, stream)
+
+    def truncate_req(self, req, n):
+        fm_context_truncate_req(self.handle, req, n)
+
+    def context_length_req(self, req):
+        return fm_context_length_req(self.handle, req)
+
+    def draft_batch(self, noise, new_feats=None, n_new=None, logits=None, tokens=None, stream=None):
+        if tokens is None:
+            tokens = torch.empty(noise.shape[0], noise.shape[1], dtype=torch.int32, device=self.device)
+        fm_draft_batch(self.handle, noise, tokens, new_feats, n_new, logits, stream)
+        return tokens
 
     @property
     def context_length(self):

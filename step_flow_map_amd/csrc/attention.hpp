@@ -33,6 +33,7 @@
 namespace fm {
 
 constexpr int ATT_RANGES_MAX = 8;  // ranges per (branch, head) = arrivals per counter
+constexpr int FM_MAX_REQ = 4;      // requests with their own context in one launch
 constexpr int ATT_BLK = 32;        // keys per block
 
 // slot of key kk (0..31) inside a 32-key block of the value cache
@@ -45,12 +46,14 @@ template <> __host__ __device__ __forceinline__ int vt_slot<float>(int kk) { ret
 struct AttnArgs {
   const void* q;       // [B*K][ldq] queries of the block rows
   int ldq;
-  const void* kc;      // this DiT block's key cache   [nh][P][hd]
-  const void* vt;      // this DiT block's value cache [nh][P/32][hd][32]
+  const void* kc;      // this DiT block's key cache   [nh][P][hd] (request 0)
+  const void* vt;      // this DiT block's value cache [nh][P/32][hd][32] (request 0)
+  size_t req_stride;   // elements between consecutive requests' caches
   int P;               // positions per head (multiple of 32)
-  int C;               // context rows visible
-  int ctx_blocks;      // ceil(C / 32)
-  int scratch_blk;     // block index of branch 0's rows (branch b at +b)
+  int C[FM_MAX_REQ];   // context rows visible to branch b
+  int scratch_blk;     // block index of the first block rows
+  int scratch_step;    // 1: branches share request 0's cache (branch b at scratch_blk + b);
+                       // 0: branch b is request b (its rows at scratch_blk of its own cache)
   int K, d, nh;
   int n_ranges;        // ranges per (branch, head), <= 8
   int blocks_per_range;
@@ -79,11 +82,14 @@ __global__ __launch_bounds__(NW * 64) void attention_kernel(AttnArgs g) {
   const int range = blockIdx.x % g.n_ranges;
   const int bh = blockIdx.x / g.n_ranges;
   const int head = bh % g.nh, b = bh / g.nh;
-  const int nblk = g.ctx_blocks + 1;
+  const int C = g.C[b];
+  const int ctx_blocks = (C + ATT_BLK - 1) / ATT_BLK;
+  const int nblk = ctx_blocks + 1;
   const int blo = range * g.blocks_per_range;
-  const int bhi = min(nblk, blo + g.blocks_per_range);
-  const T* kbase = reinterpret_cast<const T*>(g.kc) + (size_t)head * g.P * HD;
-  const T* vbase = reinterpret_cast<const T*>(g.vt) + (size_t)head * (g.P / ATT_BLK) * HD * ATT_BLK;
+  const int bhi = min(nblk, blo + g.blocks_per_range);  // empty for ranges past a short context
+  const size_t rb = g.scratch_step ? 0 : (size_t)b * g.req_stride;
+  const T* kbase = reinterpret_cast<const T*>(g.kc) + rb + (size_t)head * g.P * HD;
+  const T* vbase = reinterpret_cast<const T*>(g.vt) + rb + (size_t)head * (g.P / ATT_BLK) * HD * ATT_BLK;
 
   // queries (B operand): lane (row j, group grp) holds piece 4s+grp of query j
   VT qf[QS];
@@ -98,8 +104,8 @@ __global__ __launch_bounds__(NW * 64) void attention_kernel(AttnArgs g) {
     VT v[PS][OT];    // value dims 16t + j, slots ps*4*VE + grp*VE ..
   };
   // physical block and number of valid keys of logical block bi
-  auto phys = [&](int bi) { return bi < g.ctx_blocks ? bi : g.scratch_blk + b; };
-  auto nvalid = [&](int bi) { return bi < g.ctx_blocks ? min(ATT_BLK, g.C - ATT_BLK * bi) : KB; };
+  auto phys = [&](int bi) { return bi < ctx_blocks ? bi : g.scratch_blk + g.scratch_step * b; };
+  auto nvalid = [&](int bi) { return bi < ctx_blocks ? min(ATT_BLK, C - ATT_BLK * bi) : KB; };
   auto load = [&](Tile& t, int bi) {
     const int pb = phys(bi);
 #pragma unroll
@@ -247,7 +253,8 @@ __global__ __launch_bounds__(NW * 64) void attention_kernel(AttnArgs g) {
   for (int c = 0; c < CPT; ++c) acc[c] = 0.f;
 #pragma unroll
   for (int w = 0; w < NW; ++w) {
-    const float wt = expf(sm[w][row] - M);  // 0 for waves without blocks
+    // 0 for waves without blocks (and for a range without blocks, where M = -inf)
+    const float wt = M == -INFINITY ? 0.f : expf(sm[w][row] - M);
     Lsum += wt * sl[w][row];
 #pragma unroll
     for (int c = 0; c < CPT; ++c) acc[c] += wt * so[w][row][c0 + c];

@@ -154,7 +154,11 @@ AttnPlan plan_attention(int n_blocks) {
 
 // cache positions per head: the context capacity rounded up to whole 32-key
 // blocks, then one scratch block per branch for the branch's block rows
+// positions per head of one request's cache: its context, then one 32-position
+// block per branch for the block rows
 int cache_positions(const fm_config& c) { return cdiv(c.C_max, ATT_BLK) * ATT_BLK + ATT_BLK * c.max_branches; }
+// row blocks of one draft: branches of one request, or requests of one batch
+int max_blocks(const fm_config& c) { return std::max(c.max_branches, c.max_requests); }
 
 struct Layout {
   size_t cache, mods, sched, h, e_state, u_pre, act_qkv, act_d, attn_o, act_f, qkv;
@@ -162,7 +166,7 @@ struct Layout {
       vs_keys, total;
 };
 
-int max_rows(const fm_config& c) { return c.max_branches * KB; }
+int max_rows(const fm_config& c) { return max_blocks(c) * KB; }
 
 size_t partial_bytes(const fm_config& c) {
   const int Mb = max_rows(c), F = c.mlp_mult * c.d, d = c.d;
@@ -191,7 +195,8 @@ Layout make_layout(const fm_config& c) {
     off = align256(off + std::max<size_t>(bytes, 1));
     return o;
   };
-  L.cache = take((size_t)c.L * 2 * cache_positions(c) * d * es);  // per block: keys, then values
+  // per DiT block: the keys of every request, then their values
+  L.cache = take((size_t)c.L * 2 * c.max_requests * cache_positions(c) * d * es);
   L.mods = take((size_t)c.max_steps * (6 * c.L + 2) * d * 4);
   L.sched = take(((size_t)2 * c.max_steps * 256 + 3 * (size_t)c.max_steps * d) * 4);
   L.h = take(Mb * d * 4);
@@ -202,15 +207,15 @@ Layout make_layout(const fm_config& c) {
   L.attn_o = take(Mb * d * es);
   L.act_f = take(Mb * F * es);
   L.qkv = take(Mb * d * es);  // queries of the block rows
-  L.att_po = take((size_t)c.max_branches * c.n_heads * ATT_MAX_RANGES * KB * hd * 4);
-  L.att_ml = take((size_t)c.max_branches * c.n_heads * ATT_MAX_RANGES * KB * 2 * 4);
+  L.att_po = take((size_t)max_blocks(c) * c.n_heads * ATT_MAX_RANGES * KB * hd * 4);
+  L.att_ml = take((size_t)max_blocks(c) * c.n_heads * ATT_MAX_RANGES * KB * 2 * 4);
   L.partial = take(partial_bytes(c));
   L.lm_part = take((size_t)LM_GRID * Mb * 8);
   L.lm_lse = take((size_t)LM_GRID * Mb * 8);
-  L.vs_stats = take((size_t)c.max_branches * (KB + 1) * VS_MAX_SLICES * 8);
-  L.vs_lse = take((size_t)c.max_branches * (KB + 1) * 4);
-  L.vs_n = take((size_t)c.max_branches * 4);
-  L.vs_keys = take((size_t)c.max_branches * VS_MAX_SLICES * 16);
+  L.vs_stats = take((size_t)max_blocks(c) * (KB + 1) * VS_MAX_SLICES * 8);
+  L.vs_lse = take((size_t)max_blocks(c) * (KB + 1) * 4);
+  L.vs_n = take((size_t)max_blocks(c) * 4);
+  L.vs_keys = take((size_t)max_blocks(c) * VS_MAX_SLICES * 16);
   L.counters = take((size_t)N_COUNTER_SLOTS * COUNTER_STRIDE * 4);
   if (c.max_steps > 1) {
     L.dsoft = take(Mb * (size_t)c.V * es);
@@ -241,6 +246,10 @@ fm_status check_config(const fm_config* c) {
   if (c->max_branches < 1 || c->max_branches > 4) return fail(FM_EINVAL, "max_branches must be in 1..4");
   if (c->max_new < 0 || c->max_new > 16) return fail(FM_EINVAL, "max_new must be in 0..16");
   if (c->max_steps < 1 || c->max_steps > 4) return fail(FM_EINVAL, "max_steps must be in 1..4");
+  if (c->max_requests < 1 || c->max_requests > FM_MAX_REQ)
+    return fail(FM_EINVAL, "max_requests must be in 1..%d", FM_MAX_REQ);
+  if (c->max_requests > 1 && c->max_branches > 1)
+    return fail(FM_EINVAL, "a handle holds either branches of one request or several requests, not both");
   return FM_OK;
 }
 
@@ -258,17 +267,17 @@ struct fm_handle {
   bool has_weights = false;
   int n_steps = 0;
   float times[8];
-  int ctx_len = 0;
-  int ctx_high = 0;  // rows [0, ctx_high) have been written at least once
+  int ctx_len[FM_MAX_REQ] = {};   // context rows of each request
+  int ctx_high[FM_MAX_REQ] = {};  // rows [0, ctx_high) have been written at least once
   int probe = FM_PROBE_NONE;
   hipEvent_t probe_start = nullptr, probe_stop = nullptr;
 
   template <typename P> P* at(size_t off) { return reinterpret_cast<P*>(ws + off); }
   // key / value cache of DiT block l
-  template <typename T> T* kcache(int l) {
-    return at<T>(lay.cache) + (size_t)l * 2 * cache_positions(cfg) * cfg.d;
-  }
-  template <typename T> T* vcache(int l) { return kcache<T>(l) + (size_t)cache_positions(cfg) * cfg.d; }
+  // key / value cache of DiT block l, request 0 (request r at + r * req_stride())
+  size_t req_stride() const { return (size_t)cache_positions(cfg) * cfg.d; }
+  template <typename T> T* kcache(int l) { return at<T>(lay.cache) + (size_t)l * 2 * cfg.max_requests * req_stride(); }
+  template <typename T> T* vcache(int l) { return kcache<T>(l) + (size_t)cfg.max_requests * req_stride(); }
 };
 
 namespace {
@@ -420,20 +429,22 @@ fm_status embed(fm_handle* h, const void* x, int ldx, int M, float alpha, float 
 }
 
 template <typename T>
-fm_status attention(fm_handle* h, int l, int B, int C, hipStream_t st) {
+fm_status attention(fm_handle* h, int l, int B, const int* C, bool own_ctx, hipStream_t st) {
   const fm_config& c = h->cfg;
   const int hd = c.d / c.n_heads;
-  const int ctx_blocks = cdiv(C, ATT_BLK);
-  AttnPlan p = plan_attention(ctx_blocks + 1);
-  AttnArgs a;
+  int c_max = 0;
+  for (int b = 0; b < B; ++b) c_max = std::max(c_max, C[b]);
+  AttnPlan p = plan_attention(cdiv(c_max, ATT_BLK) + 1);
+  AttnArgs a{};
   a.q = h->at<T>(h->lay.qkv);
   a.ldq = c.d;
   a.kc = h->kcache<T>(l);
   a.vt = h->vcache<T>(l);
+  a.req_stride = h->req_stride();
   a.P = cache_positions(c);
-  a.C = C;
-  a.ctx_blocks = ctx_blocks;
+  for (int b = 0; b < B; ++b) a.C[b] = C[b];
   a.scratch_blk = cdiv(c.C_max, ATT_BLK);
+  a.scratch_step = own_ctx ? 0 : 1;
   a.K = KB;
   a.d = c.d;
   a.nh = c.n_heads;
@@ -452,6 +463,13 @@ fm_status attention(fm_handle* h, int l, int B, int C, hipStream_t st) {
   FM_LAUNCHED("attention_kernel");
   return FM_OK;
 }
+
+// A draft over several requests: row block r is request r, with its own
+// context, to which n_new[r] rows are appended first.
+struct Batch {
+  int R;
+  int n_new[FM_MAX_REQ];
+};
 
 // Temperature > 0 drafting: tokens are sampled from softmax(logits / tau) and
 // the per-row log-normalisers are written to lse.
@@ -581,14 +599,17 @@ void qkv_cache_params(fm_handle* h, int l, EpiParams& e) {
   const fm_config& c = h->cfg;
   e.kcache = h->kcache<T>(l);
   e.vcache = h->vcache<T>(l);
+  e.req_stride = h->req_stride();
   e.P = cache_positions(c);
   e.hd = c.d / c.n_heads;
   e.d = c.d;
   e.scratch_pos0 = cdiv(c.C_max, ATT_BLK) * ATT_BLK;
+  e.scratch_step = ATT_BLK;
+  e.n_req = 1;
 }
 
 template <typename T>
-fm_status context_append_impl(fm_handle* h, const void* feats, int n, hipStream_t st) {
+fm_status context_append_impl(fm_handle* h, int req, const void* feats, int n, hipStream_t st) {
   const fm_config& c = h->cfg;
   const int K5 = c.n_ctx_layers * c.H;
   T* stage = h->at<T>(h->lay.act_qkv);
@@ -601,7 +622,11 @@ fm_status context_append_impl(fm_handle* h, const void* feats, int n, hipStream_
       e.bias = offset_rows<T>(blk(h, l, B_BQKV), c.d);
       e.rows_block = 0;
       qkv_cache_params<T>(h, l, e);
-      e.cache_pos0 = h->ctx_len + r0;
+      e.kcache = h->kcache<T>(l) + (size_t)req * h->req_stride();
+      e.vcache = h->vcache<T>(l) + (size_t)req * h->req_stride();
+      e.ctx_first[0] = 0;
+      e.ctx_first[1] = rows;
+      e.ctx_pos0[0] = h->ctx_len[req] + r0;
       e.col_offset = c.d;
       FM_TRY(gemm<T>(h, EPI_QKV, stage, c.d, rows, offset_rows<T>(blk(h, l, B_WQKV), (size_t)c.d * c.d), 2 * c.d,
                      c.d, e, st));
@@ -612,10 +637,23 @@ fm_status context_append_impl(fm_handle* h, const void* feats, int n, hipStream_
 
 template <typename T>
 fm_status draft_impl(fm_handle* h, const void* noise, int B, const void* new_feats, int n_new, int32_t* tokens,
-                     float* logits, float* hidden, hipStream_t st, const Sampling* smp = nullptr) {
+                     float* logits, float* hidden, hipStream_t st, const Sampling* smp = nullptr,
+                     const Batch* bt = nullptr) {
   const fm_config& c = h->cfg;
   const int d = c.d, F = c.mlp_mult * c.d, Mb = B * KB, L = c.L;
-  const int C = h->ctx_len + n_new;
+  // visible context of each row block, and where the new context rows go
+  int C[FM_MAX_REQ];
+  EpiParams ctx{};
+  ctx.n_req = bt ? bt->R : 1;
+  ctx.ctx_first[0] = 0;
+  for (int b = 0; b < B; ++b) {
+    const int r = bt ? b : 0;
+    C[b] = h->ctx_len[r] + (bt ? bt->n_new[b] : n_new);
+  }
+  for (int r = 0; r < ctx.n_req; ++r) {
+    ctx.ctx_pos0[r] = h->ctx_len[r];
+    ctx.ctx_first[r + 1] = ctx.ctx_first[r] + (bt ? bt->n_new[r] : n_new);
+  }
   const bool fuse_ln = ln_fusable(c, B);
   T* act_qkv = h->at<T>(h->lay.act_qkv);
   T* act_d = h->at<T>(h->lay.act_d);
@@ -650,7 +688,10 @@ fm_status draft_impl(fm_handle* h, const void* noise, int B, const void* new_fea
         e.ld_act = d;
         e.rows_block = Mb;
         qkv_cache_params<T>(h, l, e);
-        e.cache_pos0 = h->ctx_len;
+        e.scratch_step = bt ? 0 : ATT_BLK;
+        e.n_req = ctx.n_req;
+        std::memcpy(e.ctx_first, ctx.ctx_first, sizeof e.ctx_first);
+        std::memcpy(e.ctx_pos0, ctx.ctx_pos0, sizeof e.ctx_pos0);
         e.col_offset = 0;
         if (fuse_ln) {
           FM_TRY(gemm_ln<T>(h, EPI_QKV, hres, mv + 0 * d, mv + 1 * d, act_qkv + (size_t)Mb * d, m_qkv - Mb,
@@ -660,7 +701,7 @@ fm_status draft_impl(fm_handle* h, const void* noise, int B, const void* new_fea
           FM_TRY(gemm<T>(h, EPI_QKV, act_qkv, d, m_qkv, blk(h, l, B_WQKV), 3 * d, d, e, st));
         }
       }
-      FM_TRY(attention<T>(h, l, B, C, st));
+      FM_TRY(attention<T>(h, l, B, C, bt != nullptr, st));
       {
         EpiParams e{};
         e.bias = blk(h, l, B_BO);
@@ -879,36 +920,50 @@ fm_status fm_set_schedule(fm_handle* h, const float* times, int num_steps, void*
   return s;
 }
 
-fm_status fm_context_append(fm_handle* h, const void* feats, int n, void* stream) {
+fm_status fm_context_append_req(fm_handle* h, int req, const void* feats, int n, void* stream) {
   g_err.clear();
   if (!h) return fail(FM_EINVAL, "handle is NULL");
+  if (req < 0 || req >= h->cfg.max_requests)
+    return fail(FM_EINVAL, "request %d outside 0..%d", req, h->cfg.max_requests - 1);
   if (n < 0) return fail(FM_EINVAL, "n must be >= 0");
   if (n == 0) return FM_OK;
   if (!feats) return fail(FM_EINVAL, "feats is NULL");
   if (!aligned16(feats)) return fail(FM_EINVAL, "feats is not 16-byte aligned");
   if (!h->has_weights) return fail(FM_ESTATE, "fm_context_append before fm_set_weights");
-  if (h->ctx_len + n > h->cfg.C_max)
-    return fail(FM_ECAPACITY, "context of %d rows + %d exceeds C_max %d", h->ctx_len, n, h->cfg.C_max);
+  if (h->ctx_len[req] + n > h->cfg.C_max)
+    return fail(FM_ECAPACITY, "context of %d rows + %d exceeds C_max %d", h->ctx_len[req], n, h->cfg.C_max);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  fm_status s = h->cfg.dtype == FM_BF16 ? context_append_impl<bf16_t>(h, feats, n, st)
-                                        : context_append_impl<float>(h, feats, n, st);
+  fm_status s = h->cfg.dtype == FM_BF16 ? context_append_impl<bf16_t>(h, req, feats, n, st)
+                                        : context_append_impl<float>(h, req, feats, n, st);
   if (s == FM_OK) {
-    h->ctx_len += n;
-    h->ctx_high = std::max(h->ctx_high, h->ctx_len);
+    h->ctx_len[req] += n;
+    h->ctx_high[req] = std::max(h->ctx_high[req], h->ctx_len[req]);
   }
   return s;
 }
 
-fm_status fm_context_truncate(fm_handle* h, int new_len) {
+fm_status fm_context_append(fm_handle* h, const void* feats, int n, void* stream) {
+  return fm_context_append_req(h, 0, feats, n, stream);
+}
+
+fm_status fm_context_truncate_req(fm_handle* h, int req, int new_len) {
   g_err.clear();
   if (!h) return fail(FM_EINVAL, "handle is NULL");
-  if (new_len < 0 || new_len > h->ctx_high)
-    return fail(FM_EINVAL, "new length %d outside 0..%d (rows written so far)", new_len, h->ctx_high);
-  h->ctx_len = new_len;
+  if (req < 0 || req >= h->cfg.max_requests)
+    return fail(FM_EINVAL, "request %d outside 0..%d", req, h->cfg.max_requests - 1);
+  if (new_len < 0 || new_len > h->ctx_high[req])
+    return fail(FM_EINVAL, "new length %d outside 0..%d (rows written so far)", new_len, h->ctx_high[req]);
+  h->ctx_len[req] = new_len;
   return FM_OK;
 }
 
-int fm_context_length(const fm_handle* h) { return h ? h->ctx_len : -1; }
+fm_status fm_context_truncate(fm_handle* h, int new_len) { return fm_context_truncate_req(h, 0, new_len); }
+
+int fm_context_length_req(const fm_handle* h, int req) {
+  return h && req >= 0 && req < h->cfg.max_requests ? h->ctx_len[req] : -1;
+}
+
+int fm_context_length(const fm_handle* h) { return fm_context_length_req(h, 0); }
 
 static fm_status draft_checked(fm_handle* h, const void* noise, int B, const void* new_feats, int n_new,
                                int32_t* tokens, float* logits, float* hidden, void* stream, const Sampling* smp) {
@@ -922,17 +977,55 @@ static fm_status draft_checked(fm_handle* h, const void* noise, int B, const voi
   if (n_new > c.max_new) return fail(FM_ECAPACITY, "n_new %d exceeds max_new %d", n_new, c.max_new);
   if (n_new > 0 && !new_feats) return fail(FM_EINVAL, "new_feats is NULL with n_new > 0");
   if (n_new > 0 && !aligned16(new_feats)) return fail(FM_EINVAL, "new_feats is not 16-byte aligned");
-  if (h->ctx_len + n_new > c.C_max)
-    return fail(FM_ECAPACITY, "context of %d rows + %d exceeds C_max %d", h->ctx_len, n_new, c.C_max);
+  if (h->ctx_len[0] + n_new > c.C_max)
+    return fail(FM_ECAPACITY, "context of %d rows + %d exceeds C_max %d", h->ctx_len[0], n_new, c.C_max);
   if (!h->has_weights) return fail(FM_ESTATE, "fm_draft before fm_set_weights");
   if (h->n_steps < 1) return fail(FM_ESTATE, "fm_draft before fm_set_schedule");
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   fm_status s = c.dtype == FM_BF16 ? draft_impl<bf16_t>(h, noise, B, new_feats, n_new, tokens, logits, hidden, st, smp)
                                    : draft_impl<float>(h, noise, B, new_feats, n_new, tokens, logits, hidden, st, smp);
   if (s == FM_OK) {
-    h->ctx_len += n_new;
-    h->ctx_high = std::max(h->ctx_high, h->ctx_len);
+    h->ctx_len[0] += n_new;
+    h->ctx_high[0] = std::max(h->ctx_high[0], h->ctx_len[0]);
   }
+  return s;
+}
+
+fm_status fm_draft_batch(fm_handle* h, const void* noise, int R, const void* new_feats, const int* n_new,
+                         int32_t* tokens, float* logits, void* stream) {
+  g_err.clear();
+  if (!h) return fail(FM_EINVAL, "handle is NULL");
+  const fm_config& c = h->cfg;
+  if (!noise || !tokens) return fail(FM_EINVAL, "noise and tokens must not be NULL");
+  if (!aligned16(noise)) return fail(FM_EINVAL, "noise is not 16-byte aligned");
+  if (R < 1) return fail(FM_EINVAL, "R must be >= 1");
+  if (R > c.max_requests) return fail(FM_ECAPACITY, "R %d exceeds max_requests %d", R, c.max_requests);
+  Batch bt{};
+  bt.R = R;
+  int total = 0;
+  for (int r = 0; r < R; ++r) {
+    const int n = n_new ? n_new[r] : 0;
+    if (n < 0) return fail(FM_EINVAL, "n_new[%d] must be >= 0", r);
+    if (h->ctx_len[r] + n > c.C_max)
+      return fail(FM_ECAPACITY, "request %d: context of %d rows + %d exceeds C_max %d", r, h->ctx_len[r], n,
+                  c.C_max);
+    bt.n_new[r] = n;
+    total += n;
+  }
+  if (total > c.max_new) return fail(FM_ECAPACITY, "%d new context rows exceed max_new %d", total, c.max_new);
+  if (total > 0 && !new_feats) return fail(FM_EINVAL, "new_feats is NULL with new rows");
+  if (total > 0 && !aligned16(new_feats)) return fail(FM_EINVAL, "new_feats is not 16-byte aligned");
+  if (!h->has_weights) return fail(FM_ESTATE, "fm_draft_batch before fm_set_weights");
+  if (h->n_steps < 1) return fail(FM_ESTATE, "fm_draft_batch before fm_set_schedule");
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  fm_status s = c.dtype == FM_BF16
+                    ? draft_impl<bf16_t>(h, noise, R, new_feats, total, tokens, logits, nullptr, st, nullptr, &bt)
+                    : draft_impl<float>(h, noise, R, new_feats, total, tokens, logits, nullptr, st, nullptr, &bt);
+  if (s == FM_OK)
+    for (int r = 0; r < R; ++r) {
+      h->ctx_len[r] += bt.n_new[r];
+      h->ctx_high[r] = std::max(h->ctx_high[r], h->ctx_len[r]);
+    }
   return s;
 }
 

@@ -37,11 +37,16 @@ struct EpiParams {
   const float* gate;    // EPI_RESID, [N]
   // EPI_QKV (cache layout: attention.hpp)
   int rows_block;       // rows < rows_block are block rows (branch m / 16), the rest context rows
-  void* kcache;         // this DiT block's key cache   [nh][P][hd]
-  void* vcache;         // this DiT block's value cache [nh][P/32][hd][32]
+  void* kcache;         // this DiT block's key cache   [nh][P][hd] of request 0
+  void* vcache;         // this DiT block's value cache [nh][P/32][hd][32] of request 0
+  size_t req_stride;    // elements from one request's key (value) cache to the next one's
   int P, hd, d;         // positions per head, head width, model width
-  int cache_pos0;       // position of context row rows_block
-  int scratch_pos0;     // position of branch 0's first block row (branch b at +32b)
+  int scratch_pos0;     // position of the first block row
+  int scratch_step;     // 32: branches share request 0's cache, branch b's rows at +32b;
+                        // 0: branch b is request b, its rows in its own cache
+  int n_req;            // context row c belongs to request r with ctx_first[r] <= c <
+  int ctx_first[FM_MAX_REQ + 1];  // ctx_first[r + 1], at position ctx_pos0[r] + c - ctx_first[r]
+  int ctx_pos0[FM_MAX_REQ];
   int col_offset;       // logical qkv column of n = 0 (d for a K/V-only call)
 };
 
@@ -72,24 +77,30 @@ __device__ __forceinline__ void epilogue(const EpiParams& e, int m, int n, float
     *p = *p + e.gate[n] * v;
   } else {  // EPI_QKV
     const int nn = n + e.col_offset;
-    int pos;
+    int pos, req;
     if (m < e.rows_block) {
       if (nn < e.d) {
         reinterpret_cast<T*>(e.out_act)[(size_t)m * e.ld_act + nn] = from_f32<T>(v);
         return;
       }
-      pos = e.scratch_pos0 + 32 * (m >> 4) + (m & 15);
+      pos = e.scratch_pos0 + e.scratch_step * (m >> 4) + (m & 15);
+      req = e.scratch_step ? 0 : (m >> 4);
     } else {
       if (nn < e.d) return;  // queries of context rows are not needed
-      pos = e.cache_pos0 + (m - e.rows_block);
+      const int c = m - e.rows_block;
+      req = 0;
+#pragma unroll
+      for (int r = 1; r < FM_MAX_REQ; ++r) req += (r < e.n_req && c >= e.ctx_first[r]) ? 1 : 0;
+      pos = e.ctx_pos0[req] + c - e.ctx_first[req];
     }
     const int which = nn >= 2 * e.d;  // 0: key, 1: value
     const int col = nn - (1 + which) * e.d;
     const int head = col / e.hd, c = col - head * e.hd;
+    const size_t rb = (size_t)req * e.req_stride;
     if (!which)
-      reinterpret_cast<T*>(e.kcache)[((size_t)head * e.P + pos) * e.hd + c] = from_f32<T>(v);
+      reinterpret_cast<T*>(e.kcache)[rb + ((size_t)head * e.P + pos) * e.hd + c] = from_f32<T>(v);
     else
-      reinterpret_cast<T*>(e.vcache)[(((size_t)head * (e.P >> 5) + (pos >> 5)) * e.hd + c) * 32 +
+      reinterpret_cast<T*>(e.vcache)[rb + (((size_t)head * (e.P >> 5) + (pos >> 5)) * e.hd + c) * 32 +
                                      vt_slot<T>(pos & 31)] = from_f32<T>(v);
   }
 }

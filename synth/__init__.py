@@ -11,7 +11,8 @@ scaled, then rounded to nearest-even bfloat16 for bf16 workloads):
 
 * weights: tensor ``i`` of the canonical order (``weight_names``) is drawn in
   chunks of ``CHUNK`` elements, chunk ``c`` from seed ``[0, i, c]``, std 0.02;
-* context features ``[C][5][H]``: seed ``[1, c]`` per chunk, std 1;
+* context features ``[C][5][H]``: seed ``[1, c]`` per chunk, std 1 (request r > 0
+  of a batch of requests: seed ``[4, r, c]``);
 * noise block of branch ``b`` ``[K][V]``: seed ``[2, b, c]``, std 1;
 * target logits of branch ``b`` ``[K+1][V]``: seed ``[3, b, c]``, std 1.
 
@@ -53,6 +54,8 @@ class Config:
     mlp_mult: int = 4
     c_max: int = 0  # context capacity (0: c_prefill + n_new)
     temperature: float = 0.0    # 0: greedy drafting and verification; > 0: sampled
+    requests: int = 1           # independent requests drafted together, each with its own
+                                # context of c_prefill + n_new rows
 
     @property
     def hd(self) -> int:
@@ -100,6 +103,9 @@ CONFIGS = {
     "qwen3_8b_tree4": _qwen8b(name="qwen3_8b_tree4", c_prefill=4088, B=4),
     # as qwen3_8b, sampled at temperature 1 (probabilistic drafting + verify)
     "qwen3_8b_t1": _qwen8b(name="qwen3_8b_t1", temperature=1.0),
+    # four concurrent requests, each with its own context of 512 rows (508 cached
+    # + 4 appended per step), drafted together
+    "qwen3_8b_batch4": _qwen8b(name="qwen3_8b_batch4", c_prefill=508, n_new=4, requests=4),
 }
 
 # seeds of the random streams of sampled steps (one per replayed step)
@@ -217,11 +223,12 @@ def make_weights(cfg: Config, variant: str = "random") -> dict:
 # activations: context features, noise, target logits
 # --------------------------------------------------------------------------
 
-def make_features(cfg: Config, rows: int | None = None) -> np.ndarray:
-    """Target hidden states [rows][5][H] of layers 1, 9, 17, 25, 33, N(0,1)."""
+def make_features(cfg: Config, rows: int | None = None, request: int = 0) -> np.ndarray:
+    """Target hidden states [rows][5][H] of layers 1, 9, 17, 25, 33, N(0,1);
+    request 0 from seed [1], request r > 0 (its own context) from seed [4, r]."""
     rows = cfg.C if rows is None else rows
     with ThreadPoolExecutor(_workers()) as pool:
-        return _draw([1], (rows, N_CTX_LAYERS, cfg.H), 1.0, cfg.dtype, pool)
+        return _draw([1] if request == 0 else [4, request], (rows, N_CTX_LAYERS, cfg.H), 1.0, cfg.dtype, pool)
 
 
 def make_noise(cfg: Config, B: int | None = None) -> np.ndarray:

@@ -1,0 +1,123 @@
+"""GPU parity of fm_draft_batch: R independent requests, each with its own
+context, drafted together as R*16 rows.  Every request's draft must match the
+oracle's draft of that request alone (logits within 2e-2 norm-wise, tokens
+exact except reported near-ties); a request's result must not depend on the
+other requests' data (bitwise); greedy verification of the batch is per
+request."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+fm = pytest.importorskip("step_flow_map_amd")
+from gpu_util import LOGIT_RTOL, binding_weights, check_tokens, rowwise_rel_err, to_dev  # noqa: E402
+
+TINY = synth.CONFIGS["tiny"]
+MID_BF16 = TINY.with_(name="mid_bf16", dtype="bf16", V=2000, d=384, nh=3, H=520, c_prefill=300)
+
+
+def _handle(cfg, w, R, C_max, max_new=16):
+    c = fm.make_config(K=cfg.K, V=cfg.V, d=cfg.d, L=cfg.L, n_heads=cfg.nh, H=cfg.H, C_max=C_max,
+                       dtype=cfg.dtype, max_new=max_new, max_steps=max(cfg.num_steps, 1), max_requests=R)
+    return fm.Drafter(c, binding_weights(w))
+
+
+def _run(cfg, w, prefill, new, noise, feats, seed_dr=None):
+    """prefill[r] rows appended per request, then new[r] rows inside the batch
+    draft.  Returns tokens [R][K] and logits [R][K][V] (numpy)."""
+    R = len(prefill)
+    dr = _handle(cfg, w, R, C_max=max(p + n for p, n in zip(prefill, new)) + 8)
+    dr.set_schedule(cfg.times)
+    for r in range(R):
+        if prefill[r]:
+            dr.append_req(r, to_dev(feats[r][:prefill[r]]))
+    rows = [feats[r][prefill[r]:prefill[r] + new[r]] for r in range(R)]
+    cat = np.concatenate(rows) if sum(new) else None
+    logits = torch.empty(R, cfg.K, cfg.V, dtype=torch.float32, device="cuda")
+    tok = dr.draft_batch(to_dev(noise), new_feats=None if cat is None else to_dev(cat), n_new=new, logits=logits)
+    torch.cuda.synchronize()
+    for r in range(R):
+        assert dr.context_length_req(r) == prefill[r] + new[r]
+    return tok.cpu().numpy(), logits.cpu().numpy(), dr
+
+
+@pytest.mark.parametrize("cfg", [TINY, MID_BF16], ids=["tiny_f32", "mid_bf16"])
+@pytest.mark.parametrize("variant", ["random", "unit_gate"])
+def test_batch_matches_oracle_per_request(cfg, variant):
+    """Three requests with different context lengths (one empty) and
+    different numbers of appended rows (one none)."""
+    print(f"[batch parity] {cfg.name} {variant}", flush=True)
+    R = 3
+    prefill = [cfg.c_prefill, 5, 0]
+    new = [4, 0, 7]
+    w = synth.make_weights(cfg, variant)
+    feats = [synth.make_features(cfg, rows=prefill[r] + new[r], request=r) for r in range(R)]
+    noise = synth.make_noise(cfg, R)
+    tok, logits, dr = _run(cfg, w, prefill, new, noise, feats)
+    W = oracle.Weights.from_storage(w)
+    ties = []
+    for r in range(R):
+        ref = oracle.draft(W, cfg, noise[r], feats[r])
+        rel = rowwise_rel_err(logits[r], ref["logits"])
+        assert rel.max() <= LOGIT_RTOL, (r, rel.max())
+        ties += check_tokens(tok[r], logits[r], ref["logits"], ref["tokens"])
+    print(f"  near-ties {ties}")
+
+
+def test_requests_do_not_see_each_other():
+    """Request 0's draft is bitwise the same whatever request 1 holds."""
+    cfg = MID_BF16
+    w = synth.make_weights(cfg)
+    noise = synth.make_noise(cfg, 2)
+    f0 = synth.make_features(cfg, rows=40, request=0)
+    a = _run(cfg, w, [36, 20], [4, 3], noise, [f0, synth.make_features(cfg, rows=23, request=1)])
+    b = _run(cfg, w, [36, 60], [4, 1], noise, [f0, synth.make_features(cfg, rows=61, request=2)])
+    assert np.array_equal(a[0][0], b[0][0])
+    assert np.array_equal(a[1][0], b[1][0])
+    assert not np.array_equal(a[1][1], b[1][1])
+
+
+def test_batch_contexts_advance_and_truncate_per_request():
+    cfg = TINY
+    w = synth.make_weights(cfg)
+    noise = synth.make_noise(cfg, 2)
+    feats = [synth.make_features(cfg, rows=30, request=r) for r in range(2)]
+    tok1, lg1, dr = _run(cfg, w, [20, 10], [4, 8], noise, feats)
+    # roll request 0 back and draft again with the same rows: same result
+    dr.truncate_req(0, 20)
+    dr.truncate_req(1, 10)
+    cat = np.concatenate([feats[0][20:24], feats[1][10:18]])
+    lg2 = torch.empty(2, cfg.K, cfg.V, dtype=torch.float32, device="cuda")
+    tok2 = dr.draft_batch(to_dev(noise), new_feats=to_dev(cat), n_new=[4, 8], logits=lg2)
+    torch.cuda.synchronize()
+    assert np.array_equal(tok2.cpu().numpy(), tok1)
+    assert np.array_equal(lg2.cpu().numpy(), lg1)
+    with pytest.raises(fm.FlashMapError):
+        dr.truncate_req(2, 0)                       # no request 2
+    with pytest.raises(fm.FlashMapError) as e:
+        dr.draft_batch(to_dev(synth.make_noise(cfg, 3)))   # R > max_requests
+    assert e.value.status == fm.FM_ECAPACITY
+    assert dr.context_length_req(0) == 24 and dr.context_length_req(1) == 18
+
+
+def test_batch_verify_is_per_request():
+    cfg = TINY
+    w = synth.make_weights(cfg)
+    R = 3
+    noise = synth.make_noise(cfg, R)
+    feats = [synth.make_features(cfg, rows=12, request=r) for r in range(R)]
+    tok, logits, dr = _run(cfg, w, [8, 8, 8], [4, 4, 4], noise, feats)
+    T = synth.make_target_logits(cfg, R)
+    planted = [3, 16, 0]
+    for r in range(R):
+        T[r] = synth.plant(T[r], tok[r], planted[r])
+    e, a, _ = fm.verify(to_dev(T), torch.from_numpy(tok.astype(np.int32)).cuda())
+    torch.cuda.synchronize()
+    assert a.cpu().numpy().tolist() == planted
+    for r in range(R):
+        n, em = oracle.verify(T[r], tok[r])
+        assert e.cpu().numpy()[r, :n + 1].tolist() == em
