@@ -25,6 +25,9 @@ MID_BF16 = TINY.with_(name="mid_bf16", dtype="bf16", V=2000, d=384, nh=3, H=520,
 # the k-split LM head and one for the rest, the LayerNorm left unfused, and a
 # four-branch tree whose z no longer fits in registers (whole-tile LM head)
 WIDE_F32 = TINY.with_(name="wide_f32", V=1000, d=1152, nh=9)
+# bf16 at the drafter's real width (d 2048, 16 heads, MLP 8192) with a small
+# vocabulary and two blocks: the persistent block tail (W_o, LN + W_1, W_2)
+W2048_BF16 = TINY.with_(name="w2048_bf16", dtype="bf16", V=2000, d=2048, nh=16, H=520, c_prefill=40)
 
 
 def _case(cfg, variant="random", B=1, seed_noise=None):
@@ -34,8 +37,8 @@ def _case(cfg, variant="random", B=1, seed_noise=None):
     return w, feats, noise
 
 
-@pytest.mark.parametrize("cfg", [TINY, SMALL_BF16, MID_BF16, WIDE_F32],
-                         ids=["tiny_f32", "small_bf16", "mid_bf16", "wide_f32"])
+@pytest.mark.parametrize("cfg", [TINY, SMALL_BF16, MID_BF16, WIDE_F32, W2048_BF16],
+                         ids=["tiny_f32", "small_bf16", "mid_bf16", "wide_f32", "w2048_bf16"])
 @pytest.mark.parametrize("variant", ["random", "unit_gate", "gate_zero"])
 def test_draft_matches_oracle(cfg, variant):
     print(f"[draft parity] {cfg.name} {variant}", flush=True)
@@ -83,8 +86,8 @@ def test_empty_context_and_no_new_rows():
     check_draft(cfg, w, noise, feats, 0, tok, logits)
 
 
-def test_bitwise_deterministic():
-    cfg = SMALL_BF16
+@pytest.mark.parametrize("cfg", [SMALL_BF16, W2048_BF16], ids=["small_bf16", "w2048_bf16"])
+def test_bitwise_deterministic(cfg):
     w, feats, noise = _case(cfg)
     dr = make_drafter(cfg, w)
     dr.set_schedule(cfg.times)
@@ -119,7 +122,8 @@ def test_errors_enqueue_nothing():
     assert e.value.status == fm.FM_ECAPACITY
 
 
-@pytest.mark.parametrize("cfg", [TINY, SMALL_BF16, MID_BF16], ids=["tiny_f32", "small_bf16", "mid_bf16"])
+@pytest.mark.parametrize("cfg", [TINY, SMALL_BF16, MID_BF16, W2048_BF16],
+                         ids=["tiny_f32", "small_bf16", "mid_bf16", "w2048_bf16"])
 def test_two_step_schedule(cfg):
     cfg = cfg.with_(times=(0.0, 0.5, 1.0))
     w, feats, noise = _case(cfg)
