@@ -110,6 +110,18 @@ GemmPlan plan_gemm(int N, int K, fm_dtype t) {
     p.grid = p.n_groups * p.S;
     return p;
   }
+  if (p.n_groups < 256 && nch > 4 * GEMM_MAX_SPLIT && p.n_groups % 2 == 0) {
+    // narrow layer, very long k (the context fusion, k = 5H): two tiles per
+    // workgroup of 8 waves share each activation chunk, k split so that the
+    // launch has about 256 workgroups, waves loop over their chunks
+    p.tg = 2;
+    p.waves = 8;
+    p.S = std::min(GEMM_MAX_SPLIT, std::max(1, 256 / (p.n_groups / 2)));
+    p.k_split = cdiv(nch, p.S) * chunk;
+    p.S = cdiv(K, p.k_split);
+    p.grid = (p.n_groups / 2) * p.S;
+    return p;
+  }
   p.waves = p.n_groups < 256 ? 8 : 4;
   int S = 1;
   if (p.n_groups < 256 && nch > 4 * p.waves) S = std::min(GEMM_MAX_SPLIT, cdiv(256, p.n_groups));
