@@ -164,10 +164,9 @@ AttnPlan plan_attention(int n_blocks) {
   return p;
 }
 
-// cache positions per head: the context capacity rounded up to whole 32-key
-// blocks, then one scratch block per branch for the branch's block rows
-// positions per head of one request's cache: its context, then one 32-position
-// block per branch for the block rows
+// positions per head of one request's cache: the context capacity rounded up to
+// whole 32-key blocks, then one 32-position scratch block per branch for that
+// branch's block rows
 int cache_positions(const fm_config& c) { return cdiv(c.C_max, ATT_BLK) * ATT_BLK + ATT_BLK * c.max_branches; }
 // row blocks of one draft: branches of one request, or requests of one batch
 int max_blocks(const fm_config& c) { return std::max(c.max_branches, c.max_requests); }
