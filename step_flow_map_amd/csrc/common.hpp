@@ -66,6 +66,22 @@ template <> __device__ __forceinline__ float4 pack_vec<float>(const float (&y)[4
   return make_float4(y[0], y[1], y[2], y[3]);
 }
 
+// the VE values of a vec as floats
+__device__ __forceinline__ void unpack_vec(uint4 v, float (&y)[8]) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    y[2 * i] = __uint_as_float(w[i] << 16);
+    y[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+__device__ __forceinline__ void unpack_vec(float4 v, float (&y)[4]) {
+  y[0] = v.x;
+  y[1] = v.y;
+  y[2] = v.z;
+  y[3] = v.w;
+}
+
 // v if keep, else zero, without a branch or a select on the vector
 __device__ __forceinline__ uint4 vkeep(uint4 v, bool keep) {
   const uint32_t m = keep ? ~0u : 0u;

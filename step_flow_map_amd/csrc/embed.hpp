@@ -1,7 +1,8 @@
 // Noise-block embedding contraction of the flow-map jump:
 //
 //   e[m][c] = alpha * e[m][c] + beta * sum_v x[m][v] * E[v][c]
-//   h[m][c] = e[m][c] + P[m % K][c]
+//   h[m][c] = e[m][c] + P[m % K][c]        (float32, and optionally a copy in
+//                                         the storage type)
 //
 // x is the block state over the vocabulary ([M][V]: Gaussian noise at s = 0,
 // the denoiser's softmax before a later jump), E the frozen embedding [V][d]
@@ -39,6 +40,7 @@ struct EmbedArgs {
   uint32_t* counters; // n_cb*S2 first-level counters, then n_cb second-level
   float* e_state;     // [M][d] in/out
   float* h;           // [M][d] out
+  void* hb;           // [M][d] out in the storage type, or null
   float alpha, beta;  // alpha == 0: e_state is not read
   int K;              // positions per branch (rows m use position m % K)
   int use_pos;
@@ -98,20 +100,29 @@ __global__ __launch_bounds__(NW * 64) void embed_kernel(EmbedArgs g) {
   // multiples of VE, so a lane's rows are all in range or all out.  Loads use
   // clamped addresses; the range check is applied to x at use (an out-of-range
   // chunk contributes x = 0), so no loaded value is selected before the MFMA.
+  // x comes with the E rows of its chunk, one chunk ahead; from 64 rows on it
+  // is loaded at use instead (x is an L2 hit: every column block reads it),
+  // which keeps the accumulators and both E buffers in registers without spills.
+  constexpr bool X_AHEAD = MT < 4;
   auto load = [&](VT (&in)[VE], VT (&a)[MT], int v0) {
     const int vr = v0 + grp * VE;
     const int vs = vr < v_end ? vr : 0;
 #pragma unroll
     for (int r = 0; r < VE; ++r) in[r] = as_vec<T>(ldg_stream(ecol + (size_t)(vs + r) * g.d));
+    if constexpr (X_AHEAD) {
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) a[mt] = vload<T>(xrow[mt] + vs);
+      for (int mt = 0; mt < MT; ++mt) a[mt] = vload<T>(xrow[mt] + vs);
+    }
   };
   auto compute = [&](const VT (&in)[VE], const VT (&a)[MT], int v0) {
     const bool ok = v0 + grp * VE < v_end;
     VT bt[VE], am[MT];
     transpose_block(in, bt);
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) am[mt] = vkeep(a[mt], ok && xok[mt]);
+    for (int mt = 0; mt < MT; ++mt) {
+      const VT xv = X_AHEAD ? a[mt] : vload<T>(xrow[mt] + (ok ? v0 + grp * VE : 0));
+      am[mt] = vkeep(xv, ok && xok[mt]);
+    }
 #pragma unroll
     for (int t = 0; t < VE; ++t)
 #pragma unroll
@@ -191,7 +202,9 @@ __global__ __launch_bounds__(NW * 64) void embed_kernel(EmbedArgs g) {
     float e = g.beta * v;
     if (g.alpha != 0.f) e += g.alpha * g.e_state[o];
     g.e_state[o] = e;
-    g.h[o] = e + (g.use_pos ? pos_table(m % g.K, c, g.d) : 0.f);
+    const float hv = e + (g.use_pos ? pos_table(m % g.K, c, g.d) : 0.f);
+    g.h[o] = hv;
+    if (g.hb) reinterpret_cast<T*>(g.hb)[o] = from_f32<T>(hv);
   }
   (void)S;
 }

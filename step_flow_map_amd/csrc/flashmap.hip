@@ -85,19 +85,36 @@ struct GemmPlan {
 // cross-workgroup reduction at all; a split is used only when the tiles alone
 // cannot cover the CUs and the k range is long (a device-scope arrival costs a
 // memory round trip).  Workgroups of 8 waves when tiles are few, else 4.
-GemmPlan plan_gemm(int N, int K, fm_dtype t) {
+//
+// A workgroup's bytes are its weight share plus the A rows of its k range, so
+// with many rows (M > 32) A dominates: tiles are grouped two to a workgroup
+// to share it, except at 80 rows, where the two tiles' A and weight fragments
+// would not fit in registers.  Measured at 64 rows, a finer k split at the
+// same grouping moves the same bytes per CU and only adds arrivals.
+GemmPlan plan_gemm(int M, int N, int K, fm_dtype t) {
   const int chunk = gemm_chunk(t);
+  const int MT = cdiv(M, 16);
   GemmPlan p;
   p.n_groups = cdiv(N, 16);
   const int nch = std::max(1, cdiv(K, chunk));
   p.tg = 0;
   if (p.n_groups >= 256 && nch <= 8) {
-    // wide layer, short k: two tiles per workgroup of 8 waves, one chunk per wave
-    p.tg = 2;
+    // wide layer, short k: tiles per workgroup of 8 waves, one chunk per wave
+    p.tg = MT >= 5 ? 1 : 2;
     p.waves = 8;
     p.S = 1;
     p.k_split = nch * chunk;
     p.grid = cdiv(p.n_groups, p.tg);
+    return p;
+  }
+  if (p.n_groups < 256 && nch >= 16 && nch <= 4 * GEMM_MAX_SPLIT && MT >= 3) {
+    // narrow layer, long k, many rows: two tiles and eight chunks (one a wave)
+    // per workgroup of 8 waves, k split at most four ways
+    p.tg = 2;
+    p.waves = 8;
+    p.k_split = 8 * chunk;
+    p.S = cdiv(K, p.k_split);
+    p.grid = cdiv(p.n_groups, 2) * p.S;
     return p;
   }
   if (p.n_groups < 256 && nch >= 16 && nch <= 4 * GEMM_MAX_SPLIT) {
@@ -172,7 +189,7 @@ int cache_positions(const fm_config& c) { return cdiv(c.C_max, ATT_BLK) * ATT_BL
 int max_blocks(const fm_config& c) { return std::max(c.max_branches, c.max_requests); }
 
 struct Layout {
-  size_t cache, mods, sched, h, e_state, u_pre, act_qkv, act_d, attn_o, act_f, qkv;
+  size_t cache, mods, sched, h, hb, e_state, u_pre, act_qkv, act_d, attn_o, act_f, qkv;
   size_t att_po, att_ml, partial, lm_part, lm_lse, counters, dsoft, logits_tmp, sm_part, vs_stats, vs_lse, vs_n,
       vs_keys, total;
 };
@@ -185,10 +202,13 @@ size_t partial_bytes(const fm_config& c) {
   const S3 shapes[] = {{Mb + c.max_new, 3 * d, d}, {Mb, d, d}, {Mb, F, d}, {Mb, d, F},
                        {MAX_PREFILL_ROWS, d, c.n_ctx_layers * c.H}, {MAX_PREFILL_ROWS, 2 * d, d}};
   size_t mx = 0;
-  for (const S3& s : shapes) {
-    GemmPlan p = plan_gemm(s.N, s.K, c.dtype);
-    if (p.S > 1) mx = std::max(mx, (size_t)p.S * s.M * s.N * 4);
-  }
+  // the plan depends on the 16-row tiles of M: the largest M of each count
+  for (const S3& s : shapes)
+    for (int M = std::min(16, s.M);; M = std::min(s.M, M + 16)) {
+      GemmPlan p = plan_gemm(M, s.N, s.K, c.dtype);
+      if (p.S > 1) mx = std::max(mx, (size_t)p.S * M * s.N * 4);
+      if (M == s.M) break;
+    }
   for (int M = 16; M <= Mb; M += 16) {
     EmbedPlan e = plan_embed(c.d, c.dtype, M);
     mx = std::max(mx, (size_t)(e.S + e.S2) * M * d * 4);
@@ -211,6 +231,7 @@ Layout make_layout(const fm_config& c) {
   L.mods = take((size_t)c.max_steps * (6 * c.L + 2) * d * 4);
   L.sched = take(((size_t)2 * c.max_steps * 256 + 3 * (size_t)c.max_steps * d) * 4);
   L.h = take(Mb * d * 4);
+  L.hb = take(Mb * d * es);  // h in the storage type, for the fused LayerNorms
   L.e_state = take(Mb * d * 4);
   L.u_pre = take((size_t)std::max(MAX_PREFILL_ROWS, c.max_new) * d * 4);
   L.act_qkv = take((Mb + std::max(MAX_PREFILL_ROWS, c.max_new)) * d * es);
@@ -298,6 +319,8 @@ template <typename T, int MT, int EPI>
 void launch_gemm_mt(const GemmArgs& a, const EpiParams& e, int grid, int waves, int tg, hipStream_t st) {
   if (tg == 2)
     hipLaunchKernelGGL((gemm_tg_kernel<T, MT, 8, 2, EPI, false>), dim3(grid), dim3(8 * 64), 0, st, a, e, LnArgs{});
+  else if (tg == 1 && waves == 8)
+    hipLaunchKernelGGL((gemm_tg_kernel<T, MT, 8, 1, EPI, false>), dim3(grid), dim3(8 * 64), 0, st, a, e, LnArgs{});
   else if (tg == 1)
     hipLaunchKernelGGL((gemm_tg_kernel<T, MT, 4, 1, EPI, false>), dim3(grid), dim3(4 * 64), 0, st, a, e, LnArgs{});
   else if (waves == 8)
@@ -325,7 +348,7 @@ template <typename T>
 fm_status gemm(fm_handle* h, int epi, const void* A, int lda, int M, const void* W, int N, int K,
                const EpiParams& e, hipStream_t st) {
   if (M <= 0) return FM_OK;
-  GemmPlan p = plan_gemm(N, K, h->cfg.dtype);
+  GemmPlan p = plan_gemm(M, N, K, h->cfg.dtype);
   if (p.S > 1 && p.n_groups > N_COUNTER_SLOTS) return fail(FM_EINVAL, "too many column tiles for split-K");
   GemmArgs a;
   a.A = A;
@@ -353,7 +376,7 @@ fm_status gemm(fm_handle* h, int epi, const void* A, int lda, int M, const void*
 bool ln_fusable(const fm_config& c, int B) { return B == 1 && cdiv(c.d, gemm_chunk(c.dtype)) <= 8; }
 
 template <typename T>
-fm_status gemm_ln(fm_handle* h, int epi, const float* x, const float* shift, const float* scale, const void* A_ctx,
+fm_status gemm_ln(fm_handle* h, int epi, const T* x, const float* shift, const float* scale, const void* A_ctx,
                   int M_ctx, const void* W, int N, int K, const EpiParams& e, hipStream_t st) {
   if (cdiv(K, gemm_chunk(h->cfg.dtype)) > 8) return fail(FM_EINVAL, "fused LayerNorm needs k <= 8 chunks");
   GemmArgs a;
@@ -405,7 +428,7 @@ fm_status ln_mod(fm_handle* h, const float* x, int rows, const float* shift, con
 }
 
 template <typename T>
-fm_status embed(fm_handle* h, const void* x, int ldx, int M, float alpha, float beta, hipStream_t st) {
+fm_status embed(fm_handle* h, const void* x, int ldx, int M, float alpha, float beta, T* hb, hipStream_t st) {
   const fm_config& c = h->cfg;
   if (M > 64) return fail(FM_EINVAL, "embedding contraction with %d rows exceeds 64", M);
   EmbedPlan p = plan_embed(c.d, c.dtype, M);
@@ -424,6 +447,7 @@ fm_status embed(fm_handle* h, const void* x, int ldx, int M, float alpha, float 
   a.counters = h->at<uint32_t>(h->lay.counters);
   a.e_state = h->at<float>(h->lay.e_state);
   a.h = h->at<float>(h->lay.h);
+  a.hb = hb;
   a.alpha = alpha;
   a.beta = beta;
   a.K = KB;
@@ -672,6 +696,9 @@ fm_status draft_impl(fm_handle* h, const void* noise, int B, const void* new_fea
   T* attn_o = h->at<T>(h->lay.attn_o);
   T* qkv = h->at<T>(h->lay.qkv);
   float* hres = h->at<float>(h->lay.h);
+  // the fused LayerNorms read h in the storage type: its producers (embedding,
+  // the two gated residual contractions) write that copy beside h
+  T* hb = fuse_ln ? h->at<T>(h->lay.hb) : nullptr;
   const float* mods_all = h->at<float>(h->lay.mods);
 
   // context rows appended in this step: u goes below the block rows of act_qkv
@@ -682,11 +709,11 @@ fm_status draft_impl(fm_handle* h, const void* noise, int B, const void* new_fea
     const float* mods = mods_all + (size_t)j * (6 * L + 2) * d;
     if (j == 0) {
       FM_TRY(probe_begin(h, FM_PROBE_EMBED, st));
-      FM_TRY(embed<T>(h, noise, c.V, Mb, 0.f, 1.f, st));
+      FM_TRY(embed<T>(h, noise, c.V, Mb, 0.f, 1.f, hb, st));
       FM_TRY(probe_end(h, FM_PROBE_EMBED, st));
     } else {
       const float sp = h->times[j - 1];
-      FM_TRY(embed<T>(h, h->at<T>(h->lay.dsoft), c.V, Mb, (1.f - s) / (1.f - sp), (s - sp) / (1.f - sp), st));
+      FM_TRY(embed<T>(h, h->at<T>(h->lay.dsoft), c.V, Mb, (1.f - s) / (1.f - sp), (s - sp) / (1.f - sp), hb, st));
     }
     if (hidden) FM_TRY(trace_copy(hres, hidden + ((size_t)j * (L + 1)) * Mb * d, (size_t)Mb * d, st));
     const int m_qkv = Mb + (j == 0 ? n_new : 0);
@@ -705,7 +732,7 @@ fm_status draft_impl(fm_handle* h, const void* noise, int B, const void* new_fea
         std::memcpy(e.ctx_pos0, ctx.ctx_pos0, sizeof e.ctx_pos0);
         e.col_offset = 0;
         if (fuse_ln) {
-          FM_TRY(gemm_ln<T>(h, EPI_QKV, hres, mv + 0 * d, mv + 1 * d, act_qkv + (size_t)Mb * d, m_qkv - Mb,
+          FM_TRY(gemm_ln<T>(h, EPI_QKV, hb, mv + 0 * d, mv + 1 * d, act_qkv + (size_t)Mb * d, m_qkv - Mb,
                             blk(h, l, B_WQKV), 3 * d, d, e, st));
         } else {
           FM_TRY(ln_mod<T>(h, hres, Mb, mv + 0 * d, mv + 1 * d, act_qkv, d, st));
@@ -719,6 +746,8 @@ fm_status draft_impl(fm_handle* h, const void* noise, int B, const void* new_fea
         e.out_f32 = hres;
         e.ld_f32 = d;
         e.gate = mv + 2 * d;
+        e.out_act = hb;
+        e.ld_act = d;
         FM_TRY(gemm<T>(h, EPI_RESID, attn_o, d, Mb, blk(h, l, B_WO), d, d, e, st));
       }
       {
@@ -729,7 +758,7 @@ fm_status draft_impl(fm_handle* h, const void* noise, int B, const void* new_fea
         const int pk = (j == 0 && l == 0) ? FM_PROBE_FC1 : -1;
         if (fuse_ln) {
           FM_TRY(probe_begin(h, pk, st));
-          FM_TRY(gemm_ln<T>(h, EPI_GELU, hres, mv + 3 * d, mv + 4 * d, nullptr, 0, blk(h, l, B_W1), F, d, e, st));
+          FM_TRY(gemm_ln<T>(h, EPI_GELU, hb, mv + 3 * d, mv + 4 * d, nullptr, 0, blk(h, l, B_W1), F, d, e, st));
           FM_TRY(probe_end(h, pk, st));
         } else {
           FM_TRY(ln_mod<T>(h, hres, Mb, mv + 3 * d, mv + 4 * d, act_d, d, st));
@@ -744,6 +773,8 @@ fm_status draft_impl(fm_handle* h, const void* noise, int B, const void* new_fea
         e.out_f32 = hres;
         e.ld_f32 = d;
         e.gate = mv + 5 * d;
+        e.out_act = hb;
+        e.ld_act = d;
         FM_TRY(gemm<T>(h, EPI_RESID, act_f, F, Mb, blk(h, l, B_W2), d, F, e, st));
       }
       if (hidden) FM_TRY(trace_copy(hres, hidden + ((size_t)j * (L + 1) + l + 1) * Mb * d, (size_t)Mb * d, st));

@@ -23,7 +23,8 @@ enum EpiKind {
   EPI_F32 = 0,    // out_f32[m][n] = v + bias[n]
   EPI_ACT = 1,    // out_act[m][n] = T(v + bias[n])
   EPI_GELU = 2,   // out_act[m][n] = T(gelu(v + bias[n]))
-  EPI_RESID = 3,  // out_f32[m][n] += gate[n] * (v + bias[n])   (residual stream)
+  EPI_RESID = 3,  // out_f32[m][n] += gate[n] * (v + bias[n])   (residual stream);
+                  // with out_act, also the new value in the storage type there
   EPI_QKV = 4     // block rows: queries to out_act, keys/values to the branch's
                   // scratch block of the cache; context rows: keys/values to the cache
 };
@@ -32,7 +33,7 @@ struct EpiParams {
   const void* bias;     // [N] storage type, or null
   float* out_f32;       // EPI_F32 / EPI_RESID
   int ld_f32;
-  void* out_act;        // EPI_ACT / EPI_GELU / EPI_QKV
+  void* out_act;        // EPI_ACT / EPI_GELU / EPI_QKV; EPI_RESID: copy of the residual, or null
   int ld_act;
   const float* gate;    // EPI_RESID, [N]
   // EPI_QKV (cache layout: attention.hpp)
@@ -74,7 +75,9 @@ __device__ __forceinline__ void epilogue(const EpiParams& e, int m, int n, float
     reinterpret_cast<T*>(e.out_act)[(size_t)m * e.ld_act + n] = from_f32<T>(gelu_tanh(v));
   } else if (EPI == EPI_RESID) {
     float* p = e.out_f32 + (size_t)m * e.ld_f32 + n;
-    *p = *p + e.gate[n] * v;
+    const float r = *p + e.gate[n] * v;
+    *p = r;
+    if (e.out_act) reinterpret_cast<T*>(e.out_act)[(size_t)m * e.ld_act + n] = from_f32<T>(r);
   } else {  // EPI_QKV
     const int nn = n + e.col_offset;
     int pos, req;
@@ -243,10 +246,12 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs g, EpiParams e) 
 
 // LayerNorm fused into the A operand (tile-group kernel): rows 0..15 of the
 // contraction are LN(h[r]) * (1 + scale) + shift rounded to the storage type,
-// computed inside the kernel from the float32 residual rows; rows 16.. come
-// from GemmArgs::A as usual (context rows, already normalised).
+// computed inside the kernel from the residual rows in the storage type (the
+// copy their producer writes beside the float32 stream, which halves the rows'
+// bytes in bf16); rows 16.. come from GemmArgs::A as usual (context rows,
+// already normalised).  Statistics and normalisation are float32.
 struct LnArgs {
-  const float* h;      // [16][ldh] float32
+  const void* h;       // [16][ldh] storage type
   int ldh;
   const float* shift;  // [K]
   const float* scale;  // [K]
@@ -275,7 +280,6 @@ __global__ __launch_bounds__(NW * 64) void gemm_tg_kernel(GemmArgs g, EpiParams 
   constexpr int TILE_U4 = NW * 512;
   constexpr int KMAX = NW * KC;                            // LN: longest k range
   constexpr int MODQ = LN ? (KMAX / 4 + NW * 64 - 1) / (NW * 64) : 1;  // float4 of scale (and shift) per thread
-  constexpr int HQ = VE / 4;                               // float4 per fragment of residual
   constexpr int SHIFT_OFF = MODQ * NW * 64 * 4;
   __shared__ uint4 smem[TILE_U4 > RED_U4 ? TILE_U4 : RED_U4];
   __shared__ __align__(16) float smod[LN ? 2 * MODQ * NW * 64 * 4 : 1];  // scale, then shift at SHIFT_OFF
@@ -322,16 +326,12 @@ __global__ __launch_bounds__(NW * 64) void gemm_tg_kernel(GemmArgs g, EpiParams 
     // ---- issue: residual rows, modulation, A rows, weights.  Addresses are
     // clamped in range and nothing here is conditional, so no load waits for
     // another one before the statistics need the residual rows.
-    float4 hv[LN ? 8 : 1][HQ];
+    VT hv[LN ? 8 : 1];
     float4 mv[MODQ], mv2[MODQ];
     if constexpr (LN) {
-      const float* hr = ln.h + (size_t)j * ln.ldh;
+      const T* hr = reinterpret_cast<const T*>(ln.h) + (size_t)j * ln.ldh;
 #pragma unroll
-      for (int st = 0; st < 8; ++st) {
-        const int k = kok[st] ? k0 + (4 * st + grp) * VE : 0;
-#pragma unroll
-        for (int q = 0; q < HQ; ++q) hv[st][q] = *reinterpret_cast<const float4*>(hr + k + 4 * q);
-      }
+      for (int st = 0; st < 8; ++st) hv[st] = vload<T>(hr + (kok[st] ? k0 + (4 * st + grp) * VE : 0));
       const int kq = g.K / 4;
 #pragma unroll
       for (int q = 0; q < MODQ; ++q) {
@@ -369,8 +369,10 @@ __global__ __launch_bounds__(NW * 64) void gemm_tg_kernel(GemmArgs g, EpiParams 
 #pragma unroll
       for (int st = 0; st < 8; ++st) {
         const float mk = kok[st] ? 1.f : 0.f;
+        float y[VE];
+        unpack_vec(hv[st], y);
 #pragma unroll
-        for (int q = 0; q < HQ; ++q) sum += mk * ((hv[st][q].x + hv[st][q].y) + (hv[st][q].z + hv[st][q].w));
+        for (int q = 0; q < VE; q += 4) sum += mk * ((y[q] + y[q + 1]) + (y[q + 2] + y[q + 3]));
       }
       sum += __shfl_xor(sum, 16, 64);
       sum += __shfl_xor(sum, 32, 64);
@@ -379,9 +381,11 @@ __global__ __launch_bounds__(NW * 64) void gemm_tg_kernel(GemmArgs g, EpiParams 
 #pragma unroll
       for (int st = 0; st < 8; ++st) {
         const float mk = kok[st] ? 1.f : 0.f;
+        float y[VE];
+        unpack_vec(hv[st], y);
 #pragma unroll
-        for (int q = 0; q < HQ; ++q) {
-          const float a = hv[st][q].x - mw, b = hv[st][q].y - mw, cc = hv[st][q].z - mw, d = hv[st][q].w - mw;
+        for (int q = 0; q < VE; q += 4) {
+          const float a = y[q] - mw, b = y[q + 1] - mw, cc = y[q + 2] - mw, d = y[q + 3] - mw;
           m2 += mk * ((a * a + b * b) + (cc * cc + d * d));
         }
       }
@@ -407,15 +411,16 @@ __global__ __launch_bounds__(NW * 64) void gemm_tg_kernel(GemmArgs g, EpiParams 
 #pragma unroll
       for (int st = 0; st < 8; ++st) {
         const int k = kok[st] ? k0 + (4 * st + grp) * VE : 0;
-        float y[VE];
+        float x[VE], y[VE];
+        unpack_vec(hv[st], x);
 #pragma unroll
-        for (int q = 0; q < HQ; ++q) {
+        for (int q = 0; q < VE / 4; ++q) {
           const float4 sc = *reinterpret_cast<const float4*>(&smod[k + 4 * q]);
           const float4 sh = *reinterpret_cast<const float4*>(&smod[SHIFT_OFF + k + 4 * q]);
-          y[4 * q + 0] = ((hv[st][q].x - mean) * rstd) * (1.f + sc.x) + sh.x;
-          y[4 * q + 1] = ((hv[st][q].y - mean) * rstd) * (1.f + sc.y) + sh.y;
-          y[4 * q + 2] = ((hv[st][q].z - mean) * rstd) * (1.f + sc.z) + sh.z;
-          y[4 * q + 3] = ((hv[st][q].w - mean) * rstd) * (1.f + sc.w) + sh.w;
+          y[4 * q + 0] = ((x[4 * q + 0] - mean) * rstd) * (1.f + sc.x) + sh.x;
+          y[4 * q + 1] = ((x[4 * q + 1] - mean) * rstd) * (1.f + sc.y) + sh.y;
+          y[4 * q + 2] = ((x[4 * q + 2] - mean) * rstd) * (1.f + sc.z) + sh.z;
+          y[4 * q + 3] = ((x[4 * q + 3] - mean) * rstd) * (1.f + sc.w) + sh.w;
         }
         af[0][st] = pack_vec<T>(y);
       }
