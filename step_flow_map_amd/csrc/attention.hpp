@@ -29,12 +29,15 @@
 // Results never depend on scheduling.
 #pragma once
 #include "common.hpp"
+#include "stream.hpp"
 
 namespace fm {
 
 constexpr int ATT_RANGES_MAX = 8;  // ranges per (branch, head) = arrivals per counter
+constexpr int ATT_TREE_RANGES = 16;  // ranges per head of attention_tree_kernel (no counter)
 constexpr int FM_MAX_REQ = 4;      // requests with their own context in one launch
 constexpr int ATT_BLK = 32;        // keys per block
+constexpr int KB_ROWS = 16;        // block rows (queries) per branch
 
 // slot of key kk (0..31) inside a 32-key block of the value cache
 template <typename T> __host__ __device__ __forceinline__ int vt_slot(int kk);
@@ -63,6 +66,120 @@ struct AttnArgs {
   void* out;           // [B*K][d]
   float scale;         // 1/sqrt(hd)
 };
+
+// One wave's 16 queries against one 32-key block (nv valid keys): transposed
+// scores by MFMA, online softmax per query row (running max and sum, the
+// accumulator rescaled), then O^T += V^T P^T with P kept in registers.
+template <typename T, int HD>
+struct AttnTile {
+  typedef typename Vec<T>::type VT;
+  static constexpr int VE = Vec<T>::N;
+  static constexpr int QS = HD / (4 * VE);  // score MFMA steps over the head width
+  static constexpr int OT = HD / 16;        // 16-dim output tiles
+  static constexpr int PS = 32 / (4 * VE);  // P.V steps per block: bf16 1, float 2
+  VT k[2][QS];                              // keys 16*tb + j, pieces 4s+grp
+  VT v[PS][OT];                             // value dims 16t + j, slots ps*4*VE + grp*VE ..
+};
+
+template <typename T, int HD>
+__device__ __forceinline__ void attn_block(const AttnTile<T, HD>& t, const typename Vec<T>::type (&qf)[AttnTile<T, HD>::QS],
+                                           int nv, float scale, float& m_run, float& l_run,
+                                           f32x4 (&o)[AttnTile<T, HD>::OT]) {
+  typedef typename Vec<T>::type VT;
+  constexpr int QS = AttnTile<T, HD>::QS, OT = AttnTile<T, HD>::OT, PS = AttnTile<T, HD>::PS;
+  constexpr bool BF = sizeof(T) == 2;
+  const int grp = (threadIdx.x & 63) >> 4;
+  // transposed scores: sc[tb][i] = S[query j][key 16tb + 4grp + i]
+  f32x4 sc[2];
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb) {
+    sc[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < QS; ++s) mma(sc[tb], t.k[tb][s], qf[s]);
+  }
+  float mb = -INFINITY;
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int kk = 16 * tb + 4 * grp + i;
+      sc[tb][i] = kk < nv ? sc[tb][i] * scale : -INFINITY;
+      mb = fmaxf(mb, sc[tb][i]);
+    }
+  mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
+  mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
+  const float m_new = fmaxf(m_run, mb);  // finite: key 0 of every block is valid
+  const float corr = expf(m_run - m_new);
+  float p[2][4], ps_sum = 0.f;
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[tb][i] = expf(sc[tb][i] - m_new);  // 0 for masked keys
+      ps_sum += p[tb][i];
+    }
+  ps_sum += __shfl_xor(ps_sum, 16, 64);
+  ps_sum += __shfl_xor(ps_sum, 32, 64);
+  l_run = l_run * corr + ps_sum;
+  m_run = m_new;
+#pragma unroll
+  for (int ot = 0; ot < OT; ++ot)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[ot][i] *= corr;
+  // values of masked keys are zeroed (the cache there may hold anything)
+  const bool partial = nv < ATT_BLK;
+  if constexpr (BF) {
+    // P^T fragment: element e <- key (e < 4 ? 4grp+e : 16+4grp+e-4) = sc layout
+    uint32_t hi[4], lo[4];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float a = p[w >> 1][(2 * w) & 3], c = p[w >> 1][(2 * w + 1) & 3];
+      const bf16_t ah = f32_to_bf16(a), ch = f32_to_bf16(c);
+      const bf16_t al = f32_to_bf16(a - bf16_to_f32(ah)), cl = f32_to_bf16(c - bf16_to_f32(ch));
+      hi[w] = (uint32_t)ah | ((uint32_t)ch << 16);
+      lo[w] = (uint32_t)al | ((uint32_t)cl << 16);
+    }
+    const uint4 phi = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+    const uint4 plo = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+    uint4 vmask = make_uint4(~0u, ~0u, ~0u, ~0u);
+    if (partial) {
+      uint32_t mw[4];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const int e0 = 2 * w, e1 = 2 * w + 1;
+        const int k0 = e0 < 4 ? 4 * grp + e0 : 16 + 4 * grp + e0 - 4;
+        const int k1 = e1 < 4 ? 4 * grp + e1 : 16 + 4 * grp + e1 - 4;
+        mw[w] = (k0 < nv ? 0xFFFFu : 0u) | (k1 < nv ? 0xFFFF0000u : 0u);
+      }
+      vmask = make_uint4(mw[0], mw[1], mw[2], mw[3]);
+    }
+#pragma unroll
+    for (int ot = 0; ot < OT; ++ot) {
+      uint4 v = t.v[0][ot];
+      v.x &= vmask.x; v.y &= vmask.y; v.z &= vmask.z; v.w &= vmask.w;
+      mma(o[ot], v, phi);
+      mma(o[ot], v, plo);
+    }
+  } else {
+#pragma unroll
+    for (int ps = 0; ps < PS; ++ps) {
+      // step ps covers keys 16ps + 4grp + i: lane's p[ps][i]
+      const float4 pf = make_float4(p[ps][0], p[ps][1], p[ps][2], p[ps][3]);
+#pragma unroll
+      for (int ot = 0; ot < OT; ++ot) {
+        float4 v = t.v[ps][ot];
+        if (partial) {
+          const int k0 = 16 * ps + 4 * grp;
+          v.x = k0 + 0 < nv ? v.x : 0.f;
+          v.y = k0 + 1 < nv ? v.y : 0.f;
+          v.z = k0 + 2 < nv ? v.z : 0.f;
+          v.w = k0 + 3 < nv ? v.w : 0.f;
+        }
+        mma(o[ot], v, pf);
+      }
+    }
+  }
+}
 
 template <typename T, int HD, int NW>
 __global__ __launch_bounds__(NW * 64) void attention_kernel(AttnArgs g) {
@@ -99,10 +216,7 @@ __global__ __launch_bounds__(NW * 64) void attention_kernel(AttnArgs g) {
     for (int s = 0; s < QS; ++s) qf[s] = vload<T>(qrow + (4 * s + grp) * VE);
   }
 
-  struct Tile {
-    VT k[2][QS];     // keys 16*tb + j, pieces 4s+grp
-    VT v[PS][OT];    // value dims 16t + j, slots ps*4*VE + grp*VE ..
-  };
+  typedef AttnTile<T, HD> Tile;
   // physical block and number of valid keys of logical block bi
   auto phys = [&](int bi) { return bi < ctx_blocks ? bi : g.scratch_blk + g.scratch_step * b; };
   auto nvalid = [&](int bi) { return bi < ctx_blocks ? min(ATT_BLK, C - ATT_BLK * bi) : KB; };
@@ -127,110 +241,16 @@ __global__ __launch_bounds__(NW * 64) void attention_kernel(AttnArgs g) {
 #pragma unroll
   for (int t = 0; t < OT; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto process = [&](Tile& t, int bi) {
-    const int nv = nvalid(bi);
-    // transposed scores: sc[tb][i] = S[query j][key 16tb + 4grp + i]
-    f32x4 sc[2];
-#pragma unroll
-    for (int tb = 0; tb < 2; ++tb) {
-      sc[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < QS; ++s) mma(sc[tb], t.k[tb][s], qf[s]);
-    }
-    float mb = -INFINITY;
-#pragma unroll
-    for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int kk = 16 * tb + 4 * grp + i;
-        sc[tb][i] = kk < nv ? sc[tb][i] * g.scale : -INFINITY;
-        mb = fmaxf(mb, sc[tb][i]);
-      }
-    mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
-    mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
-    const float m_new = fmaxf(m_run, mb);  // finite: key 0 of every block is valid
-    const float corr = expf(m_run - m_new);
-    float p[2][4], ps_sum = 0.f;
-#pragma unroll
-    for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p[tb][i] = expf(sc[tb][i] - m_new);  // 0 for masked keys
-        ps_sum += p[tb][i];
-      }
-    ps_sum += __shfl_xor(ps_sum, 16, 64);
-    ps_sum += __shfl_xor(ps_sum, 32, 64);
-    l_run = l_run * corr + ps_sum;
-    m_run = m_new;
-#pragma unroll
-    for (int ot = 0; ot < OT; ++ot)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) o[ot][i] *= corr;
-    // values of masked keys are zeroed (the cache there may hold anything)
-    const bool partial = nv < ATT_BLK;
-    if constexpr (BF) {
-      // P^T fragment: element e <- key (e < 4 ? 4grp+e : 16+4grp+e-4) = sc layout
-      uint32_t hi[4], lo[4];
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float a = p[w >> 1][(2 * w) & 3], c = p[w >> 1][(2 * w + 1) & 3];
-        const bf16_t ah = f32_to_bf16(a), ch = f32_to_bf16(c);
-        const bf16_t al = f32_to_bf16(a - bf16_to_f32(ah)), cl = f32_to_bf16(c - bf16_to_f32(ch));
-        hi[w] = (uint32_t)ah | ((uint32_t)ch << 16);
-        lo[w] = (uint32_t)al | ((uint32_t)cl << 16);
-      }
-      const uint4 phi = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-      const uint4 plo = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-      uint4 vmask = make_uint4(~0u, ~0u, ~0u, ~0u);
-      if (partial) {
-        uint32_t mw[4];
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const int e0 = 2 * w, e1 = 2 * w + 1;
-          const int k0 = e0 < 4 ? 4 * grp + e0 : 16 + 4 * grp + e0 - 4;
-          const int k1 = e1 < 4 ? 4 * grp + e1 : 16 + 4 * grp + e1 - 4;
-          mw[w] = (k0 < nv ? 0xFFFFu : 0u) | (k1 < nv ? 0xFFFF0000u : 0u);
-        }
-        vmask = make_uint4(mw[0], mw[1], mw[2], mw[3]);
-      }
-#pragma unroll
-      for (int ot = 0; ot < OT; ++ot) {
-        uint4 v = t.v[0][ot];
-        v.x &= vmask.x; v.y &= vmask.y; v.z &= vmask.z; v.w &= vmask.w;
-        mma(o[ot], v, phi);
-        mma(o[ot], v, plo);
-      }
-    } else {
-#pragma unroll
-      for (int ps = 0; ps < PS; ++ps) {
-        // step ps covers keys 16ps + 4grp + i: lane's p[ps][i]
-        const float4 pf = make_float4(p[ps][0], p[ps][1], p[ps][2], p[ps][3]);
-#pragma unroll
-        for (int ot = 0; ot < OT; ++ot) {
-          float4 v = t.v[ps][ot];
-          if (partial) {
-            const int k0 = 16 * ps + 4 * grp;
-            v.x = k0 + 0 < nv ? v.x : 0.f;
-            v.y = k0 + 1 < nv ? v.y : 0.f;
-            v.z = k0 + 2 < nv ? v.z : 0.f;
-            v.w = k0 + 3 < nv ? v.w : 0.f;
-          }
-          mma(o[ot], v, pf);
-        }
-      }
-    }
-  };
-
   // blocks blo + wave, +NW, ... with the next block's loads in flight
   Tile t0, t1;
   int bi = blo + wave;
   if (bi < bhi) load(t0, bi);
   for (; bi < bhi; bi += 2 * NW) {
     if (bi + NW < bhi) load(t1, bi + NW);
-    process(t0, bi);
+    attn_block<T, HD>(t0, qf, nvalid(bi), g.scale, m_run, l_run, o);
     if (bi + NW < bhi) {
       if (bi + 2 * NW < bhi) load(t0, bi + 2 * NW);
-      process(t1, bi + NW);
+      attn_block<T, HD>(t1, qf, nvalid(bi + NW), g.scale, m_run, l_run, o);
     }
   }
 
@@ -299,6 +319,270 @@ __global__ __launch_bounds__(NW * 64) void attention_kernel(AttnArgs g) {
   }
 #pragma unroll
   for (int c = 0; c < CPT; ++c) out[c] = from_f32<T>(num[c] / den);
+}
+
+
+// Attention of the four branches of one tree over their shared context (bf16
+// storage).  A workgroup of 8 waves takes a (head, range of context blocks);
+// wave w serves branch w / 2 and stream w % 2, and the two streams take the
+// range's blocks alternately.  A block's keys and values (32 x HD each) are
+// read from HBM once per workgroup: every wave loads a part of the next two
+// blocks into registers while the current two are computed, writes it into
+// the other half of a double-buffered LDS stage, and one barrier per step
+// hands the stage over.  Pieces are placed in LDS with XOR swizzles (key rows
+// by key, value rows by row / 4) so that the MFMA fragment reads of each 16
+// lanes hit distinct banks.  Each branch's own 16 block rows (its scratch
+// block) are read by the branch's stream-0 wave of the last range straight
+// from HBM.  The waves of a branch merge through LDS; with several ranges the
+// ranges' partial states go to memory and attention_merge_kernel combines
+// them (spread over many workgroups: one workgroup merging all four
+// branches of a head would be bound by the bytes one CU can take in).
+// All branches see the same context length (g.C[0]).
+template <int HD>
+__global__ __launch_bounds__(512) void attention_tree_kernel(AttnArgs g) {
+  typedef bf16_t T;
+  typedef AttnTile<T, HD> Tile;
+  constexpr int NW = 8, BR = 4, WPB = NW / BR;
+  constexpr int QS = Tile::QS, OT = Tile::OT, VE = Tile::VE;
+  constexpr int KP = HD / VE;                          // 16-byte pieces per key row
+  constexpr int PART_U4 = 32 * KP;                     // a block's keys (= its values) in uint4
+  constexpr int BLOCK_U4 = 2 * PART_U4;
+  constexpr int STEP_U4 = WPB * BLOCK_U4;              // blocks of one step (one per stream)
+  constexpr int PER_LANE = STEP_U4 / (NW * 64);
+  static_assert(PER_LANE * NW * 64 == STEP_U4, "a step's blocks split evenly over the lanes");
+  constexpr int STAGE_BYTES = 2 * STEP_U4 * 16;        // two steps
+  constexpr int MERGE_BYTES = NW * KB_ROWS * (HD + 4) * 4;
+  constexpr int SMEM_BYTES = STAGE_BYTES > MERGE_BYTES ? STAGE_BYTES : MERGE_BYTES;
+  __shared__ __align__(16) unsigned char smem[SMEM_BYTES];
+  __shared__ float sm[NW][KB_ROWS], sl[NW][KB_ROWS];
+  uint4* stage = reinterpret_cast<uint4*>(smem);
+  u32x4_t* stagev = reinterpret_cast<u32x4_t*>(smem);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int j = lane & 15, grp = lane >> 4;
+  const int range = blockIdx.x % g.n_ranges, head = blockIdx.x / g.n_ranges;
+  const int b = wave / WPB, stream = wave % WPB;
+  const int C = g.C[0];
+  const int ctx_blocks = (C + ATT_BLK - 1) / ATT_BLK;
+  const int blo = min(ctx_blocks, range * g.blocks_per_range);
+  const int bhi = min(ctx_blocks, blo + g.blocks_per_range);
+  const int n_steps = (bhi - blo + WPB - 1) / WPB;
+  const T* kbase = reinterpret_cast<const T*>(g.kc) + (size_t)head * g.P * HD;
+  const T* vbase = reinterpret_cast<const T*>(g.vt) + (size_t)head * (g.P / ATT_BLK) * HD * ATT_BLK;
+
+  uint4 qf[QS];
+  {
+    const T* qrow = reinterpret_cast<const T*>(g.q) + (size_t)(b * g.K + j) * g.ldq + head * HD;
+#pragma unroll
+    for (int s = 0; s < QS; ++s) qf[s] = vload<T>(qrow + (4 * s + grp) * VE);
+  }
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4 o[OT];
+#pragma unroll
+  for (int t = 0; t < OT; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // MFMA fragments of this wave's block of a step from the stage half
+  auto frags = [&](Tile& t, int half) {
+    const uint4* kb = stage + half * STEP_U4 + stream * BLOCK_U4;
+    const uint4* vb = kb + PART_U4;
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      const int key = 16 * tb + j;
+#pragma unroll
+      for (int s = 0; s < QS; ++s) t.k[tb][s] = kb[key * KP + ((4 * s + grp) ^ (key & (KP - 1)))];
+    }
+#pragma unroll
+    for (int ot = 0; ot < OT; ++ot) {
+      const int r = 16 * ot + j;
+      t.v[0][ot] = vb[r * 4 + (grp ^ ((r >> 2) & 3))];
+    }
+  };
+
+  // lane's share of a step: element e = u*512 + tid of the step's uint4
+  // (stream, keys/values, slot); the global piece is chosen so that it lands
+  // at that slot of the swizzled layout.  Blocks past the range load block
+  // blo instead (never used).  Both addresses are formed and one selected, so
+  // no branch surrounds the load.
+  const uint4* src[PER_LANE];
+  int src_blk[PER_LANE];
+#pragma unroll
+  for (int u = 0; u < PER_LANE; ++u) {
+    const int e = u * NW * 64 + tid;
+    const int sb = e / BLOCK_U4, w = e % BLOCK_U4;
+    const int key = w / KP, kpiece = (w % KP) ^ (key & (KP - 1));
+    const int wv = w - PART_U4, r = wv >> 2, vpiece = (wv & 3) ^ ((r >> 2) & 3);
+    const T* ks = kbase + (size_t)key * HD + kpiece * VE;
+    const T* vs = vbase + (size_t)r * ATT_BLK + vpiece * VE;
+    src[u] = reinterpret_cast<const uint4*>(w < PART_U4 ? ks : vs);
+    src_blk[u] = sb;
+  }
+  // uint4 offset of block bi from block 0: keys ATT_BLK*HD elements, values HD*ATT_BLK
+  constexpr int BLK_STRIDE_U4 = ATT_BLK * HD / VE;
+  // D steps of prefetch in flight in registers: step st's share goes to
+  // pf[st % D], is written to LDS half st & 1 at the end of step st - 1, and
+  // the barrier between steps orders LDS only, so the later steps' loads stay
+  // in flight.  The steps are padded to a multiple of D; steps past the range
+  // compute nothing and fetch block blo (clamped, never used), so no branch
+  // surrounds a prefetch.
+  constexpr int D = 2;
+  if (n_steps > 0) {
+    u32x4_t pf[D][PER_LANE];  // native vectors: kept in registers
+#pragma unroll
+    for (int k = 0; k < D; ++k)
+#pragma unroll
+      for (int u = 0; u < PER_LANE; ++u) {
+        const int bi0 = blo + k * WPB + src_blk[u];
+        pf[k][u] = *reinterpret_cast<const u32x4_t*>(src[u] + (size_t)(bi0 < bhi ? bi0 : blo) * BLK_STRIDE_U4);
+      }
+#pragma unroll
+    for (int u = 0; u < PER_LANE; ++u) stagev[u * NW * 64 + tid] = pf[0][u];
+    lds_barrier();
+    for (int st0 = 0; st0 < n_steps; st0 += D) {
+#pragma unroll
+      for (int k = 0; k < D; ++k) {
+        const int st = st0 + k;
+        const int half = k & 1;  // D is even: st & 1 == k & 1
+        // pf[k] (step st) is already in LDS: refill it with step st + D
+#pragma unroll
+        for (int u = 0; u < PER_LANE; ++u) {
+          const int bi0 = blo + (st + D) * WPB + src_blk[u];
+          pf[k][u] = *reinterpret_cast<const u32x4_t*>(src[u] + (size_t)(bi0 < bhi ? bi0 : blo) * BLK_STRIDE_U4);
+        }
+        const int bi = blo + st * WPB + stream;
+        if (bi < bhi) {
+          Tile t;
+          frags(t, half);
+          attn_block<T, HD>(t, qf, min(ATT_BLK, C - ATT_BLK * bi), g.scale, m_run, l_run, o);
+        }
+#pragma unroll
+        for (int u = 0; u < PER_LANE; ++u) stagev[(half ^ 1) * STEP_U4 + u * NW * 64 + tid] = pf[(k + 1) % D][u];
+        lds_barrier();
+      }
+    }
+  }
+  // the branch's own block rows: the last range, the branch's stream-0 wave
+  if (range == g.n_ranges - 1 && stream == 0) {
+    Tile t;
+    const int pb = g.scratch_blk + b;
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      const T* kr = kbase + (size_t)(pb * ATT_BLK + 16 * tb + j) * HD;
+#pragma unroll
+      for (int s = 0; s < QS; ++s) t.k[tb][s] = vload<T>(kr + (4 * s + grp) * VE);
+    }
+    const T* vb = vbase + (size_t)pb * HD * ATT_BLK;
+#pragma unroll
+    for (int ot = 0; ot < OT; ++ot) t.v[0][ot] = vload<T>(vb + (size_t)(16 * ot + j) * ATT_BLK + grp * VE);
+    attn_block<T, HD>(t, qf, KB_ROWS, g.scale, m_run, l_run, o);
+  }
+
+  // ---- merge each branch's waves (fixed order) through LDS (the stage is free)
+  typedef float MergeRow[KB_ROWS][HD + 4];
+  MergeRow* so = reinterpret_cast<MergeRow*>(smem);
+#pragma unroll
+  for (int ot = 0; ot < OT; ++ot)
+    *reinterpret_cast<float4*>(&so[wave][j][16 * ot + 4 * grp]) = make_float4(o[ot][0], o[ot][1], o[ot][2], o[ot][3]);
+  if (grp == 0) {
+    sm[wave][j] = m_run;
+    sl[wave][j] = l_run;
+  }
+  __syncthreads();
+  // thread lt of branch mb's 128 handles column lt of all 16 rows, so every
+  // row's stores and loads below are contiguous across the lanes
+  constexpr int TPB = NW * 64 / BR;  // threads per branch (= HD at HD 128)
+  static_assert(TPB % HD == 0 || HD % TPB == 0, "columns split evenly");
+  constexpr int CPT = HD / TPB > 0 ? HD / TPB : 1;  // columns per thread
+  const int mb = tid / TPB, lt = tid % TPB, w0 = mb * WPB;
+  const int bh = mb * g.nh + head;
+  const bool col_ok = lt < HD;  // HD < TPB: the surplus threads idle
+  float acc[KB_ROWS][CPT], Mr[KB_ROWS], Lr[KB_ROWS];
+#pragma unroll
+  for (int row = 0; row < KB_ROWS; ++row) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < WPB; ++w) M = fmaxf(M, sm[w0 + w][row]);
+    float Lsum = 0.f;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) acc[row][c] = 0.f;
+#pragma unroll
+    for (int w = 0; w < WPB; ++w) {
+      const float wt = M == -INFINITY ? 0.f : expf(sm[w0 + w][row] - M);
+      Lsum += wt * sl[w0 + w][row];
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) acc[row][c] += wt * (col_ok ? so[w0 + w][row][c * TPB + lt] : 0.f);
+    }
+    Mr[row] = M;
+    Lr[row] = Lsum;
+  }
+  if (g.n_ranges == 1) {
+    if (col_ok) {
+#pragma unroll
+      for (int row = 0; row < KB_ROWS; ++row) {
+        T* out = reinterpret_cast<T*>(g.out) + (size_t)(mb * g.K + row) * g.d + head * HD;
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) out[c * TPB + lt] = from_f32<T>(acc[row][c] / Lr[row]);
+      }
+    }
+    return;
+  }
+  // ---- publish this range (row by row, contiguous); attention_merge_kernel,
+  // launched next, combines the ranges
+  if (col_ok) {
+#pragma unroll
+    for (int row = 0; row < KB_ROWS; ++row) {
+      const size_t pr = ((size_t)bh * g.n_ranges + range) * KB_ROWS + row;
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) g.part_o[pr * HD + c * TPB + lt] = acc[row][c];
+    }
+  }
+  if (lt < KB_ROWS) {
+    const size_t pr = ((size_t)bh * g.n_ranges + range) * KB_ROWS + lt;
+    float m = 0.f, l = 0.f;
+#pragma unroll
+    for (int row = 0; row < KB_ROWS; ++row) {
+      m = row == lt ? Mr[row] : m;
+      l = row == lt ? Lr[row] : l;
+    }
+    g.part_ml[pr * 2 + 0] = m;
+    g.part_ml[pr * 2 + 1] = l;
+  }
+}
+
+// Combination of the ranges' (max, sum, output) of attention_tree_kernel for
+// B branches x nh heads x 16 rows: workgroup (branch, head, 2-row group),
+// thread = column; ranges in order, so results never depend on scheduling.
+template <typename T, int HD>
+__global__ __launch_bounds__(HD) void attention_merge_kernel(AttnArgs g) {
+  constexpr int RG = 2;  // rows per workgroup
+  const int col = threadIdx.x;
+  const int bh = blockIdx.x / (KB_ROWS / RG), row0 = (blockIdx.x % (KB_ROWS / RG)) * RG;
+  const int b = bh / g.nh, head = bh % g.nh;
+  float ov[RG][ATT_TREE_RANGES], mv[RG][ATT_TREE_RANGES], lv[RG][ATT_TREE_RANGES];
+#pragma unroll
+  for (int i = 0; i < RG; ++i)
+#pragma unroll
+    for (int r = 0; r < ATT_TREE_RANGES; ++r) {
+      const bool ok = r < g.n_ranges;
+      const size_t pr = ((size_t)bh * g.n_ranges + (ok ? r : 0)) * KB_ROWS + row0 + i;
+      ov[i][r] = g.part_o[pr * HD + col];
+      mv[i][r] = ok ? g.part_ml[pr * 2 + 0] : -INFINITY;
+      lv[i][r] = g.part_ml[pr * 2 + 1];
+    }
+#pragma unroll
+  for (int i = 0; i < RG; ++i) {
+    float MM = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < ATT_TREE_RANGES; ++r) MM = fmaxf(MM, mv[i][r]);
+    float den = 0.f, num = 0.f;
+#pragma unroll
+    for (int r = 0; r < ATT_TREE_RANGES; ++r) {
+      // a range without blocks (or past n_ranges) has M = -inf: weight 0
+      const float wt = mv[i][r] == -INFINITY ? 0.f : expf(mv[i][r] - MM);
+      den += wt * lv[i][r];
+      num += wt * ov[i][r];
+    }
+    reinterpret_cast<T*>(g.out)[(size_t)(b * g.K + row0 + i) * g.d + head * HD + col] = from_f32<T>(num / den);
+  }
 }
 
 }  // namespace fm

@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <type_traits>
 #include <string>
 #include <vector>
 
@@ -239,8 +240,9 @@ Layout make_layout(const fm_config& c) {
   L.attn_o = take(Mb * d * es);
   L.act_f = take(Mb * F * es);
   L.qkv = take(Mb * d * es);  // queries of the block rows
-  L.att_po = take((size_t)max_blocks(c) * c.n_heads * ATT_MAX_RANGES * KB * hd * 4);
-  L.att_ml = take((size_t)max_blocks(c) * c.n_heads * ATT_MAX_RANGES * KB * 2 * 4);
+  const int att_ranges = std::max(ATT_MAX_RANGES, ATT_TREE_RANGES);
+  L.att_po = take((size_t)max_blocks(c) * c.n_heads * att_ranges * KB * hd * 4);
+  L.att_ml = take((size_t)max_blocks(c) * c.n_heads * att_ranges * KB * 2 * 4);
   L.partial = take(partial_bytes(c));
   L.lm_part = take((size_t)LM_GRID * Mb * 8);
   L.lm_lse = take((size_t)LM_GRID * Mb * 8);
@@ -490,6 +492,33 @@ fm_status attention(fm_handle* h, int l, int B, const int* C, bool own_ctx, hipS
   a.counters = h->at<uint32_t>(h->lay.counters);
   a.out = h->at<T>(h->lay.attn_o);
   a.scale = 1.0f / std::sqrt((float)hd);
+  if constexpr (std::is_same<T, bf16_t>::value) {
+    // four branches over one shared context: each key/value block is read once
+    // per (head, range) and served to every branch from LDS
+    bool same_ctx = true;
+    for (int bb = 1; bb < B; ++bb) same_ctx = same_ctx && C[bb] == C[0];
+    if (!own_ctx && B == 4 && same_ctx && (hd == 128 || hd == 64)) {
+      const int ctx_blocks = cdiv(C[0], ATT_BLK);
+      const int r = std::min(ATT_TREE_RANGES, std::max(1, cdiv(ctx_blocks, 4)));
+      a.blocks_per_range = std::max(1, cdiv(ctx_blocks, r));
+      a.n_ranges = std::max(1, cdiv(ctx_blocks, a.blocks_per_range));
+      const int tgrid = c.n_heads * a.n_ranges;
+      if (hd == 128)
+        hipLaunchKernelGGL((attention_tree_kernel<128>), dim3(tgrid), dim3(512), 0, st, a);
+      else
+        hipLaunchKernelGGL((attention_tree_kernel<64>), dim3(tgrid), dim3(512), 0, st, a);
+      FM_LAUNCHED("attention_tree_kernel");
+      if (a.n_ranges > 1) {
+        const int mgrid = B * c.n_heads * (KB / 2);
+        if (hd == 128)
+          hipLaunchKernelGGL((attention_merge_kernel<T, 128>), dim3(mgrid), dim3(128), 0, st, a);
+        else
+          hipLaunchKernelGGL((attention_merge_kernel<T, 64>), dim3(mgrid), dim3(64), 0, st, a);
+        FM_LAUNCHED("attention_merge_kernel");
+      }
+      return FM_OK;
+    }
+  }
   const int grid = B * c.n_heads * p.n_ranges;
   if (hd == 128)
     hipLaunchKernelGGL((attention_kernel<T, 128, ATT_WAVES>), dim3(grid), dim3(ATT_WAVES * 64), 0, st, a);
