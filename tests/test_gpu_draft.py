@@ -134,6 +134,22 @@ def test_two_step_schedule(cfg):
     print(f"  2-step {cfg.name}: logit error {rel:.2e}, near-ties {ties}")
 
 
+@pytest.mark.parametrize("prefill", [0, 24, 25, 142, 1500])
+def test_tree_shared_context_lengths(prefill):
+    """Four bf16 branches over one shared context at head width 128 (each key
+    block read once per (head, range) and served to every branch): no context
+    but the 8 appended rows, exactly one key block, one row past it, five
+    blocks (three per range: a range whose second step has one stream idle),
+    and 48 blocks over 12 ranges (merged by a separate pass)."""
+    cfg = MID_BF16.with_(name=f"mid_tree_c{prefill}", B=4, c_prefill=prefill)
+    w, feats, noise = _case(cfg, B=4)
+    dr = make_drafter(cfg, w)
+    dr.set_schedule(cfg.times)
+    tok, logits, hidden = run_draft(dr, cfg, noise, feats, cfg.c_prefill, want_hidden=True)
+    rel, ties = check_draft(cfg, w, noise, feats, cfg.c_prefill, tok, logits, hidden)
+    print(f"  tree C {cfg.C}: logit error {rel:.2e}, near-ties {ties}")
+
+
 @pytest.mark.parametrize("cfg", [TINY, SMALL_BF16, MID_BF16, WIDE_F32],
                          ids=["tiny_f32", "small_bf16", "mid_bf16", "wide_f32"])
 def test_draft_tree_of_four(cfg):
