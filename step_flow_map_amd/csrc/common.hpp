@@ -82,6 +82,16 @@ __device__ __forceinline__ void unpack_vec(float4 v, float (&y)[4]) {
   y[3] = v.w;
 }
 
+// 16 bytes per lane from global memory straight into LDS: lane i's bytes go to
+// lds_base + 16 i (lds_base must be the same for the whole wave).  Completion
+// is counted like a vector load, and the compiler waits for all outstanding
+// vector loads before any LDS read that follows, so this pays where nothing
+// else needs to stay in flight.  For data already in L2 it moves several times
+// more bytes per CU than loads into registers.
+__device__ __forceinline__ void lds_dma16(const void* src, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(src, lds_base, 16, 0, 0);
+}
+
 // v if keep, else zero, without a branch or a select on the vector
 __device__ __forceinline__ uint4 vkeep(uint4 v, bool keep) {
   const uint32_t m = keep ? ~0u : 0u;

@@ -149,6 +149,16 @@ GemmPlan plan_gemm(int M, int N, int K, fm_dtype t) {
   return p;
 }
 
+// 48..80 rows (bf16), k a multiple of the 512-wide slice, and enough
+// (column group, k slice) workgroups to cover half the CUs: the A slice is
+// kept in LDS per workgroup (gemm_as_kernel) and the slices are summed by
+// gemm_reduce_kernel.  S = k slices.
+bool use_as(int M, int N, int K, fm_dtype t, int* S) {
+  if (t != FM_BF16 || cdiv(M, 16) < 3 || cdiv(M, 16) > 5 || K % AS_KSLICE != 0) return false;
+  *S = K / AS_KSLICE;
+  return cdiv(N, 16 * AS_TILES) * *S >= 128;
+}
+
 struct EmbedPlan {
   int MT, n_cb, S, S1, S2, grid;
 };
@@ -208,6 +218,8 @@ size_t partial_bytes(const fm_config& c) {
     for (int M = std::min(16, s.M);; M = std::min(s.M, M + 16)) {
       GemmPlan p = plan_gemm(M, s.N, s.K, c.dtype);
       if (p.S > 1) mx = std::max(mx, (size_t)p.S * M * s.N * 4);
+      int S_as;
+      if (use_as(M, s.N, s.K, c.dtype, &S_as)) mx = std::max(mx, (size_t)S_as * M * s.N * 4);
       if (M == s.M) break;
     }
   for (int M = 16; M <= Mb; M += 16) {
@@ -350,6 +362,39 @@ template <typename T>
 fm_status gemm(fm_handle* h, int epi, const void* A, int lda, int M, const void* W, int N, int K,
                const EpiParams& e, hipStream_t st) {
   if (M <= 0) return FM_OK;
+  if constexpr (std::is_same<T, bf16_t>::value) {
+    int S_as;
+    if (use_as(M, N, K, h->cfg.dtype, &S_as)) {
+      GemmArgs a{};
+      a.A = A;
+      a.lda = lda;
+      a.M = M;
+      a.W = W;
+      a.ldw = K;
+      a.N = N;
+      a.K = K;
+      a.S = S_as;
+      a.k_split = AS_KSLICE;
+      a.partial = h->at<float>(h->lay.partial);
+      const int grid = cdiv(N, 16 * AS_TILES) * S_as;
+      switch (cdiv(M, 16)) {
+        case 3: hipLaunchKernelGGL((gemm_as_kernel<T, 3>), dim3(grid), dim3(512), 0, st, a); break;
+        case 4: hipLaunchKernelGGL((gemm_as_kernel<T, 4>), dim3(grid), dim3(512), 0, st, a); break;
+        default: hipLaunchKernelGGL((gemm_as_kernel<T, 5>), dim3(grid), dim3(512), 0, st, a); break;
+      }
+      FM_LAUNCHED("gemm_as_kernel");
+      const dim3 rgrid((unsigned)(((size_t)M * N + 255) / 256));
+      switch (epi) {
+        case EPI_F32: hipLaunchKernelGGL((gemm_reduce_kernel<T, EPI_F32>), rgrid, dim3(256), 0, st, a, e); break;
+        case EPI_ACT: hipLaunchKernelGGL((gemm_reduce_kernel<T, EPI_ACT>), rgrid, dim3(256), 0, st, a, e); break;
+        case EPI_GELU: hipLaunchKernelGGL((gemm_reduce_kernel<T, EPI_GELU>), rgrid, dim3(256), 0, st, a, e); break;
+        case EPI_RESID: hipLaunchKernelGGL((gemm_reduce_kernel<T, EPI_RESID>), rgrid, dim3(256), 0, st, a, e); break;
+        default: hipLaunchKernelGGL((gemm_reduce_kernel<T, EPI_QKV>), rgrid, dim3(256), 0, st, a, e); break;
+      }
+      FM_LAUNCHED("gemm_reduce_kernel");
+      return FM_OK;
+    }
+  }
   GemmPlan p = plan_gemm(M, N, K, h->cfg.dtype);
   if (p.S > 1 && p.n_groups > N_COUNTER_SLOTS) return fail(FM_EINVAL, "too many column tiles for split-K");
   GemmArgs a;

@@ -497,4 +497,88 @@ __global__ __launch_bounds__(NW * 64) void gemm_tg_kernel(GemmArgs g, EpiParams 
   }
 }
 
+
+// Many rows (48..80) against a wide weight: the rows' A slice would dominate
+// what every 16-column tile reads, so a workgroup keeps it in LDS.  A
+// workgroup owns 8 column tiles and a 512-wide k slice: wave w issues tile w's
+// two weight chunks, the workgroup copies the slice's A rows into LDS once
+// (direct global-to-LDS loads, one row's 1 KB per copy), and every wave then
+// reads its A fragments from LDS.  Each k slice writes its float32 partial with
+// plain stores; gemm_reduce_kernel, launched next, sums the slices in order
+// and runs the epilogue.  Rows >= M read row 0 (valid memory) and produce
+// outputs that are never stored.
+constexpr int AS_TILES = 8;    // column tiles per workgroup (one a wave)
+constexpr int AS_KSLICE = 512; // k per workgroup: two bf16 chunks
+template <typename T, int MT>
+__global__ __launch_bounds__(512) void gemm_as_kernel(GemmArgs g) {
+  typedef typename Vec<T>::type VT;
+  constexpr int VE = ChunkT<T>::VE;
+  constexpr int KC = ChunkT<T>::KC;
+  constexpr int NCH = AS_KSLICE / KC;             // chunks per slice
+  constexpr int PIECES = AS_KSLICE / VE;           // 16-byte pieces of a row's slice (64)
+  static_assert(PIECES == 64, "one row's slice is one 64-lane copy");
+  __shared__ uint4 sA[MT * 16 * PIECES];
+  __shared__ uint4 wtile[AS_TILES * 512];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int j = lane & 15, grp = lane >> 4;
+  const int group = blockIdx.x / g.S, s = blockIdx.x % g.S;
+  const int n0 = group * 16 * AS_TILES + 16 * wave;
+  const int k0 = s * AS_KSLICE;
+  const T* A = reinterpret_cast<const T*>(g.A);
+  const T* W = reinterpret_cast<const T*>(g.W);
+  // this wave's tile's weight chunks first (the long HBM stream)
+  uint4 r[NCH][8];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) chunk_load<T>(r[c], W, g.ldw, n0, g.N, k0 + c * KC, g.K);
+  // row rr of the slice: one copy of its 1 KB, lane i fetching piece i ^ (rr & 15)
+  // into slot rr*64 + i, so that the fragment reads below (16 rows, one piece
+  // group each) hit 16 distinct banks
+#pragma unroll
+  for (int i = 0; i < MT * 16 / 8; ++i) {
+    const int rr = i * 8 + wave;
+    const T* src = A + (size_t)(rr < g.M ? rr : 0) * g.lda + k0 + (lane ^ (rr & 15)) * VE;
+    lds_dma16(src, sA + rr * PIECES);
+  }
+  __syncthreads();  // the copies have landed (the compiler waits for all loads first)
+  f32x4 acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  uint4* wt = wtile + wave * 512;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    chunk_to_lds(r[c], wt);
+    wave_lds_sync();
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      const VT b = as_vec<T>(chunk_frag(wt, st));
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        mma(acc[mt], as_vec<T>(sA[(mt * 16 + j) * PIECES + ((c * 32 + 4 * st + grp) ^ j)]), b);
+    }
+    wave_lds_sync();
+  }
+  // D element (row 4grp + i, column j) of each row tile
+  const int n = n0 + j;
+  if (n < g.N) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = mt * 16 + 4 * grp + i;
+        if (m < g.M) g.partial[((size_t)s * g.M + m) * g.N + n] = acc[mt][i];
+      }
+  }
+}
+
+// out[m][n] = epilogue(sum over the S k slices of partial[s][m][n], in order)
+template <typename T, int EPI>
+__global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmArgs g, EpiParams e) {
+  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (size_t)g.M * g.N) return;
+  const int m = (int)(idx / g.N), n = (int)(idx % g.N);
+  float v = 0.f;
+  for (int s = 0; s < g.S; ++s) v += g.partial[((size_t)s * g.M + m) * g.N + n];
+  epilogue<T, EPI>(e, m, n, v);
+}
+
 }  // namespace fm
