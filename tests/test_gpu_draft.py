@@ -134,6 +134,19 @@ def test_two_step_schedule(cfg):
     print(f"  2-step {cfg.name}: logit error {rel:.2e}, near-ties {ties}")
 
 
+def test_draft_tree_of_three_at_width_2048():
+    """Three bf16 branches at the drafter's real width: 48 block rows (plus 8
+    appended context rows in QKV), so the contractions keep the rows' k slice
+    in LDS (three and four row tiles) and sum the slices in a second pass."""
+    cfg = W2048_BF16.with_(name="w2048_tree3", B=3)
+    w, feats, noise = _case(cfg, B=3)
+    dr = make_drafter(cfg, w)
+    dr.set_schedule(cfg.times)
+    tok, logits, hidden = run_draft(dr, cfg, noise, feats, cfg.c_prefill, want_hidden=True)
+    rel, ties = check_draft(cfg, w, noise, feats, cfg.c_prefill, tok, logits, hidden)
+    print(f"  tree of 3 at d 2048: logit error {rel:.2e}, near-ties {ties}")
+
+
 @pytest.mark.parametrize("prefill", [0, 24, 25, 142, 1500])
 def test_tree_shared_context_lengths(prefill):
     """Four bf16 branches over one shared context at head width 128 (each key
@@ -150,8 +163,8 @@ def test_tree_shared_context_lengths(prefill):
     print(f"  tree C {cfg.C}: logit error {rel:.2e}, near-ties {ties}")
 
 
-@pytest.mark.parametrize("cfg", [TINY, SMALL_BF16, MID_BF16, WIDE_F32],
-                         ids=["tiny_f32", "small_bf16", "mid_bf16", "wide_f32"])
+@pytest.mark.parametrize("cfg", [TINY, SMALL_BF16, MID_BF16, WIDE_F32, W2048_BF16],
+                         ids=["tiny_f32", "small_bf16", "mid_bf16", "wide_f32", "w2048_bf16"])
 def test_draft_tree_of_four(cfg):
     cfg = cfg.with_(B=4)
     w, feats, noise = _case(cfg, B=4)
@@ -160,9 +173,12 @@ def test_draft_tree_of_four(cfg):
     tok, logits, hidden = run_draft(dr, cfg, noise, feats, cfg.c_prefill, want_hidden=True)
     rel, ties = check_draft(cfg, w, noise, feats, cfg.c_prefill, tok, logits, hidden)
     print(f"  tree {cfg.name}: logit error {rel:.2e}, near-ties {ties}")
-    # the branches are independent: branch 2 alone gives the same draft
+    # the branches are independent: branch 2 alone gives the same draft.  The
+    # two paths round differently (alone, the fused LayerNorms read h rounded
+    # to bf16; a tree normalises the float32 rows), each within the parity
+    # bound above; a branch seeing another's rows would differ by far more
     dr1 = make_drafter(cfg.with_(B=1), w)
     dr1.set_schedule(cfg.times)
     t1, l1, _ = run_draft(dr1, cfg.with_(B=1), noise[2:3], feats, cfg.c_prefill)
     assert np.array_equal(t1[0], tok[2])
-    assert np.abs(l1[0] - logits[2]).max() <= 1e-3 * np.abs(logits[2]).max()
+    assert rowwise_rel_err(l1[0], logits[2]).max() <= 5e-3
