@@ -149,14 +149,20 @@ GemmPlan plan_gemm(int M, int N, int K, fm_dtype t) {
   return p;
 }
 
-// 48..80 rows (bf16), k a multiple of the 512-wide slice, and enough
-// (column group, k slice) workgroups to cover half the CUs: the A slice is
-// kept in LDS per workgroup (gemm_as_kernel) and the slices are summed by
-// gemm_reduce_kernel.  S = k slices.
-bool use_as(int M, int N, int K, fm_dtype t, int* S) {
-  if (t != FM_BF16 || cdiv(M, 16) < 3 || cdiv(M, 16) > 5 || K % AS_KSLICE != 0) return false;
-  *S = K / AS_KSLICE;
-  return cdiv(N, 16 * AS_TILES) * *S >= 128;
+// 48..80 rows (bf16) and enough (column group, k slice) workgroups to cover
+// half the CUs: the A slice is kept in LDS per workgroup (gemm_as_kernel) and
+// the slices are summed by gemm_reduce_kernel.  Slices of 512 (two chunks)
+// where they give enough workgroups, else of 256.  S = k slices.
+bool use_as(int M, int N, int K, fm_dtype t, int* S, int* KS) {
+  if (t != FM_BF16 || cdiv(M, 16) < 3 || cdiv(M, 16) > 5) return false;
+  const int groups = cdiv(N, 16 * AS_TILES);
+  for (int ks : {512, 256}) {
+    if (K % ks != 0 || groups * (K / ks) < 128) continue;
+    *S = K / ks;
+    *KS = ks;
+    return true;
+  }
+  return false;
 }
 
 struct EmbedPlan {
@@ -218,8 +224,8 @@ size_t partial_bytes(const fm_config& c) {
     for (int M = std::min(16, s.M);; M = std::min(s.M, M + 16)) {
       GemmPlan p = plan_gemm(M, s.N, s.K, c.dtype);
       if (p.S > 1) mx = std::max(mx, (size_t)p.S * M * s.N * 4);
-      int S_as;
-      if (use_as(M, s.N, s.K, c.dtype, &S_as)) mx = std::max(mx, (size_t)S_as * M * s.N * 4);
+      int S_as, KS_as;
+      if (use_as(M, s.N, s.K, c.dtype, &S_as, &KS_as)) mx = std::max(mx, (size_t)S_as * M * s.N * 4);
       if (M == s.M) break;
     }
   for (int M = 16; M <= Mb; M += 16) {
@@ -363,8 +369,8 @@ fm_status gemm(fm_handle* h, int epi, const void* A, int lda, int M, const void*
                const EpiParams& e, hipStream_t st) {
   if (M <= 0) return FM_OK;
   if constexpr (std::is_same<T, bf16_t>::value) {
-    int S_as;
-    if (use_as(M, N, K, h->cfg.dtype, &S_as)) {
+    int S_as, KS_as;
+    if (use_as(M, N, K, h->cfg.dtype, &S_as, &KS_as)) {
       GemmArgs a{};
       a.A = A;
       a.lda = lda;
@@ -374,13 +380,18 @@ fm_status gemm(fm_handle* h, int epi, const void* A, int lda, int M, const void*
       a.N = N;
       a.K = K;
       a.S = S_as;
-      a.k_split = AS_KSLICE;
+      a.k_split = KS_as;
       a.partial = h->at<float>(h->lay.partial);
       const int grid = cdiv(N, 16 * AS_TILES) * S_as;
-      switch (cdiv(M, 16)) {
-        case 3: hipLaunchKernelGGL((gemm_as_kernel<T, 3>), dim3(grid), dim3(512), 0, st, a); break;
-        case 4: hipLaunchKernelGGL((gemm_as_kernel<T, 4>), dim3(grid), dim3(512), 0, st, a); break;
-        default: hipLaunchKernelGGL((gemm_as_kernel<T, 5>), dim3(grid), dim3(512), 0, st, a); break;
+      const int mt = cdiv(M, 16);
+      if (KS_as == 512) {
+        if (mt == 3) hipLaunchKernelGGL((gemm_as_kernel<T, 3, 512>), dim3(grid), dim3(512), 0, st, a);
+        else if (mt == 4) hipLaunchKernelGGL((gemm_as_kernel<T, 4, 512>), dim3(grid), dim3(512), 0, st, a);
+        else hipLaunchKernelGGL((gemm_as_kernel<T, 5, 512>), dim3(grid), dim3(512), 0, st, a);
+      } else {
+        if (mt == 3) hipLaunchKernelGGL((gemm_as_kernel<T, 3, 256>), dim3(grid), dim3(512), 0, st, a);
+        else if (mt == 4) hipLaunchKernelGGL((gemm_as_kernel<T, 4, 256>), dim3(grid), dim3(512), 0, st, a);
+        else hipLaunchKernelGGL((gemm_as_kernel<T, 5, 256>), dim3(grid), dim3(512), 0, st, a);
       }
       FM_LAUNCHED("gemm_as_kernel");
       const dim3 rgrid((unsigned)(((size_t)M * N + 255) / 256));

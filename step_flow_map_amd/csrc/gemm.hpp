@@ -508,36 +508,38 @@ __global__ __launch_bounds__(NW * 64) void gemm_tg_kernel(GemmArgs g, EpiParams 
 // and runs the epilogue.  Rows >= M read row 0 (valid memory) and produce
 // outputs that are never stored.
 constexpr int AS_TILES = 8;    // column tiles per workgroup (one a wave)
-constexpr int AS_KSLICE = 512; // k per workgroup: two bf16 chunks
-template <typename T, int MT>
+template <typename T, int MT, int KS>  // KS: k per workgroup, 256 or 512 (one or two bf16 chunks)
 __global__ __launch_bounds__(512) void gemm_as_kernel(GemmArgs g) {
   typedef typename Vec<T>::type VT;
   constexpr int VE = ChunkT<T>::VE;
   constexpr int KC = ChunkT<T>::KC;
-  constexpr int NCH = AS_KSLICE / KC;             // chunks per slice
-  constexpr int PIECES = AS_KSLICE / VE;           // 16-byte pieces of a row's slice (64)
-  static_assert(PIECES == 64, "one row's slice is one 64-lane copy");
+  constexpr int NCH = KS / KC;                     // chunks per slice
+  constexpr int PIECES = KS / VE;                  // 16-byte pieces of a row's slice
+  static_assert(PIECES == 32 || PIECES == 64, "one row's slice is one copy of up to 64 lanes");
   __shared__ uint4 sA[MT * 16 * PIECES];
   __shared__ uint4 wtile[AS_TILES * 512];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int j = lane & 15, grp = lane >> 4;
   const int group = blockIdx.x / g.S, s = blockIdx.x % g.S;
   const int n0 = group * 16 * AS_TILES + 16 * wave;
-  const int k0 = s * AS_KSLICE;
+  const int k0 = s * KS;
   const T* A = reinterpret_cast<const T*>(g.A);
   const T* W = reinterpret_cast<const T*>(g.W);
   // this wave's tile's weight chunks first (the long HBM stream)
   uint4 r[NCH][8];
 #pragma unroll
   for (int c = 0; c < NCH; ++c) chunk_load<T>(r[c], W, g.ldw, n0, g.N, k0 + c * KC, g.K);
-  // row rr of the slice: one copy of its 1 KB, lane i fetching piece i ^ (rr & 15)
-  // into slot rr*64 + i, so that the fragment reads below (16 rows, one piece
-  // group each) hit 16 distinct banks
+  // row rr of the slice: one copy of its KS elements, lane i fetching piece
+  // i ^ (rr & 15) into slot rr*PIECES + i, so that the fragment reads below (16
+  // rows, one piece group each) hit 16 distinct banks.  With 32 pieces a row
+  // the upper half-wave copies row rr + 1.
+  constexpr int ROWS_PER_COPY = 64 / PIECES;
 #pragma unroll
-  for (int i = 0; i < MT * 16 / 8; ++i) {
-    const int rr = i * 8 + wave;
-    const T* src = A + (size_t)(rr < g.M ? rr : 0) * g.lda + k0 + (lane ^ (rr & 15)) * VE;
-    lds_dma16(src, sA + rr * PIECES);
+  for (int i = 0; i < MT * 16 / (8 * ROWS_PER_COPY); ++i) {
+    const int rr = (i * 8 + wave) * ROWS_PER_COPY + lane / PIECES;
+    const int pc = lane % PIECES;
+    const T* src = A + (size_t)(rr < g.M ? rr : 0) * g.lda + k0 + (pc ^ (rr & 15)) * VE;
+    lds_dma16(src, sA + (rr - lane / PIECES) * PIECES);
   }
   __syncthreads();  // the copies have landed (the compiler waits for all loads first)
   f32x4 acc[MT];
