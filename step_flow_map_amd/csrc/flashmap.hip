@@ -154,10 +154,10 @@ GemmPlan plan_gemm(int M, int N, int K, fm_dtype t) {
 // the slices are summed by gemm_reduce_kernel.  Slices of 512 (two chunks)
 // where they give enough workgroups, else of 256.  S = k slices.
 bool use_as(int M, int N, int K, fm_dtype t, int* S, int* KS) {
-  if (t != FM_BF16 || cdiv(M, 16) < 3 || cdiv(M, 16) > 5) return false;
+  if (t != FM_BF16 || cdiv(M, 16) < 3 || cdiv(M, 16) > 5 || N % 4 != 0) return false;
   const int groups = cdiv(N, 16 * AS_TILES);
   for (int ks : {512, 256}) {
-    if (K % ks != 0 || groups * (K / ks) < 128) continue;
+    if (K % ks != 0 || K / ks > AS_SMAX || groups * (K / ks) < 128) continue;
     *S = K / ks;
     *KS = ks;
     return true;
@@ -394,7 +394,7 @@ fm_status gemm(fm_handle* h, int epi, const void* A, int lda, int M, const void*
         else hipLaunchKernelGGL((gemm_as_kernel<T, 5, 256>), dim3(grid), dim3(512), 0, st, a);
       }
       FM_LAUNCHED("gemm_as_kernel");
-      const dim3 rgrid((unsigned)(((size_t)M * N + 255) / 256));
+      const dim3 rgrid((unsigned)(((size_t)M * N / 4 + 255) / 256));
       switch (epi) {
         case EPI_F32: hipLaunchKernelGGL((gemm_reduce_kernel<T, EPI_F32>), rgrid, dim3(256), 0, st, a, e); break;
         case EPI_ACT: hipLaunchKernelGGL((gemm_reduce_kernel<T, EPI_ACT>), rgrid, dim3(256), 0, st, a, e); break;

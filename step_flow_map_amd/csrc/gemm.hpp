@@ -572,15 +572,32 @@ __global__ __launch_bounds__(512) void gemm_as_kernel(GemmArgs g) {
   }
 }
 
-// out[m][n] = epilogue(sum over the S k slices of partial[s][m][n], in order)
+// out[m][n] = epilogue(sum over the S k slices of partial[s][m][n], in order).
+// A thread takes 4 adjacent outputs (N % 4 == 0) with every slice's float4 in
+// flight at once (S <= AS_SMAX).
+constexpr int AS_SMAX = 16;
 template <typename T, int EPI>
 __global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmArgs g, EpiParams e) {
-  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (size_t)g.M * g.N) return;
-  const int m = (int)(idx / g.N), n = (int)(idx % g.N);
-  float v = 0.f;
-  for (int s = 0; s < g.S; ++s) v += g.partial[((size_t)s * g.M + m) * g.N + n];
-  epilogue<T, EPI>(e, m, n, v);
+  const size_t q = (size_t)blockIdx.x * 256 + threadIdx.x;  // float4 index of [M][N]
+  if (q * 4 >= (size_t)g.M * g.N) return;
+  const size_t mn = (size_t)g.M * g.N;
+  float4 pv[AS_SMAX];
+#pragma unroll
+  for (int s = 0; s < AS_SMAX; ++s)
+    pv[s] = s < g.S ? reinterpret_cast<const float4*>(g.partial + s * mn)[q] : make_float4(0.f, 0.f, 0.f, 0.f);
+  float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int s = 0; s < AS_SMAX; ++s) {
+    v.x += pv[s].x;
+    v.y += pv[s].y;
+    v.z += pv[s].z;
+    v.w += pv[s].w;
+  }
+  const int m = (int)(q * 4 / g.N), n = (int)(q * 4 % g.N);
+  epilogue<T, EPI>(e, m, n + 0, v.x);
+  epilogue<T, EPI>(e, m, n + 1, v.y);
+  epilogue<T, EPI>(e, m, n + 2, v.z);
+  epilogue<T, EPI>(e, m, n + 3, v.w);
 }
 
 }  // namespace fm
