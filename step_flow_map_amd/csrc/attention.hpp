@@ -554,31 +554,41 @@ __global__ __launch_bounds__(512) void attention_tree_kernel(AttnArgs g) {
 template <typename T, int HD>
 __global__ __launch_bounds__(HD) void attention_merge_kernel(AttnArgs g) {
   constexpr int RG = 2;  // rows per workgroup
+  static_assert(HD >= RG * ATT_TREE_RANGES, "one (row, range) pair per thread");
+  __shared__ float2 sml[RG][ATT_TREE_RANGES];
   const int col = threadIdx.x;
   const int bh = blockIdx.x / (KB_ROWS / RG), row0 = (blockIdx.x % (KB_ROWS / RG)) * RG;
   const int b = bh / g.nh, head = bh % g.nh;
-  float ov[RG][ATT_TREE_RANGES], mv[RG][ATT_TREE_RANGES], lv[RG][ATT_TREE_RANGES];
+  // the rows' (max, sum) of every range: one pair per thread, through LDS
+  {
+    const int i = col / ATT_TREE_RANGES, r = col % ATT_TREE_RANGES;
+    if (i < RG) {
+      const size_t pr = ((size_t)bh * g.n_ranges + (r < g.n_ranges ? r : 0)) * KB_ROWS + row0 + i;
+      const float2 ml = reinterpret_cast<const float2*>(g.part_ml)[pr];
+      // a range past n_ranges (or one without blocks, M = -inf) gets weight 0
+      sml[i][r] = make_float2(r < g.n_ranges ? ml.x : -INFINITY, ml.y);
+    }
+  }
+  float ov[RG][ATT_TREE_RANGES];
 #pragma unroll
   for (int i = 0; i < RG; ++i)
 #pragma unroll
     for (int r = 0; r < ATT_TREE_RANGES; ++r) {
-      const bool ok = r < g.n_ranges;
-      const size_t pr = ((size_t)bh * g.n_ranges + (ok ? r : 0)) * KB_ROWS + row0 + i;
+      const size_t pr = ((size_t)bh * g.n_ranges + (r < g.n_ranges ? r : 0)) * KB_ROWS + row0 + i;
       ov[i][r] = g.part_o[pr * HD + col];
-      mv[i][r] = ok ? g.part_ml[pr * 2 + 0] : -INFINITY;
-      lv[i][r] = g.part_ml[pr * 2 + 1];
     }
+  __syncthreads();
 #pragma unroll
   for (int i = 0; i < RG; ++i) {
     float MM = -INFINITY;
 #pragma unroll
-    for (int r = 0; r < ATT_TREE_RANGES; ++r) MM = fmaxf(MM, mv[i][r]);
+    for (int r = 0; r < ATT_TREE_RANGES; ++r) MM = fmaxf(MM, sml[i][r].x);
     float den = 0.f, num = 0.f;
 #pragma unroll
     for (int r = 0; r < ATT_TREE_RANGES; ++r) {
-      // a range without blocks (or past n_ranges) has M = -inf: weight 0
-      const float wt = mv[i][r] == -INFINITY ? 0.f : expf(mv[i][r] - MM);
-      den += wt * lv[i][r];
+      const float2 ml = sml[i][r];
+      const float wt = ml.x == -INFINITY ? 0.f : expf(ml.x - MM);
+      den += wt * ml.y;
       num += wt * ov[i][r];
     }
     reinterpret_cast<T*>(g.out)[(size_t)(b * g.K + row0 + i) * g.d + head * HD + col] = from_f32<T>(num / den);
