@@ -394,13 +394,14 @@ fm_status gemm(fm_handle* h, int epi, const void* A, int lda, int M, const void*
         else hipLaunchKernelGGL((gemm_as_kernel<T, 5, 256>), dim3(grid), dim3(512), 0, st, a);
       }
       FM_LAUNCHED("gemm_as_kernel");
-      const dim3 rgrid((unsigned)(((size_t)M * N / 4 + 255) / 256));
+      const dim3 rgrid4((unsigned)(((size_t)M * N / 4 + 255) / 256));
+      const dim3 rgrid1((unsigned)(((size_t)M * N + 255) / 256));
       switch (epi) {
-        case EPI_F32: hipLaunchKernelGGL((gemm_reduce_kernel<T, EPI_F32>), rgrid, dim3(256), 0, st, a, e); break;
-        case EPI_ACT: hipLaunchKernelGGL((gemm_reduce_kernel<T, EPI_ACT>), rgrid, dim3(256), 0, st, a, e); break;
-        case EPI_GELU: hipLaunchKernelGGL((gemm_reduce_kernel<T, EPI_GELU>), rgrid, dim3(256), 0, st, a, e); break;
-        case EPI_RESID: hipLaunchKernelGGL((gemm_reduce_kernel<T, EPI_RESID>), rgrid, dim3(256), 0, st, a, e); break;
-        default: hipLaunchKernelGGL((gemm_reduce_kernel<T, EPI_QKV>), rgrid, dim3(256), 0, st, a, e); break;
+        case EPI_F32: hipLaunchKernelGGL((gemm_reduce_kernel<T, EPI_F32, 4>), rgrid4, dim3(256), 0, st, a, e); break;
+        case EPI_ACT: hipLaunchKernelGGL((gemm_reduce_kernel<T, EPI_ACT, 4>), rgrid4, dim3(256), 0, st, a, e); break;
+        case EPI_GELU: hipLaunchKernelGGL((gemm_reduce_kernel<T, EPI_GELU, 4>), rgrid4, dim3(256), 0, st, a, e); break;
+        case EPI_RESID: hipLaunchKernelGGL((gemm_reduce_kernel<T, EPI_RESID, 4>), rgrid4, dim3(256), 0, st, a, e); break;
+        default: hipLaunchKernelGGL((gemm_reduce_kernel<T, EPI_QKV, 1>), rgrid1, dim3(256), 0, st, a, e); break;
       }
       FM_LAUNCHED("gemm_reduce_kernel");
       return FM_OK;

@@ -573,31 +573,41 @@ __global__ __launch_bounds__(512) void gemm_as_kernel(GemmArgs g) {
 }
 
 // out[m][n] = epilogue(sum over the S k slices of partial[s][m][n], in order).
-// A thread takes 4 adjacent outputs (N % 4 == 0) with every slice's float4 in
-// flight at once (S <= AS_SMAX).
+// A thread takes VW adjacent outputs (N % VW == 0) with every slice's values in
+// flight at once (S <= AS_SMAX).  The QKV epilogue scatters into the caches, so
+// it runs one output per thread (more threads in flight).
 constexpr int AS_SMAX = 16;
-template <typename T, int EPI>
+template <typename T, int EPI, int VW>
 __global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmArgs g, EpiParams e) {
-  const size_t q = (size_t)blockIdx.x * 256 + threadIdx.x;  // float4 index of [M][N]
-  if (q * 4 >= (size_t)g.M * g.N) return;
+  static_assert(VW == 1 || VW == 4, "one or four outputs per thread");
+  const size_t q = (size_t)blockIdx.x * 256 + threadIdx.x;  // VW-element index of [M][N]
   const size_t mn = (size_t)g.M * g.N;
-  float4 pv[AS_SMAX];
+  if (q * VW >= mn) return;
+  float v[VW];
 #pragma unroll
-  for (int s = 0; s < AS_SMAX; ++s)
-    pv[s] = s < g.S ? reinterpret_cast<const float4*>(g.partial + s * mn)[q] : make_float4(0.f, 0.f, 0.f, 0.f);
-  float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int c = 0; c < VW; ++c) v[c] = 0.f;
+  if constexpr (VW == 4) {
+    float4 pv[AS_SMAX];
 #pragma unroll
-  for (int s = 0; s < AS_SMAX; ++s) {
-    v.x += pv[s].x;
-    v.y += pv[s].y;
-    v.z += pv[s].z;
-    v.w += pv[s].w;
+    for (int s = 0; s < AS_SMAX; ++s)
+      pv[s] = s < g.S ? reinterpret_cast<const float4*>(g.partial + s * mn)[q] : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int s = 0; s < AS_SMAX; ++s) {
+      v[0] += pv[s].x;
+      v[1] += pv[s].y;
+      v[2] += pv[s].z;
+      v[3] += pv[s].w;
+    }
+  } else {
+    float pv[AS_SMAX];
+#pragma unroll
+    for (int s = 0; s < AS_SMAX; ++s) pv[s] = s < g.S ? g.partial[s * mn + q] : 0.f;
+#pragma unroll
+    for (int s = 0; s < AS_SMAX; ++s) v[0] += pv[s];
   }
-  const int m = (int)(q * 4 / g.N), n = (int)(q * 4 % g.N);
-  epilogue<T, EPI>(e, m, n + 0, v.x);
-  epilogue<T, EPI>(e, m, n + 1, v.y);
-  epilogue<T, EPI>(e, m, n + 2, v.z);
-  epilogue<T, EPI>(e, m, n + 3, v.w);
+  const int m = (int)(q * VW / g.N), n = (int)(q * VW % g.N);
+#pragma unroll
+  for (int c = 0; c < VW; ++c) epilogue<T, EPI>(e, m, n + c, v[c]);
 }
 
 }  // namespace fm
