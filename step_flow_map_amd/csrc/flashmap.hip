@@ -165,6 +165,13 @@ bool use_as(int M, int N, int K, fm_dtype t, int* S, int* KS) {
   return false;
 }
 
+// a gated residual contraction on that path whose row-wise reduce can also
+// apply the LayerNorm that follows (widths 2048 and 4096)
+bool resid_ln_fused(int M, int N, int K, fm_dtype t) {
+  int S, KS;
+  return use_as(M, N, K, t, &S, &KS) && (N == 2048 || N == 4096);
+}
+
 struct EmbedPlan {
   int MT, n_cb, S, S1, S2, grid;
 };
@@ -384,6 +391,9 @@ fm_status gemm(fm_handle* h, int epi, const void* A, int lda, int M, const void*
       a.partial = h->at<float>(h->lay.partial);
       const int grid = cdiv(N, 16 * AS_TILES) * S_as;
       const int mt = cdiv(M, 16);
+      const bool ln_after = epi == EPI_RESID && e.ln_out;
+      if (ln_after && !resid_ln_fused(M, N, K, h->cfg.dtype))
+        return fail(FM_EINVAL, "no LayerNorm-fused reduce for this contraction");
       if (KS_as == 512) {
         if (mt == 3) hipLaunchKernelGGL((gemm_as_kernel<T, 3, 512>), dim3(grid), dim3(512), 0, st, a);
         else if (mt == 4) hipLaunchKernelGGL((gemm_as_kernel<T, 4, 512>), dim3(grid), dim3(512), 0, st, a);
@@ -394,6 +404,14 @@ fm_status gemm(fm_handle* h, int epi, const void* A, int lda, int M, const void*
         else hipLaunchKernelGGL((gemm_as_kernel<T, 5, 256>), dim3(grid), dim3(512), 0, st, a);
       }
       FM_LAUNCHED("gemm_as_kernel");
+      if (ln_after) {
+        if (N == 2048)
+          hipLaunchKernelGGL((gemm_reduce_ln_kernel<T, 2>), dim3(M), dim3(1024), 0, st, a, e, 1e-6f);
+        else
+          hipLaunchKernelGGL((gemm_reduce_ln_kernel<T, 4>), dim3(M), dim3(1024), 0, st, a, e, 1e-6f);
+        FM_LAUNCHED("gemm_reduce_ln_kernel");
+        return FM_OK;
+      }
       const dim3 rgrid4((unsigned)(((size_t)M * N / 4 + 255) / 256));
       const dim3 rgrid1((unsigned)(((size_t)M * N + 255) / 256));
       switch (epi) {
@@ -776,6 +794,8 @@ fm_status draft_impl(fm_handle* h, const void* noise, int B, const void* new_fea
     ctx.ctx_first[r + 1] = ctx.ctx_first[r] + (bt ? bt->n_new[r] : n_new);
   }
   const bool fuse_ln = ln_fusable(c, B);
+  // many rows: the reduces of W_o and fc2 also write the LayerNorm that follows
+  const bool ln_in_reduce = !fuse_ln && resid_ln_fused(Mb, d, d, c.dtype) && resid_ln_fused(Mb, d, F, c.dtype);
   T* act_qkv = h->at<T>(h->lay.act_qkv);
   T* act_d = h->at<T>(h->lay.act_d);
   T* act_f = h->at<T>(h->lay.act_f);
@@ -821,7 +841,8 @@ fm_status draft_impl(fm_handle* h, const void* noise, int B, const void* new_fea
           FM_TRY(gemm_ln<T>(h, EPI_QKV, hb, mv + 0 * d, mv + 1 * d, act_qkv + (size_t)Mb * d, m_qkv - Mb,
                             blk(h, l, B_WQKV), 3 * d, d, e, st));
         } else {
-          FM_TRY(ln_mod<T>(h, hres, Mb, mv + 0 * d, mv + 1 * d, act_qkv, d, st));
+          // block 0's rows come from the embedding; later ones were normalised by fc2's reduce
+          if (!ln_in_reduce || l == 0) FM_TRY(ln_mod<T>(h, hres, Mb, mv + 0 * d, mv + 1 * d, act_qkv, d, st));
           FM_TRY(gemm<T>(h, EPI_QKV, act_qkv, d, m_qkv, blk(h, l, B_WQKV), 3 * d, d, e, st));
         }
       }
@@ -834,6 +855,12 @@ fm_status draft_impl(fm_handle* h, const void* noise, int B, const void* new_fea
         e.gate = mv + 2 * d;
         e.out_act = hb;
         e.ld_act = d;
+        if (ln_in_reduce) {  // LN2 for fc1
+          e.ln_shift = mv + 3 * d;
+          e.ln_scale = mv + 4 * d;
+          e.ln_out = act_d;
+          e.ln_ldo = d;
+        }
         FM_TRY(gemm<T>(h, EPI_RESID, attn_o, d, Mb, blk(h, l, B_WO), d, d, e, st));
       }
       {
@@ -847,7 +874,7 @@ fm_status draft_impl(fm_handle* h, const void* noise, int B, const void* new_fea
           FM_TRY(gemm_ln<T>(h, EPI_GELU, hb, mv + 3 * d, mv + 4 * d, nullptr, 0, blk(h, l, B_W1), F, d, e, st));
           FM_TRY(probe_end(h, pk, st));
         } else {
-          FM_TRY(ln_mod<T>(h, hres, Mb, mv + 3 * d, mv + 4 * d, act_d, d, st));
+          if (!ln_in_reduce) FM_TRY(ln_mod<T>(h, hres, Mb, mv + 3 * d, mv + 4 * d, act_d, d, st));
           FM_TRY(probe_begin(h, pk, st));
           FM_TRY(gemm<T>(h, EPI_GELU, act_d, d, Mb, blk(h, l, B_W1), F, d, e, st));
           FM_TRY(probe_end(h, pk, st));
@@ -861,12 +888,19 @@ fm_status draft_impl(fm_handle* h, const void* noise, int B, const void* new_fea
         e.gate = mv + 5 * d;
         e.out_act = hb;
         e.ld_act = d;
+        if (ln_in_reduce) {  // the next block's LN1, or the final LN before the LM head
+          const float* nm = mods + (size_t)6 * (l + 1) * d;
+          e.ln_shift = nm;
+          e.ln_scale = nm + d;
+          e.ln_out = l + 1 < L ? act_qkv : act_d;
+          e.ln_ldo = d;
+        }
         FM_TRY(gemm<T>(h, EPI_RESID, act_f, F, Mb, blk(h, l, B_W2), d, F, e, st));
       }
       if (hidden) FM_TRY(trace_copy(hres, hidden + ((size_t)j * (L + 1) + l + 1) * Mb * d, (size_t)Mb * d, st));
     }
     const float* fin = mods + (size_t)6 * L * d;  // shift_f, scale_f
-    FM_TRY(ln_mod<T>(h, hres, Mb, fin, fin + d, act_d, d, st));
+    if (!ln_in_reduce) FM_TRY(ln_mod<T>(h, hres, Mb, fin, fin + d, act_d, d, st));
     if (t == 1.f) {
       FM_TRY(probe_begin(h, FM_PROBE_LM_HEAD, st));
       FM_TRY(lm_head<T>(h, act_d, Mb, logits, tokens, st, smp));

@@ -16,6 +16,7 @@
 #include "common.hpp"
 #include "stream.hpp"
 #include "attention.hpp"
+#include "norm.hpp"
 
 namespace fm {
 
@@ -49,6 +50,12 @@ struct EpiParams {
   int ctx_first[FM_MAX_REQ + 1];  // ctx_first[r + 1], at position ctx_pos0[r] + c - ctx_first[r]
   int ctx_pos0[FM_MAX_REQ];
   int col_offset;       // logical qkv column of n = 0 (d for a K/V-only call)
+  // EPI_RESID through gemm_reduce_ln_kernel: the LayerNorm + modulation of the
+  // updated rows, written in the storage type (the next contraction's operand)
+  const float* ln_shift;
+  const float* ln_scale;
+  void* ln_out;
+  int ln_ldo;
 };
 
 constexpr int GEMM_SPLIT_MAX = 8;  // k splits per tile (= arrivals per counter)
@@ -608,6 +615,56 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmArgs g, EpiParams 
   const int m = (int)(q * VW / g.N), n = (int)(q * VW % g.N);
 #pragma unroll
   for (int c = 0; c < VW; ++c) epilogue<T, EPI>(e, m, n + c, v[c]);
+}
+
+
+// EPI_RESID reduce fused with the LayerNorm that follows it: one workgroup of
+// 1024 threads per row m sums the S k slices of its N = 1024 * PER columns (in
+// order, all slices in flight), applies the gated residual update to h, and
+// writes LN(h[m]) * (1 + ln_scale) + ln_shift in the storage type (two-pass
+// mean and variance, as ln_mod_kernel).
+template <typename T, int PER>
+__global__ __launch_bounds__(1024) void gemm_reduce_ln_kernel(GemmArgs g, EpiParams e, float eps) {
+  constexpr int NT = 1024;
+  constexpr int SM = AS_SMAX;  // slices in flight (S <= SM)
+  __shared__ float red[NT / 64];
+  const int m = blockIdx.x, t = threadIdx.x;
+  const size_t mn = (size_t)g.M * g.N;
+  float pv[SM][PER];
+#pragma unroll
+  for (int s = 0; s < SM; ++s)
+#pragma unroll
+    for (int p = 0; p < PER; ++p)
+      pv[s][p] = s < g.S ? g.partial[s * mn + (size_t)m * g.N + t + p * NT] : 0.f;
+  float v[PER], sc[PER], sh[PER], sum = 0.f;
+#pragma unroll
+  for (int p = 0; p < PER; ++p) {
+    const int c = t + p * NT;
+    float a = 0.f;
+#pragma unroll
+    for (int s = 0; s < SM; ++s) a += pv[s][p];
+    if (e.bias) a += to_f32<T>(reinterpret_cast<const T*>(e.bias)[c]);
+    float* hp = e.out_f32 + (size_t)m * e.ld_f32 + c;
+    const float r = *hp + e.gate[c] * a;
+    *hp = r;
+    if (e.out_act) reinterpret_cast<T*>(e.out_act)[(size_t)m * e.ld_act + c] = from_f32<T>(r);
+    v[p] = r;
+    sc[p] = e.ln_scale[c];
+    sh[p] = e.ln_shift[c];
+    sum += r;
+  }
+  const float mean = block_sum<T, NT>(sum, red) / (float)g.N;
+  float q = 0.f;
+#pragma unroll
+  for (int p = 0; p < PER; ++p) {
+    const float dv = v[p] - mean;
+    q += dv * dv;
+  }
+  const float var = block_sum<T, NT>(q, red) / (float)g.N;
+  const float rstd = 1.f / sqrtf(var + eps);
+  T* o = reinterpret_cast<T*>(e.ln_out) + (size_t)m * e.ln_ldo;
+#pragma unroll
+  for (int p = 0; p < PER; ++p) o[t + p * NT] = from_f32<T>((v[p] - mean) * rstd * (1.f + sc[p]) + sh[p]);
 }
 
 }  // namespace fm
