@@ -68,6 +68,34 @@ def test_batch_matches_oracle_per_request(cfg, variant):
     print(f"  near-ties {ties}")
 
 
+W2048_BF16 = TINY.with_(name="w2048_bf16", dtype="bf16", V=2000, d=2048, nh=16, H=520, c_prefill=40)
+
+
+def test_batch_of_four_at_width_2048():
+    """Four requests at the drafter's real width (64 block rows plus 13
+    appended context rows in QKV): the contractions keep the rows' k slice in
+    LDS, and the residual reduces apply the following LayerNorm.  Contexts of
+    40, 33, 0 and 70 rows appending 4, 0, 7 and 2."""
+    cfg = W2048_BF16
+    print(f"[batch parity] {cfg.name} x4", flush=True)
+    R = 4
+    prefill = [40, 33, 0, 70]
+    new = [4, 0, 7, 2]
+    w = synth.make_weights(cfg)
+    feats = [synth.make_features(cfg, rows=prefill[r] + new[r], request=r) for r in range(R)]
+    noise = synth.make_noise(cfg, R)
+    tok, logits, dr = _run(cfg, w, prefill, new, noise, feats)
+    W = oracle.Weights.from_storage(w)
+    ties, worst = [], 0.0
+    for r in range(R):
+        ref = oracle.draft(W, cfg, noise[r], feats[r])
+        rel = rowwise_rel_err(logits[r], ref["logits"])
+        worst = max(worst, float(rel.max()))
+        assert rel.max() <= LOGIT_RTOL, (r, rel.max())
+        ties += check_tokens(tok[r], logits[r], ref["logits"], ref["tokens"])
+    print(f"  max row logit error {worst:.2e}; near-ties {ties}")
+
+
 def test_requests_do_not_see_each_other():
     """Request 0's draft is bitwise the same whatever request 1 holds."""
     cfg = MID_BF16
