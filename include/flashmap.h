@@ -57,7 +57,8 @@ typedef enum fm_dtype {
  *   divides d with d / n_heads in {64, 128}; mlp_mult >= 1; n_ctx_layers == 5;
  *   V >= 16 and H >= 1 with V and H multiples of 8 (bf16) or 4 (f32), so
  *   every row starts 16-byte aligned;
- *   1 <= max_branches <= 4; 0 <= max_new <= 16; C_max >= 0; 1 <= max_steps <= 4;
+ *   1 <= max_branches <= 4; 0 <= max_new <= 16; C_max >= 0; 1 <= max_steps <= 4,
+ *   and V <= 524288 when max_steps > 1 (the softmax between jumps);
  *   1 <= max_requests <= 4, and max_branches == 1 when max_requests > 1. */
 typedef struct fm_config {
   int K;             /* drafted block length (16)                            */

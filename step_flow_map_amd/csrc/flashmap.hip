@@ -305,6 +305,8 @@ fm_status check_config(const fm_config* c) {
   if (c->max_branches < 1 || c->max_branches > 4) return fail(FM_EINVAL, "max_branches must be in 1..4");
   if (c->max_new < 0 || c->max_new > 16) return fail(FM_EINVAL, "max_new must be in 0..16");
   if (c->max_steps < 1 || c->max_steps > 4) return fail(FM_EINVAL, "max_steps must be in 1..4");
+  if (c->max_steps > 1 && cdiv(c->V, SOFTMAX_CHUNK) > 128)
+    return fail(FM_EINVAL, "schedules of several jumps take V <= %d (got %d)", 128 * SOFTMAX_CHUNK, c->V);
   if (c->max_requests < 1 || c->max_requests > FM_MAX_REQ)
     return fail(FM_EINVAL, "max_requests must be in 1..%d", FM_MAX_REQ);
   if (c->max_requests > 1 && c->max_branches > 1)
@@ -680,7 +682,7 @@ fm_status softmax_rows(fm_handle* h, int M, hipStream_t st) {
   SoftmaxArgs a;
   a.logits = h->at<float>(h->lay.logits_tmp);
   a.V = c.V;
-  a.n_chunks = cdiv(c.V, SOFTMAX_CHUNK);
+  a.n_chunks = cdiv(c.V, SOFTMAX_CHUNK);  // <= 128 (checked with the configuration)
   a.part = h->at<float>(h->lay.sm_part);
   a.counters = nullptr;
   a.out = h->at<T>(h->lay.dsoft);
