@@ -31,11 +31,11 @@ struct LmArgs {
   const void* W;      // [V][d]
   int V;
   float* logits;      // [M][V] or null
-  uint64_t* partial;  // [gridDim.x][M]
+  uint64_t* partial;  // [M][gridDim.x]
   float tau;          // 0: greedy argmax; > 0: sampling at this temperature
   uint32_t seed_lo, seed_hi;
   int K;              // rows per branch
-  float2* lse_part;   // [gridDim.x][M] (tau > 0)
+  float2* lse_part;   // [M][gridDim.x] (tau > 0)
 };
 
 // Online log-sum-exp state (m, s): sum of exp(x - m) over the values seen.
@@ -193,8 +193,8 @@ __global__ __launch_bounds__(NW * 64) void lmhead_kernel(LmArgs g) {
       k = umax64(k, wbest[w][m]);
       lse_merge(a, b, wlse[w][m].x, wlse[w][m].y);
     }
-    g.partial[(size_t)blockIdx.x * g.M + m] = k;
-    if (g.tau > 0.f) g.lse_part[(size_t)blockIdx.x * g.M + m] = make_float2(a, b);
+    g.partial[(size_t)m * gridDim.x + blockIdx.x] = k;
+    if (g.tau > 0.f) g.lse_part[(size_t)m * gridDim.x + blockIdx.x] = make_float2(a, b);
   }
 }
 
@@ -322,66 +322,63 @@ __global__ __launch_bounds__(NW * 64) void lmhead_ks_kernel(LmArgs g) {
     const int ln = el & 63, q = el >> 6;
     const int m = (q >> 2) * 16 + 4 * (ln >> 4) + (q & 3);
     if (el < ELEMS && (ln & 15) == 0 && m < g.M) {
-      g.partial[(size_t)blockIdx.x * g.M + m] = k;
-      if (g.tau > 0.f) g.lse_part[(size_t)blockIdx.x * g.M + m] = make_float2(a, b);
+      g.partial[(size_t)m * gridDim.x + blockIdx.x] = k;
+      if (g.tau > 0.f) g.lse_part[(size_t)m * gridDim.x + blockIdx.x] = make_float2(a, b);
     }
   }
 }
 
-// tokens[m] = index of max over G workgroup keys, and with lse_part given
-// lse[m] = M + log(sum_g s_g exp(m_g - M)) over the G workgroup states (M the
-// largest m_g; each thread rescales its partial sum once to the row's M).  1024 threads, tpr threads per row on consecutive lanes of
-// one wave (M <= 64); each thread keeps eight loads in flight at once, so
-// G = 512 costs one memory latency for up to 16 rows.  Reductions run over
-// fixed trees, so results are reproducible.
-constexpr int FIN_THREADS = 1024;
+// tokens[m] = index of max over the G workgroup keys of row m, and with
+// lse_part given lse[m] = log sum_g s_g exp(m_g) over the row's G workgroup
+// (max, sum) states.
+// One workgroup per row: the row's G workgroup keys (and states) are
+// contiguous; every thread folds its strided share, then waves and the
+// workgroup combine in a fixed order (keys by max, states by log-sum-exp).
+constexpr int FIN_THREADS = 256;
 __global__ __launch_bounds__(FIN_THREADS) void argmax_finalize_kernel(const uint64_t* partial, int G, int M,
                                                                      int32_t* tokens, const float2* lse_part,
                                                                      float* lse) {
-  int mp = 16;
-  while (mp < M) mp <<= 1;
-  const int tpr = FIN_THREADS / mp;
-  const int m = threadIdx.x / tpr, sub = threadIdx.x % tpr;
-  const int mr = m < M ? m : 0;
+  __shared__ uint64_t sk[FIN_THREADS / 64];
+  __shared__ float2 ss[FIN_THREADS / 64];
+  const int m = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const uint64_t* pk = partial + (size_t)m * G;
+  const float2* pe = lse_part ? lse_part + (size_t)m * G : nullptr;
   uint64_t k = 0ull;
-  float mx = -INFINITY, sum = 0.f;  // this thread's states: sum of s_g exp(m_g - mx)
-  for (int b0 = sub; b0 < G; b0 += 8 * tpr) {
-    uint64_t v[8];
-    float2 e[8];
+  float mx = -INFINITY, sum = 0.f;
+  for (int g0 = t; g0 < G; g0 += 4 * FIN_THREADS) {
+    uint64_t v[4];
+    float2 e[4];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int gi = b0 + u * tpr;
-      const size_t at = (size_t)(gi < G ? gi : 0) * M + mr;
-      v[u] = partial[at];
-      if (lse_part) e[u] = lse_part[at];
+    for (int u = 0; u < 4; ++u) {
+      const int gi = g0 + u * FIN_THREADS;
+      v[u] = gi < G ? pk[gi] : 0ull;
+      if (pe) e[u] = gi < G ? pe[gi] : make_float2(-INFINITY, 0.f);
     }
-    float bm = mx;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const bool in = b0 + u * tpr < G;
-      k = umax64(k, in ? v[u] : 0ull);
-      if (lse_part && in) bm = fmaxf(bm, e[u].x);
-    }
-    if (lse_part) {
-      float bs = mx == -INFINITY ? 0.f : sum * expf(mx - bm);
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (b0 + u * tpr < G) bs += e[u].y * expf(e[u].x - bm);
-      mx = bm;
-      sum = bs;
+    for (int u = 0; u < 4; ++u) {
+      k = umax64(k, v[u]);
+      if (pe) lse_merge(mx, sum, e[u].x, e[u].y);
     }
   }
-  float gm = mx;
-  for (int o = 1; o < tpr; o <<= 1) {  // tpr <= 64
+  for (int o = 1; o < 64; o <<= 1) {
     k = umax64(k, shfl_xor_u64(k, o));
-    if (lse_part) gm = fmaxf(gm, __shfl_xor(gm, o, 64));
+    if (pe) lse_shfl_merge(mx, sum, o);
   }
-  if (lse_part) {
-    float t = mx == -INFINITY ? 0.f : sum * expf(mx - gm);
-    for (int o = 1; o < tpr; o <<= 1) t += __shfl_xor(t, o, 64);
-    if (m < M && sub == 0) lse[m] = gm + logf(t);
+  if (lane == 0) {
+    sk[wave] = k;
+    ss[wave] = make_float2(mx, sum);
   }
-  if (m < M && sub == 0) tokens[m] = (int32_t)argmax_key_index(k);
+  __syncthreads();
+  if (t == 0) {
+    uint64_t kk = sk[0];
+    float a = ss[0].x, b = ss[0].y;
+    for (int w = 1; w < FIN_THREADS / 64; ++w) {
+      kk = umax64(kk, sk[w]);
+      lse_merge(a, b, ss[w].x, ss[w].y);
+    }
+    tokens[m] = (int32_t)argmax_key_index(kk);
+    if (pe) lse[m] = a + logf(b);
+  }
 }
 
 }  // namespace fm
