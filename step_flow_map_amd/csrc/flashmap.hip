@@ -986,7 +986,7 @@ fm_status verify_sample_impl(fm_handle* h, const void* tl, int B, const float* Q
   a.accept = accept;
   hipLaunchKernelGGL((vs_stats_kernel<T>), dim3(a.S, B * (KB + 1)), dim3(VS_THREADS), 0, st, a);
   FM_LAUNCHED("vs_stats_kernel");
-  hipLaunchKernelGGL((vs_accept_kernel<T, KB + 1>), dim3(B), dim3(VS_THREADS), 0, st, a);
+  hipLaunchKernelGGL((vs_accept_kernel<T, KB + 1>), dim3(B), dim3(VS_ACCEPT_THREADS), 0, st, a);
   FM_LAUNCHED("vs_accept_kernel");
   hipLaunchKernelGGL((vs_keys_kernel<T>), dim3(a.S, B), dim3(VS_THREADS), 0, st, a);
   FM_LAUNCHED("vs_keys_kernel");

@@ -161,16 +161,16 @@ __global__ __launch_bounds__(VS_THREADS) void vs_stats_kernel(VsArgs g) {
   }
 }
 
-// One workgroup per branch: thread t holds slice t of every row (S <= 256;
-// all R = K + 1 loads in flight at once).  A row's log-normaliser is M +
-// log(sum_t s_t exp(m_t - M)) with M the largest slice maximum: a max
-// reduction, one exponential per slice and a sum, each over a fixed tree.
-// Lane i of wave 0 then tests draft i.
+// One workgroup of 16 waves per branch: wave w merges the slice states of
+// rows w, w + 16, ... (S <= 256 slices, four per lane, all loads in flight).
+// A row's log-normaliser is M + log(sum_t s_t exp(m_t - M)) with M the
+// largest slice maximum: a max reduction, one exponential per slice and a
+// sum, each over a fixed tree.  Lane i of wave 0 then tests draft i.
+constexpr int VS_ACCEPT_THREADS = 1024;
 template <typename T, int R>
-__global__ __launch_bounds__(VS_THREADS) void vs_accept_kernel(VsArgs g) {
+__global__ __launch_bounds__(VS_ACCEPT_THREADS) void vs_accept_kernel(VsArgs g) {
   static_assert(R <= 65, "K <= 64");
-  constexpr int NWV = VS_THREADS / 64;
-  __shared__ float smax[R][NWV], ssum[R][NWV];
+  constexpr int NWV = VS_ACCEPT_THREADS / 64;
   __shared__ float slse[R];
   const int b = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
   // the drafted token's target and drafter logits, loaded up front
@@ -183,34 +183,23 @@ __global__ __launch_bounds__(VS_THREADS) void vs_accept_kernel(VsArgs g) {
     q_d = g.Q[((size_t)b * g.K + lane) * g.V + d];
     lseq = g.lseQ[b * g.K + lane];
   }
-  float2 e[R];
+  for (int j = wave; j < R; j += NWV) {
+    float2 e[4];
 #pragma unroll
-  for (int j = 0; j < R; ++j)
-    e[j] = t < g.S ? g.stats[((size_t)b * R + j) * g.S + t] : make_float2(-INFINITY, 0.f);
-#pragma unroll
-  for (int j = 0; j < R; ++j) {
-    const float m = warp_max(e[j].x);
-    if (lane == 0) smax[j][wave] = m;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int j = 0; j < R; ++j) {
-    float M = smax[j][0];
-#pragma unroll
-    for (int w = 1; w < NWV; ++w) M = fmaxf(M, smax[j][w]);
-    const float v = t < g.S ? e[j].y * expf(e[j].x - M) : 0.f;
-    const float sum = warp_sum(v);
-    if (lane == 0) ssum[j][wave] = sum;
-  }
-  __syncthreads();
-  for (int j = t; j < R; j += VS_THREADS) {
-    float M = smax[j][0], sum = ssum[j][0];
-    for (int w = 1; w < NWV; ++w) {
-      M = fmaxf(M, smax[j][w]);
-      sum += ssum[j][w];
+    for (int u = 0; u < 4; ++u) {
+      const int i = lane + 64 * u;
+      e[u] = i < g.S ? g.stats[((size_t)b * R + j) * g.S + i] : make_float2(-INFINITY, 0.f);
     }
-    slse[j] = M + logf(sum);
-    g.lse_rows[b * R + j] = slse[j];
+    float M = fmaxf(fmaxf(e[0].x, e[1].x), fmaxf(e[2].x, e[3].x));
+    M = warp_max(M);
+    float v = 0.f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v += lane + 64 * u < g.S ? e[u].y * expf(e[u].x - M) : 0.f;
+    const float sum = warp_sum(v);
+    if (lane == 0) {
+      slse[j] = M + logf(sum);
+      g.lse_rows[b * R + j] = slse[j];
+    }
   }
   __syncthreads();
   if (wave == 0) {
