@@ -85,7 +85,6 @@ template <typename T, int HD>
 __device__ __forceinline__ void attn_block(const AttnTile<T, HD>& t, const typename Vec<T>::type (&qf)[AttnTile<T, HD>::QS],
                                            int nv, float scale, float& m_run, float& l_run,
                                            f32x4 (&o)[AttnTile<T, HD>::OT]) {
-  typedef typename Vec<T>::type VT;
   constexpr int QS = AttnTile<T, HD>::QS, OT = AttnTile<T, HD>::OT, PS = AttnTile<T, HD>::PS;
   constexpr bool BF = sizeof(T) == 2;
   const int grp = (threadIdx.x & 63) >> 4;
@@ -189,7 +188,6 @@ __global__ __launch_bounds__(NW * 64) void attention_kernel(AttnArgs g) {
   constexpr int QS = HD / (4 * VE);   // score MFMA steps over the head width
   constexpr int OT = HD / 16;         // 16-dim output tiles
   constexpr int PS = 32 / (4 * VE);   // P.V steps per block: bf16 1, float 2
-  constexpr bool BF = sizeof(T) == 2;
   __shared__ float so[NW][KB][HD + 4];
   __shared__ float sm[NW][KB], sl[NW][KB];
   __shared__ int flag;

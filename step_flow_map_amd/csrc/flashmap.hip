@@ -669,7 +669,7 @@ fm_status lm_head(fm_handle* h, const void* z, int M, float* logits, int32_t* to
     FM_LAUNCHED("lmhead_kernel");
   }
   if (tokens) {
-    hipLaunchKernelGGL(argmax_finalize_kernel, dim3(M), dim3(FIN_THREADS), 0, st, a.partial, grid, M, tokens,
+    hipLaunchKernelGGL(argmax_finalize_kernel, dim3(M), dim3(FIN_THREADS), 0, st, a.partial, grid, tokens,
                        a.lse_part, smp ? smp->lse : nullptr);
     FM_LAUNCHED("argmax_finalize_kernel");
   }

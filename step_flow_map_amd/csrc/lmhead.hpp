@@ -335,7 +335,7 @@ __global__ __launch_bounds__(NW * 64) void lmhead_ks_kernel(LmArgs g) {
 // contiguous; every thread folds its strided share, then waves and the
 // workgroup combine in a fixed order (keys by max, states by log-sum-exp).
 constexpr int FIN_THREADS = 256;
-__global__ __launch_bounds__(FIN_THREADS) void argmax_finalize_kernel(const uint64_t* partial, int G, int M,
+__global__ __launch_bounds__(FIN_THREADS) void argmax_finalize_kernel(const uint64_t* partial, int G,
                                                                      int32_t* tokens, const float2* lse_part,
                                                                      float* lse) {
   __shared__ uint64_t sk[FIN_THREADS / 64];
