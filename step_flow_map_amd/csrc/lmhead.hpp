@@ -66,7 +66,7 @@ __device__ __forceinline__ void lse_shfl_merge(float& m, float& s, int o) {
 // One finished logit v at (row m, token n): running key, log-sum-exp state,
 // optional dump.
 __device__ __forceinline__ void lm_visit(const LmArgs& g, float v, int m, int n, uint64_t& best, float& lm,
-                                         float& ls) {
+                                         float& ls, bool write = true) {
   float key = v;
   if (g.tau > 0.f) {
     const float x = v / g.tau;
@@ -75,7 +75,7 @@ __device__ __forceinline__ void lm_visit(const LmArgs& g, float v, int m, int n,
                                   g.seed_hi));
   }
   best = umax64(best, argmax_key(key, (uint32_t)n));
-  if (g.logits) g.logits[(size_t)m * g.V + n] = v;
+  if (write && g.logits) g.logits[(size_t)m * g.V + n] = v;
 }
 
 template <typename T, int MT, int NW>
@@ -208,7 +208,11 @@ __global__ __launch_bounds__(NW * 64) void lmhead_kernel(LmArgs g) {
 // per tile suffices); every thread then sums the waves in order for its fixed
 // output elements, updates its running key and writes the logit if asked.
 // The keys of a row are combined over 16 lanes and written per workgroup for
-// argmax_finalize_kernel.
+// argmax_finalize_kernel.  With 16 rows, logits that are asked for wait in LDS
+// (one 1 KB tile per vocabulary tile, up to LM_STAGE_TILES) and are written
+// after the last tile: written tile by tile, their 64-byte row pieces slowed
+// the weight stream by about 10%.
+constexpr int LM_STAGE_TILES = 20;
 template <typename T, int MT, int NW, int CPW>
 __global__ __launch_bounds__(NW * 64) void lmhead_ks_kernel(LmArgs g) {
   typedef typename Vec<T>::type VT;
@@ -218,6 +222,8 @@ __global__ __launch_bounds__(NW * 64) void lmhead_ks_kernel(LmArgs g) {
   constexpr int PER = (ELEMS + NW * 64 - 1) / (NW * 64);  // outputs per thread
   __shared__ uint4 wtiles[NW * 512];
   __shared__ float red[2][NW * ELEMS];
+  constexpr int NT_STAGE = MT == 1 ? LM_STAGE_TILES : 0;
+  __shared__ __align__(16) float slog[NT_STAGE ? NT_STAGE * ELEMS : 4];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int j = lane & 15, grp = lane >> 4;
@@ -228,6 +234,7 @@ __global__ __launch_bounds__(NW * 64) void lmhead_ks_kernel(LmArgs g) {
   const int ntiles = (g.V + 15) / 16;
   const int G = gridDim.x;
   const int nt = (int)blockIdx.x < ntiles ? (ntiles - 1 - (int)blockIdx.x) / G + 1 : 0;
+  const bool stage = NT_STAGE > 0 && g.logits != nullptr && nt <= NT_STAGE;
 
   // z fragments of this wave's chunks: rows >= M and columns >= d are zeroed
   VT zf[CPW][MT][8];
@@ -292,7 +299,8 @@ __global__ __launch_bounds__(NW * 64) void lmhead_ks_kernel(LmArgs g) {
         float v = 0.f;
 #pragma unroll
         for (int w = 0; w < NW; ++w) v += rd[w * ELEMS + el];
-        if (n < g.V && m < g.M) lm_visit(g, v, m, n, best[r], lm[r], ls[r]);
+        if (stage) slog[it * ELEMS + el] = v;
+        if (n < g.V && m < g.M) lm_visit(g, v, m, n, best[r], lm[r], ls[r], !stage);
       }
     }
   };
@@ -308,6 +316,26 @@ __global__ __launch_bounds__(NW * 64) void lmhead_ks_kernel(LmArgs g) {
     }
   }
 
+  if (stage) {
+    // tile it's logit (row m, column c) sits at slog[it*ELEMS + (m&3)*64 + (m>>2)*16 + c]
+    __syncthreads();
+    const bool v4 = (g.V & 3) == 0;
+    for (int idx = tid; idx < nt * 64; idx += NW * 64) {
+      const int it = idx >> 6, m = (idx >> 2) & 15, c = (idx & 3) * 4;
+      const int n = ((int)blockIdx.x + it * G) * 16 + c;
+      if (m >= g.M) continue;
+      const float4 v = *reinterpret_cast<const float4*>(&slog[it * ELEMS + (m & 3) * 64 + (m >> 2) * 16 + c]);
+      float* dst = g.logits + (size_t)m * g.V + n;
+      if (v4 && n + 3 < g.V) {
+        *reinterpret_cast<float4*>(dst) = v;
+      } else {
+        if (n < g.V) dst[0] = v.x;
+        if (n + 1 < g.V) dst[1] = v.y;
+        if (n + 2 < g.V) dst[2] = v.z;
+        if (n + 3 < g.V) dst[3] = v.w;
+      }
+    }
+  }
   // a row's keys: 16 lanes (the tile's columns) of one wave
 #pragma unroll
   for (int r = 0; r < PER; ++r) {
