@@ -26,6 +26,10 @@ TINY = synth.CONFIGS["tiny"]
 SMALL_BF16 = TINY.with_(name="small_bf16", dtype="bf16", V=1000, H=520)
 MID_BF16 = TINY.with_(name="mid_bf16", dtype="bf16", V=2000, d=384, nh=3, H=520, c_prefill=300)
 WIDE_F32 = TINY.with_(name="wide_f32", V=1000, d=1152, nh=9)
+# 10,625 vocabulary tiles over 512 LM-head workgroups: 20 or 21 tiles each, so
+# the logits of one launch are written both ways (held in LDS up to 20 tiles,
+# stored tile by tile beyond)
+WIDEV_BF16 = TINY.with_(name="widev_bf16", dtype="bf16", V=170000, H=520)
 
 def _run_sample(cfg, tau, seed, B=1):
     cfg = cfg.with_(B=B)
@@ -41,10 +45,10 @@ def _run_sample(cfg, tau, seed, B=1):
     return cfg, w, feats, noise, dr, tok, logits, lse
 
 
-@pytest.mark.parametrize("cfg,B", [(TINY, 1), (SMALL_BF16, 1), (MID_BF16, 1), (WIDE_F32, 1), (TINY, 4),
-                                   (MID_BF16, 4), (WIDE_F32, 4)],
-                         ids=["tiny_f32", "small_bf16", "mid_bf16", "wide_f32", "tiny_tree", "mid_tree",
-                              "wide_tree"])
+@pytest.mark.parametrize("cfg,B", [(TINY, 1), (SMALL_BF16, 1), (MID_BF16, 1), (WIDE_F32, 1), (WIDEV_BF16, 1),
+                                   (TINY, 4), (MID_BF16, 4), (WIDE_F32, 4)],
+                         ids=["tiny_f32", "small_bf16", "mid_bf16", "wide_f32", "widev_bf16", "tiny_tree",
+                              "mid_tree", "wide_tree"])
 @pytest.mark.parametrize("tau", [0.6, 1.0])
 def test_draft_sample_matches_oracle(cfg, B, tau):
     seed = 1234 + B
