@@ -203,7 +203,7 @@ __global__ __launch_bounds__(NW * 64) void lmhead_kernel(LmArgs g) {
 // registers for the whole kernel (any number of rows up to 64, no z traffic in
 // the loop).  A workgroup takes tiles blockIdx, blockIdx+G, ... (a tile is 16
 // vocabulary rows, one contiguous stretch of W_lm); its waves stream their
-// chunks of the tile (the next tile's chunks in flight), multiply, and put
+// chunks of the tile (each next chunk in flight), multiply, and put
 // their partial tile into LDS (two buffers by tile parity, so one LDS barrier
 // per tile suffices); every thread then sums the waves in order for its fixed
 // output elements, updates its running key and writes the logit if asked.
@@ -258,31 +258,14 @@ __global__ __launch_bounds__(NW * 64) void lmhead_ks_kernel(LmArgs g) {
     ls[r] = 0.f;
   }
 
-  // chunks of tile it (of this workgroup); tiles past the end read row 0
-  auto load = [&](uint4 (&rb)[CPW][8], int it) {
+  // this wave's chunk u of tile it (of this workgroup); tiles past the end read row 0
+  auto load_chunk = [&](uint4 (&rb)[8], int it, int u) {
     const int t = (int)blockIdx.x + it * G;
-#pragma unroll
-    for (int u = 0; u < CPW; ++u) {
-      const int c = min(wave + u * NW, nch - 1);
-      chunk_load<T>(rb[u], W, g.d, t * 16, g.V, c * KC, g.d);
-    }
+    const int c = min(wave + u * NW, nch - 1);
+    chunk_load<T>(rb, W, g.d, t * 16, g.V, c * KC, g.d);
   };
-  auto process = [&](const uint4 (&rb)[CPW][8], int it) {
-    f32x4 acc[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int u = 0; u < CPW; ++u) {
-      chunk_to_lds(rb[u], wt);
-      wave_lds_sync();
-#pragma unroll
-      for (int st = 0; st < 8; ++st) {
-        const VT b = as_vec<T>(chunk_frag(wt, st));
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) mma(acc[mt], zf[u][mt][st], b);
-      }
-      wave_lds_sync();
-    }
+  // the waves' partial tile through LDS, then each thread's fixed outputs
+  auto finish = [&](f32x4 (&acc)[MT], int it) {
     float* rd = red[it & 1];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
@@ -304,17 +287,34 @@ __global__ __launch_bounds__(NW * 64) void lmhead_ks_kernel(LmArgs g) {
       }
     }
   };
-
-  uint4 r0[CPW][8], r1[CPW][8];
-  load(r0, 0);
-  for (int it = 0; it < nt; it += 2) {
-    load(r1, it + 1);
-    process(r0, it);
-    if (it + 1 < nt) {
-      load(r0, it + 2);
-      process(r1, it + 1);
+  // One register buffer: each chunk of the tile goes to the wave's LDS tile,
+  // the next tile's same chunk is issued into the freed registers, and the
+  // MFMAs read LDS meanwhile.  Two buffers made 64 rows spill (107.6 against
+  // 103.7 us) and were no faster at 16 rows.
+  auto process = [&](uint4 (&rb)[CPW][8], int it) {
+    f32x4 acc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < CPW; ++u) {
+      chunk_to_lds(rb[u], wt);
+      load_chunk(rb[u], it + 1, u);
+      wave_lds_sync();
+#pragma unroll
+      for (int st = 0; st < 8; ++st) {
+        const VT b = as_vec<T>(chunk_frag(wt, st));
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) mma(acc[mt], zf[u][mt][st], b);
+      }
+      wave_lds_sync();
     }
-  }
+    finish(acc, it);
+  };
+
+  uint4 r0[CPW][8];
+#pragma unroll
+  for (int u = 0; u < CPW; ++u) load_chunk(r0[u], 0, u);
+  for (int it = 0; it < nt; ++it) process(r0, it);
 
   if (stage) {
     // tile it's logit (row m, column c) sits at slog[it*ELEMS + (m&3)*64 + (m>>2)*16 + c]
