@@ -13,29 +13,35 @@
 // operands, one per column; E is read exactly once.
 //
 // Work split: a wave covers 16*VE columns; a workgroup's waves take
-// interleaved 4*VE-row chunks (next chunk in flight) of one row range.  The
-// S = S1*S2 row splits of a column block reduce in two levels of at most a few
-// arrivals each (a device-scope counter with many arrivals serialises): the
-// last of each group of S1 splits sums their partials, the last of the S2
-// groups sums the group sums, in order, and writes e and h.  Workgroups that
-// read the same x rows are placed on the same XCD (the hardware deals
-// workgroups round-robin over the 8 XCDs), so x is fetched once per XCD.
+// interleaved 4*VE-row chunks (next chunk in flight) of one row range.  A
+// column block's row splits reduce in two levels of at most a few arrivals
+// each (a device-scope counter with many arrivals serialises): the last of
+// each group of up to S1 splits sums their partials, the last of the groups
+// sums the group sums, in order, and writes e and h.  Column blocks get Sf
+// row splits, or Ss for the blocks with cb % 4 == 1: with 16 blocks of 256
+// bytes those stream about 20% slower (their offset in each 4 KB row of E),
+// so they get shorter row ranges and every workgroup finishes at about the
+// same time.  Workgroups that read the same x rows are placed on the same XCD
+// (the hardware deals workgroups round-robin over the 8 XCDs), so x is
+// fetched about once per XCD.
 #pragma once
 #include "common.hpp"
 #include "stream.hpp"
 
 namespace fm {
 
-constexpr int EMB_LEVEL_MAX = 4;  // splits per group and groups per column block
+constexpr int EMB_LEVEL_MAX = 5;  // splits per group and groups per column block
 
 struct EmbedArgs {
   const void* x;      // [M][ldx]
   int ldx, M, V;
   const void* E;      // [V][d]
   int d;
-  int S1, S2;         // splits of V: S = S1*S2 (multiple of 8), groups of S1
-  int rows_split;     // rows of V per split (multiple of 4*VE)
-  float* partial;     // [S][M][d]
+  int Sf, Ss;         // row splits of a column block (Ss for cb % 4 == 1, Ss >= Sf)
+  int S1, S2;         // splits per first-level group; most groups of a column block
+  int rows_split;     // rows of V per split with Sf splits (multiple of 4*VE)
+  int rows_split_s;   // the same with Ss splits
+  float* partial;     // [Ss][M][d]
   float* gpartial;    // [S2][M][d]
   uint32_t* counters; // n_cb*S2 first-level counters, then n_cb second-level
   float* e_state;     // [M][d] in/out
@@ -69,14 +75,26 @@ __global__ __launch_bounds__(NW * 64) void embed_kernel(EmbedArgs g) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int j = lane & 15, grp = lane >> 4;
   const int n_cb = g.d / COLS;
-  const int S = g.S1 * g.S2;
-  // XCD-aware placement: blocks bid, bid+8, ... run on one XCD
+  // XCD-aware placement: blocks bid, bid+8, ... run on one XCD, which takes
+  // consecutive entries e of the list (split 0 of every column block, split 1,
+  // ..., then the slow blocks' further splits); the grid is a multiple of 8
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-  const int cb = slot % n_cb;
-  const int s = (slot / n_cb) * 8 + xcd;
+  const int e = xcd * (int)(gridDim.x >> 3) + slot;
+  int cb, s;
+  if (e < g.Sf * n_cb) {
+    s = e / n_cb;
+    cb = e % n_cb;
+  } else {
+    const int e2 = e - g.Sf * n_cb, n_slow = n_cb / 4;
+    s = g.Sf + e2 / n_slow;
+    cb = 4 * (e2 % n_slow) + 1;
+  }
+  const bool slow = g.Ss > g.Sf && (cb & 3) == 1;
+  const int S_cb = slow ? g.Ss : g.Sf;
+  const int rows = slow ? g.rows_split_s : g.rows_split;
   const int c0 = cb * COLS;
-  const int v_begin = s * g.rows_split;
-  const int v_end = min(g.V, v_begin + g.rows_split);
+  const int v_begin = s * rows;
+  const int v_end = min(g.V, v_begin + rows);
   const T* X = reinterpret_cast<const T*>(g.x);
   const T* E = reinterpret_cast<const T*>(g.E);
 
@@ -169,23 +187,25 @@ __global__ __launch_bounds__(NW * 64) void embed_kernel(EmbedArgs g) {
     val[r] = el < ELEMS ? red[el] : 0.f;
     if (em[r] < g.M) st_coh(&g.partial[((size_t)s * g.M + em[r]) * g.d + ec[r]], val[r]);
   }
-  // level 1: the last of the S1 splits of this group sums them in order
+  // level 1: the last of the splits of this group sums them in order
   const int grp1 = s / g.S1;
-  if (!arrive(&g.counters[(cb * g.S2 + grp1) * COUNTER_STRIDE], (uint32_t)g.S1, &flag)) return;
+  const int n1 = min(g.S1, S_cb - grp1 * g.S1);  // splits in this group
+  const int n2 = (S_cb + g.S1 - 1) / g.S1;       // groups of this column block
+  if (!arrive(&g.counters[(cb * g.S2 + grp1) * COUNTER_STRIDE], (uint32_t)n1, &flag)) return;
 #pragma unroll
   for (int r = 0; r < PER_THREAD; ++r) {
     const bool ok = em[r] < g.M;
     float pv[EMB_LEVEL_MAX];
 #pragma unroll
     for (int q = 0; q < EMB_LEVEL_MAX; ++q)
-      pv[q] = (ok && q < g.S1) ? ld_coh(&g.partial[((size_t)(grp1 * g.S1 + q) * g.M + em[r]) * g.d + ec[r]]) : 0.f;
+      pv[q] = (ok && q < n1) ? ld_coh(&g.partial[((size_t)(grp1 * g.S1 + q) * g.M + em[r]) * g.d + ec[r]]) : 0.f;
     float v = 0.f;
 #pragma unroll
     for (int q = 0; q < EMB_LEVEL_MAX; ++q) v += pv[q];
     if (ok) st_coh(&g.gpartial[((size_t)grp1 * g.M + em[r]) * g.d + ec[r]], v);
   }
   // level 2: the last group sums the group sums in order and writes e and h
-  if (!arrive(&g.counters[(n_cb * g.S2 + cb) * COUNTER_STRIDE], (uint32_t)g.S2, &flag)) return;
+  if (!arrive(&g.counters[(n_cb * g.S2 + cb) * COUNTER_STRIDE], (uint32_t)n2, &flag)) return;
 #pragma unroll
   for (int r = 0; r < PER_THREAD; ++r) {
     const int m = em[r], c = ec[r];
@@ -193,7 +213,7 @@ __global__ __launch_bounds__(NW * 64) void embed_kernel(EmbedArgs g) {
     float pv[EMB_LEVEL_MAX];
 #pragma unroll
     for (int q = 0; q < EMB_LEVEL_MAX; ++q)
-      pv[q] = (ok && q < g.S2) ? ld_coh(&g.gpartial[((size_t)q * g.M + m) * g.d + c]) : 0.f;
+      pv[q] = (ok && q < n2) ? ld_coh(&g.gpartial[((size_t)q * g.M + m) * g.d + c]) : 0.f;
     if (!ok) continue;
     float v = 0.f;
 #pragma unroll
@@ -206,7 +226,6 @@ __global__ __launch_bounds__(NW * 64) void embed_kernel(EmbedArgs g) {
     g.h[o] = hv;
     if (g.hb) reinterpret_cast<T*>(g.hb)[o] = from_f32<T>(hv);
   }
-  (void)S;
 }
 
 }  // namespace fm
