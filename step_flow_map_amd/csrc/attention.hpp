@@ -261,8 +261,11 @@ __global__ __launch_bounds__(NW * 64) void attention_kernel(AttnArgs g) {
     sl[wave][j] = l_run;
   }
   __syncthreads();
+  // thread: row tid / TPR, columns c0 + c*TPR (c < CPT), so that each store
+  // and load below covers TPR consecutive floats of a row
   constexpr int CPT = KB * HD / (NW * 64);  // output columns per thread
-  const int row = tid / (HD / CPT), c0 = (tid % (HD / CPT)) * CPT;
+  constexpr int TPR = HD / CPT;             // threads per row
+  const int row = tid / TPR, c0 = tid % TPR;
   float M = -INFINITY;
 #pragma unroll
   for (int w = 0; w < NW; ++w) M = fmaxf(M, sm[w][row]);
@@ -275,18 +278,18 @@ __global__ __launch_bounds__(NW * 64) void attention_kernel(AttnArgs g) {
     const float wt = M == -INFINITY ? 0.f : expf(sm[w][row] - M);
     Lsum += wt * sl[w][row];
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) acc[c] += wt * so[w][row][c0 + c];
+    for (int c = 0; c < CPT; ++c) acc[c] += wt * so[w][row][c0 + c * TPR];
   }
   T* out = reinterpret_cast<T*>(g.out) + (size_t)(b * g.K + row) * g.d + head * HD + c0;
   if (g.n_ranges == 1) {
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) out[c] = from_f32<T>(acc[c] / Lsum);
+    for (int c = 0; c < CPT; ++c) out[c * TPR] = from_f32<T>(acc[c] / Lsum);
     return;
   }
   // ---- publish this range, the last range of the (branch, head) merges
   const size_t pbase = ((size_t)bh * g.n_ranges + range) * KB + row;
 #pragma unroll
-  for (int c = 0; c < CPT; ++c) st_coh(&g.part_o[pbase * HD + c0 + c], acc[c]);
+  for (int c = 0; c < CPT; ++c) st_coh(&g.part_o[pbase * HD + c0 + c * TPR], acc[c]);
   if (c0 == 0) {
     st_coh(&g.part_ml[pbase * 2 + 0], M);
     st_coh(&g.part_ml[pbase * 2 + 1], Lsum);
@@ -300,7 +303,7 @@ __global__ __launch_bounds__(NW * 64) void attention_kernel(AttnArgs g) {
     mv[r] = ok ? ld_coh(&g.part_ml[pi * 2]) : -INFINITY;
     lv[r] = ok ? ld_coh(&g.part_ml[pi * 2 + 1]) : 0.f;
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) ov[r][c] = ok ? ld_coh(&g.part_o[pi * HD + c0 + c]) : 0.f;
+    for (int c = 0; c < CPT; ++c) ov[r][c] = ok ? ld_coh(&g.part_o[pi * HD + c0 + c * TPR]) : 0.f;
   }
   float MM = -INFINITY;
 #pragma unroll
@@ -316,7 +319,7 @@ __global__ __launch_bounds__(NW * 64) void attention_kernel(AttnArgs g) {
     for (int c = 0; c < CPT; ++c) num[c] += wt * ov[r][c];
   }
 #pragma unroll
-  for (int c = 0; c < CPT; ++c) out[c] = from_f32<T>(num[c] / den);
+  for (int c = 0; c < CPT; ++c) out[c * TPR] = from_f32<T>(num[c] / den);
 }
 
 
