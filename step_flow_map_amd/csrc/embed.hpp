@@ -30,7 +30,8 @@
 
 namespace fm {
 
-constexpr int EMB_LEVEL_MAX = 5;  // splits per group and groups per column block
+constexpr int EMB_LEVEL_MAX = 5;   // splits per group and groups per column block
+constexpr int EMB_SPLITS_MAX = 19; // row splits of a column block
 
 struct EmbedArgs {
   const void* x;      // [M][ldx]
@@ -50,6 +51,7 @@ struct EmbedArgs {
   float alpha, beta;  // alpha == 0: e_state is not read
   int K;              // positions per branch (rows m use position m % K)
   int use_pos;
+  int sep;            // 1: partials only (plain stores); embed_reduce_kernel sums them
 };
 
 // P[k][c] = sin(k w_c) for c < d/2, cos(k w_{c-d/2}) otherwise,
@@ -190,8 +192,13 @@ __global__ __launch_bounds__(NW * 64) void embed_kernel(EmbedArgs g) {
     em[r] = el < ELEMS ? m : g.M;
     ec[r] = c0 + cl;
     val[r] = el < ELEMS ? red[((mt * VE + t) * 4 + i) * 64 + grp * 16 + j] : 0.f;
-    if (em[r] < g.M) st_coh(&g.partial[((size_t)s * g.M + em[r]) * g.d + ec[r]], val[r]);
+    if (g.sep) {
+      if (em[r] < g.M) g.partial[((size_t)s * g.M + em[r]) * g.d + ec[r]] = val[r];
+    } else if (em[r] < g.M) {
+      st_coh(&g.partial[((size_t)s * g.M + em[r]) * g.d + ec[r]], val[r]);
+    }
   }
+  if (g.sep) return;
   // level 1: the last of the splits of this group sums them in order
   const int grp1 = s / g.S1;
   const int n1 = min(g.S1, S_cb - grp1 * g.S1);  // splits in this group
@@ -231,6 +238,32 @@ __global__ __launch_bounds__(NW * 64) void embed_kernel(EmbedArgs g) {
     g.h[o] = hv;
     if (g.hb) reinterpret_cast<T*>(g.hb)[o] = from_f32<T>(hv);
   }
+}
+
+// The sum over a column block's row splits, in split order, and the epilogue
+// of embed_kernel (e, h and its copy in the storage type), one thread per
+// output; launched after embed_kernel with sep set (the kernel boundary orders
+// the partials' plain stores before these loads).
+template <typename T>
+__global__ __launch_bounds__(256) void embed_reduce_kernel(EmbedArgs g) {
+  constexpr int COLS = 16 * Vec<T>::N;
+  const int q = blockIdx.x * 256 + threadIdx.x;
+  if (q >= g.M * g.d) return;
+  const int m = q / g.d, c = q % g.d, cb = c / COLS;
+  const int S_cb = (g.Ss > g.Sf && (cb & 3) == 1) ? g.Ss : g.Sf;
+  // every split's load in flight at once, then the sum in split order
+  float pv[EMB_SPLITS_MAX];
+#pragma unroll
+  for (int s = 0; s < EMB_SPLITS_MAX; ++s) pv[s] = s < S_cb ? g.partial[((size_t)s * g.M + m) * g.d + c] : 0.f;
+  float v = 0.f;
+#pragma unroll
+  for (int s = 0; s < EMB_SPLITS_MAX; ++s) v += pv[s];
+  float e = g.beta * v;
+  if (g.alpha != 0.f) e += g.alpha * g.e_state[q];
+  g.e_state[q] = e;
+  const float hv = e + (g.use_pos ? pos_table(m % g.K, c, g.d) : 0.f);
+  g.h[q] = hv;
+  if (g.hb) reinterpret_cast<T*>(g.hb)[q] = from_f32<T>(hv);
 }
 
 }  // namespace fm

@@ -193,7 +193,7 @@ EmbedPlan plan_embed(int d, fm_dtype t, int M) {
     p.Sf = p.Ss = 16;
     p.S1 = 4;
   }
-  p.S = p.Ss;
+  p.S = p.Ss;  // at most EMB_SPLITS_MAX
   p.S2 = cdiv(p.S, p.S1);
   p.grid = p.n_cb * p.Sf + (p.Ss - p.Sf) * (p.n_cb / 4);
   return p;
@@ -516,8 +516,14 @@ fm_status ln_mod(fm_handle* h, const float* x, int rows, const float* shift, con
   return FM_OK;
 }
 
+fm_status probe_begin(fm_handle* h, int kernel, hipStream_t st);
+fm_status probe_end(fm_handle* h, int kernel, hipStream_t st);
+
+// probe: FM_PROBE_EMBED brackets embed_kernel alone (the kernel the counters
+// and the roofline describe); -1 records nothing
 template <typename T>
-fm_status embed(fm_handle* h, const void* x, int ldx, int M, float alpha, float beta, T* hb, hipStream_t st) {
+fm_status embed(fm_handle* h, const void* x, int ldx, int M, float alpha, float beta, T* hb, hipStream_t st,
+                int probe = -1) {
   const fm_config& c = h->cfg;
   if (M > 64) return fail(FM_EINVAL, "embedding contraction with %d rows exceeds 64", M);
   EmbedPlan p = plan_embed(c.d, c.dtype, M);
@@ -544,7 +550,10 @@ fm_status embed(fm_handle* h, const void* x, int ldx, int M, float alpha, float 
   a.beta = beta;
   a.K = KB;
   a.use_pos = 1;
+  a.sep = 1;
+  if (p.S > EMB_SPLITS_MAX) return fail(FM_EINVAL, "embedding with %d row splits (at most %d)", p.S, EMB_SPLITS_MAX);
   const dim3 grid(p.grid), block(EMB_WAVES * 64);
+  FM_TRY(probe_begin(h, probe, st));
   switch (p.MT) {
     case 1: hipLaunchKernelGGL((embed_kernel<T, 1, EMB_WAVES>), grid, block, 0, st, a); break;
     case 2: hipLaunchKernelGGL((embed_kernel<T, 2, EMB_WAVES>), grid, block, 0, st, a); break;
@@ -552,6 +561,11 @@ fm_status embed(fm_handle* h, const void* x, int ldx, int M, float alpha, float 
     default: hipLaunchKernelGGL((embed_kernel<T, 4, EMB_WAVES>), grid, block, 0, st, a); break;
   }
   FM_LAUNCHED("embed_kernel");
+  FM_TRY(probe_end(h, probe, st));
+  if (a.sep) {
+    hipLaunchKernelGGL((embed_reduce_kernel<T>), dim3(cdiv(M * c.d, 256)), dim3(256), 0, st, a);
+    FM_LAUNCHED("embed_reduce_kernel");
+  }
   return FM_OK;
 }
 
@@ -829,9 +843,7 @@ fm_status draft_impl(fm_handle* h, const void* noise, int B, const void* new_fea
     const float s = h->times[j], t = h->times[j + 1];
     const float* mods = mods_all + (size_t)j * (6 * L + 2) * d;
     if (j == 0) {
-      FM_TRY(probe_begin(h, FM_PROBE_EMBED, st));
-      FM_TRY(embed<T>(h, noise, c.V, Mb, 0.f, 1.f, hb, st));
-      FM_TRY(probe_end(h, FM_PROBE_EMBED, st));
+      FM_TRY(embed<T>(h, noise, c.V, Mb, 0.f, 1.f, hb, st, FM_PROBE_EMBED));
     } else {
       const float sp = h->times[j - 1];
       FM_TRY(embed<T>(h, h->at<T>(h->lay.dsoft), c.V, Mb, (1.f - s) / (1.f - sp), (s - sp) / (1.f - sp), hb, st));
