@@ -267,8 +267,10 @@ fm_status fm_verify_sample(fm_handle *h, const void *target_logits, fm_dtype dty
 /* Kernels a probe can bracket. */
 typedef enum fm_probe_kernel {
   FM_PROBE_NONE = 0,
-  FM_PROBE_EMBED = 1,    /* noise-block embedding contraction (first jump)    */
-  FM_PROBE_LM_HEAD = 2,  /* LM head + fused argmax (last jump)                */
+  FM_PROBE_EMBED = 1,    /* noise-block embedding kernel (first jump; without
+                            its split-sum kernel)                             */
+  FM_PROBE_LM_HEAD = 2,  /* LM head kernel with fused per-workgroup argmax keys
+                            (last jump; without the merge of those keys)      */
   FM_PROBE_FC1 = 3,      /* first MLP contraction of block 0 (first jump)     */
   FM_PROBE_VERIFY = 4    /* unused by fm_draft; reserved                      */
 } fm_probe_kernel;

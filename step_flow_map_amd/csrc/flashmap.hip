@@ -647,9 +647,11 @@ struct Sampling {
   float* lse;  // [M]
 };
 
+// probe: FM_PROBE_LM_HEAD brackets the LM head kernel alone (not the argmax
+// merge); -1 records nothing
 template <typename T>
 fm_status lm_head(fm_handle* h, const void* z, int M, float* logits, int32_t* tokens, hipStream_t st,
-                  const Sampling* smp = nullptr) {
+                  const Sampling* smp = nullptr, int probe = -1) {
   const fm_config& c = h->cfg;
   LmArgs a{};
   a.tau = smp ? smp->tau : 0.f;
@@ -673,6 +675,7 @@ fm_status lm_head(fm_handle* h, const void* z, int M, float* logits, int32_t* to
   const int grid = ks ? std::min(mt == 1 ? LM_GRID : LM_GRID / 2, cdiv(c.V, 16))
                       : std::min(LM_GRID / 2, cdiv(cdiv(c.V, 16), LM_WAVES));
   const dim3 block(LM_WAVES * 64);
+  FM_TRY(probe_begin(h, probe, st));
   if (ks) {
     switch (mt * 8 + cpw) {
       case 9: hipLaunchKernelGGL((lmhead_ks_kernel<T, 1, LM_WAVES, 1>), dim3(grid), block, 0, st, a); break;
@@ -695,6 +698,7 @@ fm_status lm_head(fm_handle* h, const void* z, int M, float* logits, int32_t* to
     }
     FM_LAUNCHED("lmhead_kernel");
   }
+  FM_TRY(probe_end(h, probe, st));
   if (tokens) {
     hipLaunchKernelGGL(argmax_finalize_kernel, dim3(M), dim3(FIN_THREADS), 0, st, a.partial, grid, tokens,
                        a.lse_part, smp ? smp->lse : nullptr);
@@ -929,9 +933,7 @@ fm_status draft_impl(fm_handle* h, const void* noise, int B, const void* new_fea
     const float* fin = mods + (size_t)6 * L * d;  // shift_f, scale_f
     if (!ln_in_reduce) FM_TRY(ln_mod<T>(h, hres, Mb, fin, fin + d, act_d, d, st));
     if (t == 1.f) {
-      FM_TRY(probe_begin(h, FM_PROBE_LM_HEAD, st));
-      FM_TRY(lm_head<T>(h, act_d, Mb, logits, tokens, st, smp));
-      FM_TRY(probe_end(h, FM_PROBE_LM_HEAD, st));
+      FM_TRY(lm_head<T>(h, act_d, Mb, logits, tokens, st, smp, FM_PROBE_LM_HEAD));
     } else {
       FM_TRY(lm_head<T>(h, act_d, Mb, h->at<float>(h->lay.logits_tmp), nullptr, st));
       FM_TRY(softmax_rows<T>(h, Mb, st));
