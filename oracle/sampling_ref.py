@@ -7,10 +7,10 @@ it shares no code with it.
 Sources.  The pages require a separate "probabilistic" draft-sampling mode for
 requests sampled at temperature above 0 and report results at temperatures 0
 and 1 (feinterview.poetries.top, the deployment list of the last section;
-wire.sakhanda.co, "Как развернуть FlashMap?").  The alphasignal.ai page ("Why
-drafting still costs time") defines lossless verification as keeping the
-target model's output distribution under the same sampling settings.  The pages
-give no rule beyond that.  READING: the standard speculative-sampling rule.
+wire.sakhanda.co, "Как развернуть FlashMap?").  By the alphasignal.ai page
+("Why drafting still costs time"), verification is lossless when it leaves the
+distribution of the target's samples unchanged.  The pages give no rule beyond
+that.  READING: the standard speculative-sampling rule.
   - Drafts: at temperature tau every block row i is sampled independently from
     q_i = softmax(l_i / tau), where l_i are the drafter's float32 logits of the
     last jump.

@@ -46,6 +46,24 @@ def test_philox_rounds_invert():
         assert _philox_inverse(out, seed) == [int(x) for x in ctr]
 
 
+def test_philox_known_answer_vectors():
+    """The generator's published known-answer vectors (tests/golden/
+    philox4x32_10_kat.json): zero counter and key, all-ones counter and key,
+    and the hexadecimal digits of pi.  A wrong multiplier, Weyl constant,
+    round count or word order changes every output word."""
+    import json
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", "philox4x32_10_kat.json")
+    with open(path) as f:
+        kat = json.load(f)
+    assert len(kat["cases"]) == 3
+    for case in kat["cases"]:
+        ctr = np.array([int(x, 16) for x in case["counter"]], dtype=np.uint64)
+        k0, k1 = (int(x, 16) for x in case["key"])
+        out = S.philox4x32_10(ctr[None, :], k0 | (k1 << 32))[0]
+        assert [int(x) for x in out] == [int(x, 16) for x in case["output"]], case
+
+
 def test_philox_output_is_uniform_and_decorrelated():
     n = 1 << 17
     ctr = np.zeros((n, 4), dtype=np.uint64)
