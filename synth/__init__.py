@@ -13,7 +13,9 @@ scaled, then rounded to nearest-even bfloat16 for bf16 workloads):
   chunks of ``CHUNK`` elements, chunk ``c`` from seed ``[0, i, c]``, std 0.02;
 * context features ``[C][5][H]``: seed ``[1, c]`` per chunk, std 1 (request r > 0
   of a batch of requests: seed ``[4, r, c]``);
-* noise block of branch ``b`` ``[K][V]``: seed ``[2, b, c]``, std 1;
+* noise block of branch ``b`` ``[K][V]``: seed ``[2, b, c]``, std 1; a parity
+  test that meets a near-tie re-runs on the next draw k = 1, 2, ..., seed
+  ``[6, k, b, c]``;
 * target logits of branch ``b`` ``[K+1][V]``: seed ``[3, b, c]``, std 1.
 
 Shapes follow the drafter the pages describe (a 6-block DiT of width 2048 with
@@ -231,11 +233,12 @@ def make_features(cfg: Config, rows: int | None = None, request: int = 0) -> np.
         return _draw([1] if request == 0 else [4, request], (rows, N_CTX_LAYERS, cfg.H), 1.0, cfg.dtype, pool)
 
 
-def make_noise(cfg: Config, B: int | None = None) -> np.ndarray:
-    """Gaussian noise blocks [B][K][V], N(0,1); branch b from seed [2, b]."""
+def make_noise(cfg: Config, B: int | None = None, draw: int = 0) -> np.ndarray:
+    """Gaussian noise blocks [B][K][V], N(0,1); branch b from seed [2, b], or
+    from seed [6, draw, b] for a later draw (draw >= 1)."""
     B = cfg.B if B is None else B
     with ThreadPoolExecutor(_workers()) as pool:
-        return np.stack([_draw([2, b], (cfg.K, cfg.V), 1.0, cfg.dtype, pool)
+        return np.stack([_draw([2, b] if draw == 0 else [6, draw, b], (cfg.K, cfg.V), 1.0, cfg.dtype, pool)
                          for b in range(B)])
 
 

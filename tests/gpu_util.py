@@ -15,8 +15,17 @@ S = oracle.sampling
 LOGIT_RTOL = 2e-2
 # residual stream after every block, same norm-wise measure
 HIDDEN_RTOL = 2e-2
-# a draft token may differ from the oracle's only where the oracle's gap between
-# the two candidates is within NEAR_TIE_FACTOR x the row's measured logit error
+# Regression bound on the same row-wise measure, beside the 2e-2 contract: a
+# kernel that drifts toward the contract fails here first.
+LOGIT_REGRESS = {"f32": 1e-5, "bf16": 5e-3}
+# Fixed logit-error figures, measured once over the random-weight variants of
+# every parity case (row-wise relative error at most 6e-7 in float32 and
+# 1.5e-3 in bf16).  They size the near-tie window; a row's own error never does.
+TIE_ERR = {"f32": 1e-6, "bf16": 2e-3}
+# A draft token may differ from the oracle's only where the oracle's gap between
+# the two candidates is within NEAR_TIE_FACTOR x TIE_ERR x max |ref| of that row.
+# Such a near-tie is reported; at most one is allowed per case, and the case is
+# then run again on the next noise draw, which must match exactly.
 NEAR_TIE_FACTOR = 4.0
 
 
@@ -67,8 +76,13 @@ def rowwise_rel_err(got: np.ndarray, ref: np.ndarray) -> np.ndarray:
     return np.abs(got - ref).max(axis=1) / np.maximum(np.abs(ref).max(axis=1), 1e-30)
 
 
-def check_tokens(tok_gpu, logits_gpu, ref_logits, ref_tok):
-    """Exact token parity, except near-ties (reported).  Also: each GPU token is
+def tie_window(ref_row: np.ndarray, dtype: str) -> float:
+    """Absolute near-tie window of one row of oracle logits."""
+    return NEAR_TIE_FACTOR * TIE_ERR[dtype] * float(np.abs(ref_row).max())
+
+
+def check_tokens(tok_gpu, logits_gpu, ref_logits, ref_tok, dtype):
+    """Exact token parity, except near-ties (returned).  Also: each GPU token is
     the lowest-index argmax of the GPU's own float32 logits, always."""
     tok_gpu = tok_gpu.reshape(-1)
     lg = logits_gpu.reshape(-1, logits_gpu.shape[-1])
@@ -79,25 +93,50 @@ def check_tokens(tok_gpu, logits_gpu, ref_logits, ref_tok):
     ties = []
     for r in range(tok_gpu.shape[0]):
         if tok_gpu[r] != rt[r]:
-            err = np.abs(lg[r].astype(np.float64) - lr[r]).max()
-            gap = lr[r][rt[r]] - lr[r][tok_gpu[r]]
-            assert gap <= NEAR_TIE_FACTOR * err, (
-                f"row {r}: token {tok_gpu[r]} vs oracle {rt[r]}, oracle gap {gap:.3e} > "
-                f"{NEAR_TIE_FACTOR} x logit error {err:.3e}")
-            ties.append((r, float(gap), float(err)))
+            gap = float(lr[r][rt[r]] - lr[r][tok_gpu[r]])
+            win = tie_window(lr[r], dtype)
+            assert gap <= win, (
+                f"row {r}: token {tok_gpu[r]} vs oracle {rt[r]}, oracle gap {gap:.3e} outside the "
+                f"near-tie window {win:.3e}")
+            ties.append((r, gap, win))
     return ties
 
 
+def check_logits(logits_gpu, ref_logits, dtype, what=""):
+    """Row-wise relative error within the contract and the regression bound;
+    returns the largest."""
+    rel = rowwise_rel_err(logits_gpu, ref_logits)
+    assert rel.max() <= LOGIT_RTOL, f"{what} logit error {rel.max():.3e} above {LOGIT_RTOL}"
+    assert rel.max() <= LOGIT_REGRESS[dtype], (
+        f"{what} logit error {rel.max():.3e} above the regression bound {LOGIT_REGRESS[dtype]}")
+    return float(rel.max())
+
+
+def exact_or_reseed(case, label=""):
+    """Token parity over noise draws.  case(draw) runs one parity case on noise
+    draw `draw` (checking everything else itself) and returns its near-ties.
+    Draw 0 may have at most one; if it has one, the case runs again on draw 1,
+    which must match the oracle exactly."""
+    ties = case(0)
+    if not ties:
+        return
+    assert len(ties) == 1, f"{label}: {len(ties)} near-ties on draw 0 (at most one per case): {ties}"
+    print(f"  {label}: near-tie {ties[0]} on draw 0; running draw 1", flush=True)
+    again = case(1)
+    assert not again, f"{label}: near-tie again on draw 1: {again}"
+
+
 def check_draft(cfg, w, noise, feats, prefill, tok, logits, hidden=None, times=None):
+    """Every branch against the oracle's draft of it: logits (contract and
+    regression bound), the embedding state, tokens.  Returns (largest logit
+    error, near-ties)."""
     W = oracle.Weights.from_storage(w)
     rel_max = 0.0
     all_ties = []
     for b in range(noise.shape[0]):
         ref = oracle.draft(W, cfg, noise[b], feats, times=times)
-        rel = rowwise_rel_err(logits[b], ref["logits"])
-        assert rel.max() <= LOGIT_RTOL, f"branch {b}: logit error {rel.max():.3e}"
-        rel_max = max(rel_max, float(rel.max()))
-        all_ties += check_tokens(tok[b], logits[b], ref["logits"], ref["tokens"])
+        rel_max = max(rel_max, check_logits(logits[b], ref["logits"], cfg.dtype, f"branch {b}:"))
+        all_ties += [(b,) + t for t in check_tokens(tok[b], logits[b], ref["logits"], ref["tokens"], cfg.dtype)]
         if hidden is not None:
             for j, jt in enumerate(ref["jumps"]):
                 e = rowwise_rel_err(hidden[j, 0, b], jt["h0"])
@@ -118,8 +157,11 @@ def _sample_keys(logits_row, tau, seed, row, branch):
     return logits_row.astype(np.float64) / tau + S.gumbel(np.arange(V), row, branch, S.STREAM_DRAFT, seed)
 
 
-def check_sampled_tokens(tok, logits_gpu, ref_logits, tau, seed):
-    """tok [B][K]; logits [B][K][V]; returns the near-ties."""
+def check_sampled_tokens(tok, logits_gpu, ref_logits, tau, seed, dtype):
+    """tok [B][K]; logits [B][K][V]; returns the near-ties.  Every GPU token is
+    the Gumbel-max winner of the GPU's own logits (up to float32 rounding of
+    the key); it equals the oracle's sample except where the oracle's two best
+    keys lie within the fixed near-tie window divided by tau."""
     ties = []
     B, K, _ = logits_gpu.shape
     for b in range(B):
@@ -131,10 +173,10 @@ def check_sampled_tokens(tok, logits_gpu, ref_logits, tau, seed):
             ref = _sample_keys(ref_logits[b][i], tau, seed, i, b)
             r = int(np.flatnonzero(ref == ref.max())[0])
             if t != r:
-                err = np.abs(logits_gpu[b, i].astype(np.float64) - ref_logits[b][i]).max() / tau
-                gap = ref[r] - ref[t]
-                assert gap <= NEAR_TIE_FACTOR * err + eps, (b, i, t, r, gap, err)
-                ties.append((b, i, float(gap)))
+                win = tie_window(ref_logits[b][i], dtype) / tau + eps
+                gap = float(ref[r] - ref[t])
+                assert gap <= win, (b, i, t, r, gap, win)
+                ties.append((b, i, gap, win))
     return ties
 
 

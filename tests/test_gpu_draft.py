@@ -11,7 +11,7 @@ import synth
 pytestmark = pytest.mark.gpu
 
 fm = pytest.importorskip("step_flow_map_amd")
-from gpu_util import check_draft, make_drafter, run_draft, rowwise_rel_err, to_dev  # noqa: E402
+from gpu_util import check_draft, exact_or_reseed, make_drafter, run_draft, rowwise_rel_err, to_dev  # noqa: E402
 
 TINY = synth.CONFIGS["tiny"]
 # bf16 with ragged vocabulary (1000 = 62.5 column tiles, 31.25 row chunks) and
@@ -30,10 +30,10 @@ WIDE_F32 = TINY.with_(name="wide_f32", V=1000, d=1152, nh=9)
 W2048_BF16 = TINY.with_(name="w2048_bf16", dtype="bf16", V=2000, d=2048, nh=16, H=520, c_prefill=40)
 
 
-def _case(cfg, variant="random", B=1, seed_noise=None):
+def _case(cfg, variant="random", B=1, draw=0):
     w = synth.make_weights(cfg, variant)
     feats = synth.make_features(cfg)
-    noise = synth.make_noise(cfg, B)
+    noise = synth.make_noise(cfg, B, draw)
     return w, feats, noise
 
 
@@ -42,18 +42,26 @@ def _case(cfg, variant="random", B=1, seed_noise=None):
 @pytest.mark.parametrize("variant", ["random", "unit_gate", "gate_zero"])
 def test_draft_matches_oracle(cfg, variant):
     print(f"[draft parity] {cfg.name} {variant}", flush=True)
-    w, feats, noise = _case(cfg, variant)
+    w = synth.make_weights(cfg, variant)
+    feats = synth.make_features(cfg)
+    W = oracle.Weights.from_storage(w)
     dr = make_drafter(cfg, w)
     dr.set_schedule(cfg.times)
-    tok, logits, hidden = run_draft(dr, cfg, noise, feats, cfg.c_prefill, want_hidden=True)
-    rel, ties = check_draft(cfg, w, noise, feats, cfg.c_prefill, tok, logits, hidden)
-    print(f"  max row logit error {rel:.2e}, near-ties {ties}")
-    # per-block residual stream
-    W = oracle.Weights.from_storage(w)
-    ref = oracle.draft(W, cfg, noise[0], feats, trace=True)
-    for l, blk in enumerate(ref["jumps"][0]["blocks"]):
-        e = rowwise_rel_err(hidden[0, l + 1, 0], blk["h"])
-        assert e.max() < 2e-2, (l, e.max())
+
+    def case(draw):
+        noise = synth.make_noise(cfg, 1, draw)
+        dr.truncate(0)
+        tok, logits, hidden = run_draft(dr, cfg, noise, feats, cfg.c_prefill, want_hidden=True)
+        rel, ties = check_draft(cfg, w, noise, feats, cfg.c_prefill, tok, logits, hidden)
+        print(f"  draw {draw}: max row logit error {rel:.2e}, near-ties {ties}")
+        # per-block residual stream
+        ref = oracle.draft(W, cfg, noise[0], feats, trace=True)
+        for l, blk in enumerate(ref["jumps"][0]["blocks"]):
+            e = rowwise_rel_err(hidden[0, l + 1, 0], blk["h"])
+            assert e.max() < 2e-2, (l, e.max())
+        return ties
+
+    exact_or_reseed(case, f"{cfg.name} {variant}")
 
 
 def test_context_paths_agree():
@@ -78,12 +86,17 @@ def test_context_paths_agree():
 
 def test_empty_context_and_no_new_rows():
     cfg = SMALL_BF16.with_(c_prefill=0, n_new=0)
-    w, _, noise = _case(cfg)
+    w = synth.make_weights(cfg)
     feats = np.zeros((0, 5, cfg.H), dtype=np.uint16)
     dr = make_drafter(cfg, w, C_max=8)
     dr.set_schedule(cfg.times)
-    tok, logits, _ = run_draft(dr, cfg, noise, feats, 0)
-    check_draft(cfg, w, noise, feats, 0, tok, logits)
+
+    def case(draw):
+        noise = synth.make_noise(cfg, 1, draw)
+        tok, logits, _ = run_draft(dr, cfg, noise, feats, 0)
+        return check_draft(cfg, w, noise, feats, 0, tok, logits)[1]
+
+    exact_or_reseed(case, "empty context")
 
 
 @pytest.mark.parametrize("cfg", [SMALL_BF16, W2048_BF16], ids=["small_bf16", "w2048_bf16"])
@@ -122,29 +135,39 @@ def test_errors_enqueue_nothing():
     assert e.value.status == fm.FM_ECAPACITY
 
 
+def _parity(cfg, label, B=1, variant="random", after=None):
+    """Draft B branches on each noise draw the re-seed rule asks for and check
+    them against the oracle (residual stream after every block included);
+    after(dr, noise, tok, logits), if given, adds checks of that draw."""
+    w = synth.make_weights(cfg, variant)
+    feats = synth.make_features(cfg)
+    dr = make_drafter(cfg, w)
+    dr.set_schedule(cfg.times)
+
+    def case(draw):
+        noise = synth.make_noise(cfg, B, draw)
+        dr.truncate(0)
+        tok, logits, hidden = run_draft(dr, cfg, noise, feats, cfg.c_prefill, want_hidden=True)
+        rel, ties = check_draft(cfg, w, noise, feats, cfg.c_prefill, tok, logits, hidden)
+        print(f"  {label} draw {draw}: logit error {rel:.2e}, near-ties {ties}", flush=True)
+        if after is not None:
+            after(w, feats, noise, tok, logits)
+        return ties
+
+    exact_or_reseed(case, label)
+
+
 @pytest.mark.parametrize("cfg", [TINY, SMALL_BF16, MID_BF16, W2048_BF16],
                          ids=["tiny_f32", "small_bf16", "mid_bf16", "w2048_bf16"])
 def test_two_step_schedule(cfg):
-    cfg = cfg.with_(times=(0.0, 0.5, 1.0))
-    w, feats, noise = _case(cfg)
-    dr = make_drafter(cfg, w)
-    dr.set_schedule(cfg.times)
-    tok, logits, hidden = run_draft(dr, cfg, noise, feats, cfg.c_prefill, want_hidden=True)
-    rel, ties = check_draft(cfg, w, noise, feats, cfg.c_prefill, tok, logits, hidden)
-    print(f"  2-step {cfg.name}: logit error {rel:.2e}, near-ties {ties}")
+    _parity(cfg.with_(times=(0.0, 0.5, 1.0)), f"2-step {cfg.name}")
 
 
 def test_draft_tree_of_three_at_width_2048():
     """Three bf16 branches at the drafter's real width: 48 block rows (plus 8
     appended context rows in QKV), so the contractions keep the rows' k slice
     in LDS (three and four row tiles) and sum the slices in a second pass."""
-    cfg = W2048_BF16.with_(name="w2048_tree3", B=3)
-    w, feats, noise = _case(cfg, B=3)
-    dr = make_drafter(cfg, w)
-    dr.set_schedule(cfg.times)
-    tok, logits, hidden = run_draft(dr, cfg, noise, feats, cfg.c_prefill, want_hidden=True)
-    rel, ties = check_draft(cfg, w, noise, feats, cfg.c_prefill, tok, logits, hidden)
-    print(f"  tree of 3 at d 2048: logit error {rel:.2e}, near-ties {ties}")
+    _parity(W2048_BF16.with_(name="w2048_tree3", B=3), "tree of 3 at d 2048", B=3)
 
 
 @pytest.mark.parametrize("prefill", [0, 24, 25, 142, 1500])
@@ -155,30 +178,23 @@ def test_tree_shared_context_lengths(prefill):
     blocks (three per range: a range whose second step has one stream idle),
     and 48 blocks over 12 ranges (merged by a separate pass)."""
     cfg = MID_BF16.with_(name=f"mid_tree_c{prefill}", B=4, c_prefill=prefill)
-    w, feats, noise = _case(cfg, B=4)
-    dr = make_drafter(cfg, w)
-    dr.set_schedule(cfg.times)
-    tok, logits, hidden = run_draft(dr, cfg, noise, feats, cfg.c_prefill, want_hidden=True)
-    rel, ties = check_draft(cfg, w, noise, feats, cfg.c_prefill, tok, logits, hidden)
-    print(f"  tree C {cfg.C}: logit error {rel:.2e}, near-ties {ties}")
+    _parity(cfg, f"tree C {cfg.C}", B=4)
 
 
 @pytest.mark.parametrize("cfg", [TINY, SMALL_BF16, MID_BF16, WIDE_F32, W2048_BF16],
                          ids=["tiny_f32", "small_bf16", "mid_bf16", "wide_f32", "w2048_bf16"])
 def test_draft_tree_of_four(cfg):
     cfg = cfg.with_(B=4)
-    w, feats, noise = _case(cfg, B=4)
-    dr = make_drafter(cfg, w)
-    dr.set_schedule(cfg.times)
-    tok, logits, hidden = run_draft(dr, cfg, noise, feats, cfg.c_prefill, want_hidden=True)
-    rel, ties = check_draft(cfg, w, noise, feats, cfg.c_prefill, tok, logits, hidden)
-    print(f"  tree {cfg.name}: logit error {rel:.2e}, near-ties {ties}")
-    # the branches are independent: branch 2 alone gives the same draft.  The
-    # two paths round differently (alone, the fused LayerNorms read h rounded
-    # to bf16; a tree normalises the float32 rows), each within the parity
-    # bound above; a branch seeing another's rows would differ by far more
-    dr1 = make_drafter(cfg.with_(B=1), w)
-    dr1.set_schedule(cfg.times)
-    t1, l1, _ = run_draft(dr1, cfg.with_(B=1), noise[2:3], feats, cfg.c_prefill)
-    assert np.array_equal(t1[0], tok[2])
-    assert rowwise_rel_err(l1[0], logits[2]).max() <= 5e-3
+
+    def branch_alone(w, feats, noise, tok, logits):
+        # the branches are independent: branch 2 alone gives the same draft,
+        # up to the rounding order of the two launch shapes; a branch seeing
+        # another's rows would differ by far more
+        one = cfg.with_(B=1)
+        dr1 = make_drafter(one, w)
+        dr1.set_schedule(one.times)
+        t1, l1, _ = run_draft(dr1, one, noise[2:3], feats, one.c_prefill)
+        assert np.array_equal(t1[0], tok[2])
+        assert rowwise_rel_err(l1[0], logits[2]).max() <= 5e-3
+
+    _parity(cfg, f"tree {cfg.name}", B=4, after=branch_alone)

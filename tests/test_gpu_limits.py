@@ -13,7 +13,7 @@ import synth
 pytestmark = pytest.mark.gpu
 
 fm = pytest.importorskip("step_flow_map_amd")
-from gpu_util import check_draft, make_drafter, run_draft, to_dev  # noqa: E402
+from gpu_util import check_draft, exact_or_reseed, make_drafter, run_draft, to_dev  # noqa: E402
 
 TINY = synth.CONFIGS["tiny"]
 WIDEST = TINY.with_(name="widest_bf16", dtype="bf16", V=1000, d=4096, nh=32, H=520, L=1, c_prefill=24, n_new=16)
@@ -26,12 +26,18 @@ def _draft_parity(cfg, B=1, C_max=None):
     print(f"[limits] {cfg.name} B={B}", flush=True)
     w = synth.make_weights(cfg)
     feats = synth.make_features(cfg)
-    noise = synth.make_noise(cfg, B)
     dr = make_drafter(cfg, w, C_max=C_max)
     dr.set_schedule(cfg.times)
-    tok, logits, _ = run_draft(dr, cfg, noise, feats, cfg.c_prefill)
-    rel, ties = check_draft(cfg, w, noise, feats, cfg.c_prefill, tok, logits)
-    print(f"  logit error {rel:.2e}, near-ties {ties}", flush=True)
+
+    def case(draw):
+        noise = synth.make_noise(cfg, B, draw)
+        dr.truncate(0)
+        tok, logits, _ = run_draft(dr, cfg, noise, feats, cfg.c_prefill)
+        rel, ties = check_draft(cfg, w, noise, feats, cfg.c_prefill, tok, logits)
+        print(f"  draw {draw}: logit error {rel:.2e}, near-ties {ties}", flush=True)
+        return ties
+
+    exact_or_reseed(case, f"{cfg.name} B={B}")
     return dr
 
 
