@@ -145,6 +145,10 @@ def main():
     ap.add_argument("--config", default="qwen3_8b", choices=sorted(synth.CONFIGS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="time eager calls instead of graph replays")
+    ap.add_argument("--cycle", action="store_true",
+                    help="replay one graph of draft + verify without resetting the context, which then grows "
+                         "by the appended rows every step (the speculative loop) from the workload's prefill; "
+                         "the capacity covers every replay")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only copy this many bytes device to device five times and exit (the plain copy "
                          "kernel that calibrates the FETCH_SIZE / WRITE_SIZE counters)")
@@ -191,7 +195,9 @@ def main():
     dev = torch.device("cuda", 0)
     R = cfg.requests
     NB = cfg.B * R   # row blocks
-    c = fm.make_config(K=cfg.K, V=cfg.V, d=cfg.d, L=cfg.L, n_heads=cfg.nh, H=cfg.H, C_max=cfg.capacity,
+    n_replays = len(synth.PLANTED_ACCEPT) + args.warmup + args.steps + 1
+    C_max = cfg.c_prefill + n_replays * cfg.n_new + cfg.n_new if args.cycle else cfg.capacity
+    c = fm.make_config(K=cfg.K, V=cfg.V, d=cfg.d, L=cfg.L, n_heads=cfg.nh, H=cfg.H, C_max=C_max,
                        dtype=cfg.dtype, max_branches=cfg.B, max_new=max(R * cfg.n_new, 1),
                        max_steps=cfg.num_steps, max_requests=R)
     dr = fm.Drafter(c, binding_weights(w))
@@ -259,15 +265,28 @@ def main():
 
     stream = torch.cuda.current_stream()
     graphs = []
-    if not args.eager:
+    if args.cycle:
+        # one graph, no reset: every replay appends n_new rows to each context
+        T, seed, _ = sets[0]
+        step(T, seed)   # warm the path outside capture
+        torch.cuda.synchronize()
+        for r in range(R):
+            dr.truncate_req(r, cfg.c_prefill)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            draft_and_verify(T, seed)
+        dr.sync_context()
+        graphs = [g] * len(sets)
+    elif not args.eager:
+        # a graph per target set; each replay first resets the device-resident
+        # context length (a captured write), so every step appends the same rows
+        # and attends over the same context
         for T, seed, _ in sets:
             step(T, seed)   # warm the path outside capture
             torch.cuda.synchronize()
             g = torch.cuda.CUDAGraph()
-            for r in range(R):
-                dr.truncate_req(r, cfg.c_prefill)
             with torch.cuda.graph(g):
-                draft_and_verify(T, seed)
+                step(T, seed)
             graphs.append(g)
         torch.cuda.synchronize()
 
@@ -295,6 +314,13 @@ def main():
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
+    ctx_range = None
+    if args.cycle:
+        dr.sync_context()
+        ctx_end = dr.context_length_req(0)
+        ctx_range = [ctx_end - (args.steps - 1) * cfg.n_new, ctx_end]   # rows seen by the first and last timed step
+        for r in range(R):
+            dr.truncate_req(r, cfg.c_prefill)
 
     # live per-kernel durations: events around the kernel's launch, eager calls
     kernels = {}
@@ -338,7 +364,8 @@ def main():
                    "heads": cfg.nh, "H": cfg.H, "context": cfg.C, "new_rows_per_step": cfg.n_new,
                    "branches": cfg.B, "requests": R, "schedule": list(cfg.times),
                    "temperature": cfg.temperature,
-                   "replay": "eager" if args.eager else "hipgraph"},
+                   "replay": "eager" if args.eager else "hipgraph"}
+                  | ({"context_grows": True, "context_timed": ctx_range} if args.cycle else {}),
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": kd["gbs"], "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": kd["gbs"] / HBM_PEAK_GBS, "traffic": traffic,
                      "alg_bytes_per_launch": kd["alg_bytes"], "us_per_launch": kd["us"]},

@@ -21,8 +21,9 @@
  *     comment says "host".  They must stay valid until the stream reaches the
  *     call (weights: for the handle's lifetime).
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
- *     Calls only enqueue work; they never synchronize and never allocate
- *     device memory, so a draft+verify sequence can be captured in a HIP graph.
+ *     Calls only enqueue work (fm_create and fm_context_sync also wait); they
+ *     never allocate device memory, so a draft+verify sequence can be captured
+ *     in a HIP graph, and replays of it follow the growing context.
  *   - Every argument check runs on the host before anything is enqueued.  On
  *     an error status nothing has been enqueued and no output was written;
  *     fm_last_error() describes the failure (thread-local string).
@@ -141,27 +142,46 @@ fm_status fm_set_weights(fm_handle *h, const fm_weights *w);
  * (order, num_steps outside 1..max_steps), FM_ESTATE (no weights), FM_EHIP. */
 fm_status fm_set_schedule(fm_handle *h, const float *times, int num_steps, void *stream);
 
+/* Context length.  Each request's length lives on the device, in the
+ * workspace: kernels read it when the stream reaches them, and the calls that
+ * append rows (fm_context_append, fm_draft, fm_draft_sample, fm_draft_batch)
+ * advance it in their last kernel.  A captured HIP graph of a draft therefore
+ * appends its rows and attends over the grown context on every replay (the
+ * pages' cycle appends rows every cycle: alphasignal.ai, "Why drafting still
+ * costs time").  The host keeps a mirror, advanced by the calls it sees (not by
+ * replays), for the argument checks; fm_context_sync reloads it.  On the
+ * device an append never passes C_max: the length stops there, rows past it
+ * are not written, and a flag reports it to fm_context_sync. */
+
 /* Append n rows of target hidden states to the context (prefill, or rows
  * accepted outside fm_draft).  feats: [n][n_ctx_layers][H], layers in the
  * order 1, 9, 17, 25, 33 (feinterview.poetries.top, second section).  For
  * each row: u = LN(W_f concat(feats) + b_f); for each block the row's key and
- * value (W_k u + b_k, W_v u + b_v) are written to the cache.  Errors:
- * FM_EINVAL, FM_ECAPACITY (length + n > C_max), FM_ESTATE, FM_EHIP. */
+ * value (W_k u + b_k, W_v u + b_v) are written to the cache at the device
+ * length and on.  Errors: FM_EINVAL, FM_ECAPACITY (mirror length + n >
+ * C_max), FM_ESTATE, FM_EHIP. */
 fm_status fm_context_append(fm_handle *h, const void *feats, int n, void *stream);
 
 /* Roll the context back (or forward over rows already written) to new_len
- * rows: host bookkeeping only, nothing is enqueued.  Errors: FM_EINVAL
- * (new_len < 0 or new_len > the highest row ever written). */
-fm_status fm_context_truncate(fm_handle *h, int new_len);
+ * rows: enqueues the write of the device length on `stream` and sets the
+ * mirror.  Errors: FM_EINVAL (new_len < 0 or new_len > the highest row the
+ * host has seen written), FM_EHIP. */
+fm_status fm_context_truncate(fm_handle *h, int new_len, void *stream);
 
-/* Current context length (rows), or -1 for a NULL handle. */
+/* Current context length (rows) of the host mirror, or -1 for a NULL handle. */
 int fm_context_length(const fm_handle *h);
+
+/* Wait for `stream`, then load the device lengths of every request into the
+ * host mirror (after graph replays).  Not for use inside a graph capture.
+ * Errors: FM_EINVAL, FM_EHIP, FM_ECAPACITY (an append on the device reached
+ * C_max and dropped rows since the last sync; the flag is then cleared). */
+fm_status fm_context_sync(fm_handle *h, void *stream);
 
 /* The same three calls for request `req` (0 <= req < max_requests) of a
  * handle that holds several requests; the calls above act on request 0.
  * Errors as above, plus FM_EINVAL for req out of range (length: -1). */
 fm_status fm_context_append_req(fm_handle *h, int req, const void *feats, int n, void *stream);
-fm_status fm_context_truncate_req(fm_handle *h, int req, int new_len);
+fm_status fm_context_truncate_req(fm_handle *h, int req, int new_len, void *stream);
 int fm_context_length_req(const fm_handle *h, int req);
 
 /* One drafting step (feinterview.poetries.top, first section: the same noise
@@ -181,9 +201,11 @@ int fm_context_length_req(const fm_handle *h, int req);
  * attention of the block rows over [context; own block] keys, MLP), final
  * LN/modulation, logits = z W_lm^T; at t = 1 the tokens are the row argmax
  * of the float32 logits (lowest index among equal maxima); before t = 1 the
- * state moves by the flow map of the linear interpolant.  The context length
- * advances by n_new.  Errors: FM_EINVAL, FM_ECAPACITY, FM_ESTATE (no weights
- * or no schedule), FM_EHIP. */
+ * state moves by the flow map of the linear interpolant.  The new rows go to
+ * the cache at the device length, the block rows attend over that length +
+ * n_new rows, and the device length then advances by n_new (the mirror at
+ * once).  Errors: FM_EINVAL, FM_ECAPACITY (mirror length + n_new > C_max),
+ * FM_ESTATE (no weights or no schedule), FM_EHIP. */
 fm_status fm_draft(fm_handle *h, const void *noise, int B, const void *new_feats, int n_new,
                    int32_t *tokens, float *logits, float *hidden, void *stream);
 
@@ -240,8 +262,8 @@ fm_status fm_verify(const void *target_logits, fm_dtype dtype, int B, int K, int
                     void *stream);
 
 /* Probabilistic verification at temperature > 0 (alphasignal.ai, "Why
- * drafting still costs time": lossless = the target's output distribution is
- * kept under the same sampling settings).  The speculative-sampling rule, with
+ * drafting still costs time": lossless verification leaves the distribution
+ * of the target's samples unchanged).  The speculative-sampling rule, with
  * p_j = softmax(target_logits_j / temperature) and q_i the drafter's
  * distribution (draft_logits_i / temperature normalised by draft_lse_i):
  *   draft i is accepted while u_i * q_i(d_i) < p_i(d_i), u_i the uniform of

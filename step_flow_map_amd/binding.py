@@ -70,13 +70,15 @@ def lib() -> ctypes.CDLL:
     L.fm_set_schedule.restype = st
     L.fm_context_append.argtypes = [vp, vp, i, vp]
     L.fm_context_append.restype = st
-    L.fm_context_truncate.argtypes = [vp, i]
+    L.fm_context_truncate.argtypes = [vp, i, vp]
     L.fm_context_truncate.restype = st
+    L.fm_context_sync.argtypes = [vp, vp]
+    L.fm_context_sync.restype = st
     L.fm_context_length.argtypes = [vp]
     L.fm_context_length.restype = i
     L.fm_context_append_req.argtypes = [vp, i, vp, i, vp]
     L.fm_context_append_req.restype = st
-    L.fm_context_truncate_req.argtypes = [vp, i, i]
+    L.fm_context_truncate_req.argtypes = [vp, i, i, vp]
     L.fm_context_truncate_req.restype = st
     L.fm_context_length_req.argtypes = [vp, i]
     L.fm_context_length_req.restype = i
@@ -179,8 +181,12 @@ def fm_context_append(h, feats, stream=None):
     _check(lib().fm_context_append(h, _ptr(feats), n, _stream(stream)))
 
 
-def fm_context_truncate(h, new_len: int):
-    _check(lib().fm_context_truncate(h, int(new_len)))
+def fm_context_truncate(h, new_len: int, stream=None):
+    _check(lib().fm_context_truncate(h, int(new_len), _stream(stream)))
+
+
+def fm_context_sync(h, stream=None):
+    _check(lib().fm_context_sync(h, _stream(stream)))
 
 
 def fm_context_length(h) -> int:
@@ -192,8 +198,8 @@ def fm_context_append_req(h, req: int, feats, stream=None):
     _check(lib().fm_context_append_req(h, int(req), _ptr(feats), n, _stream(stream)))
 
 
-def fm_context_truncate_req(h, req: int, new_len: int):
-    _check(lib().fm_context_truncate_req(h, int(req), int(new_len)))
+def fm_context_truncate_req(h, req: int, new_len: int, stream=None):
+    _check(lib().fm_context_truncate_req(h, int(req), int(new_len), _stream(stream)))
 
 
 def fm_context_length_req(h, req: int) -> int:
@@ -285,14 +291,17 @@ class Drafter:
     def append(self, feats, stream=None):
         fm_context_append(self.handle, feats, stream)
 
-    def truncate(self, n):
-        fm_context_truncate(self.handle, n)
+    def truncate(self, n, stream=None):
+        fm_context_truncate(self.handle, n, stream)
+
+    def sync_context(self, stream=None):
+        fm_context_sync(self.handle, stream)
 
     def append_req(self, req, feats, stream=None):
         fm_context_append_req(self.handle, req, feats, stream)
 
-    def truncate_req(self, req, n):
-        fm_context_truncate_req(self.handle, req, n)
+    def truncate_req(self, req, n, stream=None):
+        fm_context_truncate_req(self.handle, req, n, stream)
 
     def context_length_req(self, req):
         return fm_context_length_req(self.handle, req)

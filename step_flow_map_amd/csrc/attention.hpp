@@ -35,7 +35,6 @@ namespace fm {
 
 constexpr int ATT_RANGES_MAX = 8;  // ranges per (branch, head) = arrivals per counter
 constexpr int ATT_TREE_RANGES = 16;  // ranges per head of attention_tree_kernel (no counter)
-constexpr int FM_MAX_REQ = 4;      // requests with their own context in one launch
 constexpr int ATT_BLK = 32;        // keys per block
 constexpr int KB_ROWS = 16;        // block rows (queries) per branch
 
@@ -53,19 +52,59 @@ struct AttnArgs {
   const void* vt;      // this DiT block's value cache [nh][P/32][hd][32] (request 0)
   size_t req_stride;   // elements between consecutive requests' caches
   int P;               // positions per head (multiple of 32)
-  int C[FM_MAX_REQ];   // context rows visible to branch b
+  const int* ctx_len;  // device: context length of each request before this call
+  int n_new[FM_MAX_REQ];  // rows this call appends for branch b's request
+  int ctx_cap;         // cache capacity (C_max): visible rows never exceed it
   int scratch_blk;     // block index of the first block rows
   int scratch_step;    // 1: branches share request 0's cache (branch b at scratch_blk + b);
                        // 0: branch b is request b (its rows at scratch_blk of its own cache)
   int K, d, nh;
-  int n_ranges;        // ranges per (branch, head), <= 8
-  int blocks_per_range;
+  int n_ranges;        // range slots per (branch, head) in the grid (at most ATT_RANGES_MAX,
+                       // or ATT_TREE_RANGES for the tree kernel); the ranges in use are
+                       // planned on the device from the visible context
   float* part_o;       // [B*nh][n_ranges][K][HD]
   float* part_ml;      // [B*nh][n_ranges][K][2]
   uint32_t* counters;  // [B*nh], COUNTER_STRIDE apart
   void* out;           // [B*K][d]
   float scale;         // 1/sqrt(hd)
 };
+
+// Context rows branch b sees: its request's length when the stream reaches the
+// call (device-resident, so one captured graph stays valid as the context
+// grows) plus the rows the call appends, clipped to the cache capacity.
+__device__ __forceinline__ int visible_ctx(const AttnArgs& g, int b) {
+  const int req = g.scratch_step ? 0 : b;
+  return min(g.ctx_len[req] + g.n_new[b], g.ctx_cap);
+}
+
+// Key ranges of attention_kernel for n_blocks 32-key blocks of one (branch,
+// head) over workgroups of nw waves: about one block a wave (all of a wave's
+// loads in flight at once), but at most 6 ranges, since every further arrival
+// at the merge costs more than a second block per wave (measured at 18 and 66
+// blocks).  The same plan runs on the host (grid size, for the capacity) and
+// on the device (the ranges in use, for the current length).
+__host__ __device__ inline int attn_max_ranges(int n_blocks, int nw) {
+  const int r = (n_blocks + nw - 1) / nw;
+  return r < 6 ? (r < 1 ? 1 : r) : (6 < ATT_RANGES_MAX ? 6 : ATT_RANGES_MAX);
+}
+__host__ __device__ inline void attn_plan(int n_blocks, int nw, int& n_ranges, int& per_range) {
+  const int r = attn_max_ranges(n_blocks, nw);
+  per_range = (n_blocks + r - 1) / r;
+  n_ranges = (n_blocks + per_range - 1) / per_range;
+}
+// the same for attention_tree_kernel over ctx_blocks context blocks (at least
+// one range, which also serves the branches' own rows)
+__host__ __device__ inline int tree_max_ranges(int ctx_blocks) {
+  const int r = (ctx_blocks + 3) / 4;
+  return r < 1 ? 1 : (r < ATT_TREE_RANGES ? r : ATT_TREE_RANGES);
+}
+__host__ __device__ inline void tree_plan(int ctx_blocks, int& n_ranges, int& per_range) {
+  const int r = tree_max_ranges(ctx_blocks);
+  per_range = (ctx_blocks + r - 1) / r;
+  if (per_range < 1) per_range = 1;
+  n_ranges = (ctx_blocks + per_range - 1) / per_range;
+  if (n_ranges < 1) n_ranges = 1;
+}
 
 // One wave's 16 queries against one 32-key block (nv valid keys): transposed
 // scores by MFMA, online softmax per query row (running max and sum, the
@@ -197,11 +236,14 @@ __global__ __launch_bounds__(NW * 64) void attention_kernel(AttnArgs g) {
   const int range = blockIdx.x % g.n_ranges;
   const int bh = blockIdx.x / g.n_ranges;
   const int head = bh % g.nh, b = bh / g.nh;
-  const int C = g.C[b];
+  const int C = visible_ctx(g, b);
   const int ctx_blocks = (C + ATT_BLK - 1) / ATT_BLK;
   const int nblk = ctx_blocks + 1;
-  const int blo = range * g.blocks_per_range;
-  const int bhi = min(nblk, blo + g.blocks_per_range);  // empty for ranges past a short context
+  int n_ranges, per_range;
+  attn_plan(nblk, NW, n_ranges, per_range);
+  if (range >= n_ranges) return;  // a slot the current length does not use
+  const int blo = range * per_range;
+  const int bhi = min(nblk, blo + per_range);
   const size_t rb = g.scratch_step ? 0 : (size_t)b * g.req_stride;
   const T* kbase = reinterpret_cast<const T*>(g.kc) + rb + (size_t)head * g.P * HD;
   const T* vbase = reinterpret_cast<const T*>(g.vt) + rb + (size_t)head * (g.P / ATT_BLK) * HD * ATT_BLK;
@@ -281,7 +323,7 @@ __global__ __launch_bounds__(NW * 64) void attention_kernel(AttnArgs g) {
     for (int c = 0; c < CPT; ++c) acc[c] += wt * so[w][row][c0 + c * TPR];
   }
   T* out = reinterpret_cast<T*>(g.out) + (size_t)(b * g.K + row) * g.d + head * HD + c0;
-  if (g.n_ranges == 1) {
+  if (n_ranges == 1) {
 #pragma unroll
     for (int c = 0; c < CPT; ++c) out[c * TPR] = from_f32<T>(acc[c] / Lsum);
     return;
@@ -294,11 +336,11 @@ __global__ __launch_bounds__(NW * 64) void attention_kernel(AttnArgs g) {
     st_coh(&g.part_ml[pbase * 2 + 0], M);
     st_coh(&g.part_ml[pbase * 2 + 1], Lsum);
   }
-  if (!arrive(&g.counters[bh * COUNTER_STRIDE], (uint32_t)g.n_ranges, &flag)) return;
+  if (!arrive(&g.counters[bh * COUNTER_STRIDE], (uint32_t)n_ranges, &flag)) return;
   float mv[ATT_RANGES_MAX], lv[ATT_RANGES_MAX], ov[ATT_RANGES_MAX][CPT];
 #pragma unroll
   for (int r = 0; r < ATT_RANGES_MAX; ++r) {
-    const bool ok = r < g.n_ranges;
+    const bool ok = r < n_ranges;
     const size_t pi = ((size_t)bh * g.n_ranges + (ok ? r : 0)) * KB + row;
     mv[r] = ok ? ld_coh(&g.part_ml[pi * 2]) : -INFINITY;
     lv[r] = ok ? ld_coh(&g.part_ml[pi * 2 + 1]) : 0.f;
@@ -313,7 +355,7 @@ __global__ __launch_bounds__(NW * 64) void attention_kernel(AttnArgs g) {
   for (int c = 0; c < CPT; ++c) num[c] = 0.f;
 #pragma unroll
   for (int r = 0; r < ATT_RANGES_MAX; ++r) {
-    const float wt = r < g.n_ranges ? expf(mv[r] - MM) : 0.f;
+    const float wt = r < n_ranges ? expf(mv[r] - MM) : 0.f;
     den += wt * lv[r];
 #pragma unroll
     for (int c = 0; c < CPT; ++c) num[c] += wt * ov[r][c];
@@ -363,10 +405,13 @@ __global__ __launch_bounds__(512) void attention_tree_kernel(AttnArgs g) {
   const int j = lane & 15, grp = lane >> 4;
   const int range = blockIdx.x % g.n_ranges, head = blockIdx.x / g.n_ranges;
   const int b = wave / WPB, stream = wave % WPB;
-  const int C = g.C[0];
+  const int C = visible_ctx(g, 0);
   const int ctx_blocks = (C + ATT_BLK - 1) / ATT_BLK;
-  const int blo = min(ctx_blocks, range * g.blocks_per_range);
-  const int bhi = min(ctx_blocks, blo + g.blocks_per_range);
+  int n_ranges, per_range;
+  tree_plan(ctx_blocks, n_ranges, per_range);
+  if (range >= n_ranges) return;  // a slot the current length does not use
+  const int blo = min(ctx_blocks, range * per_range);
+  const int bhi = min(ctx_blocks, blo + per_range);
   const int n_steps = (bhi - blo + WPB - 1) / WPB;
   const T* kbase = reinterpret_cast<const T*>(g.kc) + (size_t)head * g.P * HD;
   const T* vbase = reinterpret_cast<const T*>(g.vt) + (size_t)head * (g.P / ATT_BLK) * HD * ATT_BLK;
@@ -462,7 +507,7 @@ __global__ __launch_bounds__(512) void attention_tree_kernel(AttnArgs g) {
     }
   }
   // the branch's own block rows: the last range, the branch's stream-0 wave
-  if (range == g.n_ranges - 1 && stream == 0) {
+  if (range == n_ranges - 1 && stream == 0) {
     Tile t;
     const int pb = g.scratch_blk + b;
 #pragma unroll
@@ -515,7 +560,7 @@ __global__ __launch_bounds__(512) void attention_tree_kernel(AttnArgs g) {
     Mr[row] = M;
     Lr[row] = Lsum;
   }
-  if (g.n_ranges == 1) {
+  if (n_ranges == 1) {
     if (col_ok) {
 #pragma unroll
       for (int row = 0; row < KB_ROWS; ++row) {
@@ -560,14 +605,17 @@ __global__ __launch_bounds__(HD) void attention_merge_kernel(AttnArgs g) {
   const int col = threadIdx.x;
   const int bh = blockIdx.x / (KB_ROWS / RG), row0 = (blockIdx.x % (KB_ROWS / RG)) * RG;
   const int b = bh / g.nh, head = bh % g.nh;
+  int n_ranges, per_range;
+  tree_plan((visible_ctx(g, 0) + ATT_BLK - 1) / ATT_BLK, n_ranges, per_range);
+  if (n_ranges == 1) return;  // attention_tree_kernel wrote the output itself
   // the rows' (max, sum) of every range: one pair per thread, through LDS
   {
     const int i = col / ATT_TREE_RANGES, r = col % ATT_TREE_RANGES;
     if (i < RG) {
-      const size_t pr = ((size_t)bh * g.n_ranges + (r < g.n_ranges ? r : 0)) * KB_ROWS + row0 + i;
+      const size_t pr = ((size_t)bh * g.n_ranges + (r < n_ranges ? r : 0)) * KB_ROWS + row0 + i;
       const float2 ml = reinterpret_cast<const float2*>(g.part_ml)[pr];
       // a range past n_ranges (or one without blocks, M = -inf) gets weight 0
-      sml[i][r] = make_float2(r < g.n_ranges ? ml.x : -INFINITY, ml.y);
+      sml[i][r] = make_float2(r < n_ranges ? ml.x : -INFINITY, ml.y);
     }
   }
   float ov[RG][ATT_TREE_RANGES];
@@ -575,7 +623,7 @@ __global__ __launch_bounds__(HD) void attention_merge_kernel(AttnArgs g) {
   for (int i = 0; i < RG; ++i)
 #pragma unroll
     for (int r = 0; r < ATT_TREE_RANGES; ++r) {
-      const size_t pr = ((size_t)bh * g.n_ranges + (r < g.n_ranges ? r : 0)) * KB_ROWS + row0 + i;
+      const size_t pr = ((size_t)bh * g.n_ranges + (r < n_ranges ? r : 0)) * KB_ROWS + row0 + i;
       ov[i][r] = g.part_o[pr * HD + col];
     }
   __syncthreads();

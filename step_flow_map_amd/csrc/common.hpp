@@ -17,6 +17,8 @@
 
 namespace fm {
 
+constexpr int FM_MAX_REQ = 4;  // requests with their own context in one launch
+
 typedef uint16_t bf16_t;
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));

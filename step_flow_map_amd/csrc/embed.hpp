@@ -1,8 +1,7 @@
 // Noise-block embedding contraction of the flow-map jump:
 //
 //   e[m][c] = alpha * e[m][c] + beta * sum_v x[m][v] * E[v][c]
-//   h[m][c] = e[m][c] + P[m % K][c]        (float32, and optionally a copy in
-//                                         the storage type)
+//   h[m][c] = e[m][c] + P[m % K][c]        (float32)
 //
 // x is the block state over the vocabulary ([M][V]: Gaussian noise at s = 0,
 // the denoiser's softmax before a later jump), E the frozen embedding [V][d]
@@ -13,11 +12,11 @@
 // operands, one per column; E is read exactly once.
 //
 // Work split: a wave covers 16*VE columns; a workgroup's waves take
-// interleaved 4*VE-row chunks (next chunk in flight) of one row range.  A
-// column block's row splits reduce in two levels of at most a few arrivals
-// each (a device-scope counter with many arrivals serialises): the last of
-// each group of up to S1 splits sums their partials, the last of the groups
-// sums the group sums, in order, and writes e and h.  Column blocks get Sf
+// interleaved 4*VE-row chunks (next chunk in flight) of one row range (a
+// "split" of V), sum their accumulators through LDS in wave order and store
+// the split's float32 partial with plain stores.  embed_reduce_kernel,
+// launched next, sums a column block's splits in split order and writes e
+// and h, so the result never depends on scheduling.  Column blocks get Sf
 // row splits, or Ss for the blocks with cb % 4 == 1: with 16 blocks of 256
 // bytes those stream about 20% slower (their offset in each 4 KB row of E),
 // so they get shorter row ranges and every workgroup finishes at about the
@@ -30,7 +29,6 @@
 
 namespace fm {
 
-constexpr int EMB_LEVEL_MAX = 5;   // splits per group and groups per column block
 constexpr int EMB_SPLITS_MAX = 19; // row splits of a column block
 
 struct EmbedArgs {
@@ -39,19 +37,14 @@ struct EmbedArgs {
   const void* E;      // [V][d]
   int d;
   int Sf, Ss;         // row splits of a column block (Ss for cb % 4 == 1, Ss >= Sf)
-  int S1, S2;         // splits per first-level group; most groups of a column block
   int rows_split;     // rows of V per split with Sf splits (multiple of 4*VE)
   int rows_split_s;   // the same with Ss splits
   float* partial;     // [Ss][M][d]
-  float* gpartial;    // [S2][M][d]
-  uint32_t* counters; // n_cb*S2 first-level counters, then n_cb second-level
   float* e_state;     // [M][d] in/out
   float* h;           // [M][d] out
-  void* hb;           // [M][d] out in the storage type, or null
   float alpha, beta;  // alpha == 0: e_state is not read
   int K;              // positions per branch (rows m use position m % K)
   int use_pos;
-  int sep;            // 1: partials only (plain stores); embed_reduce_kernel sums them
 };
 
 // P[k][c] = sin(k w_c) for c < d/2, cos(k w_{c-d/2}) otherwise,
@@ -72,7 +65,6 @@ __global__ __launch_bounds__(NW * 64) void embed_kernel(EmbedArgs g) {
   constexpr int COLS = 16 * VE; // columns per wave
   constexpr int ELEMS = MT * VE * 4 * 64;
   __shared__ float red[ELEMS];
-  __shared__ int flag;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int j = lane & 15, grp = lane >> 4;
@@ -92,7 +84,6 @@ __global__ __launch_bounds__(NW * 64) void embed_kernel(EmbedArgs g) {
     cb = 4 * (e2 % n_slow) + 1;
   }
   const bool slow = g.Ss > g.Sf && (cb & 3) == 1;
-  const int S_cb = slow ? g.Ss : g.Sf;
   const int rows = slow ? g.rows_split_s : g.rows_split;
   const int c0 = cb * COLS;
   const int v_begin = s * rows;
@@ -176,74 +167,25 @@ __global__ __launch_bounds__(NW * 64) void embed_kernel(EmbedArgs g) {
     }
     __syncthreads();
   }
-  constexpr int PER_THREAD = (ELEMS + NW * 64 - 1) / (NW * 64);
-  int em[PER_THREAD], ec[PER_THREAD];
-  float val[PER_THREAD];
   // thread element el = row el / COLS, column el % COLS: consecutive lanes
-  // take consecutive columns, so the partial stores and loads below coalesce
-  // into whole row segments (lane-strided 4-byte stores each made a
-  // transaction of their own: 20 MB of writes for 3 MB of partials)
+  // take consecutive columns, so the partial stores coalesce into whole row
+  // segments (lane-strided 4-byte stores each made a transaction of their own)
+  constexpr int PER_THREAD = (ELEMS + NW * 64 - 1) / (NW * 64);
 #pragma unroll
   for (int r = 0; r < PER_THREAD; ++r) {
     const int el = threadIdx.x + r * NW * 64;
     const int cl = el % COLS, m = el / COLS;
     // the MFMA output acc[mt][t][i] of lane (grp, j) is row mt*16 + 4*grp + i, column j*VE + t
     const int j = cl / VE, t = cl % VE, mt = m >> 4, grp = (m & 15) >> 2, i = m & 3;
-    em[r] = el < ELEMS ? m : g.M;
-    ec[r] = c0 + cl;
-    val[r] = el < ELEMS ? red[((mt * VE + t) * 4 + i) * 64 + grp * 16 + j] : 0.f;
-    if (g.sep) {
-      if (em[r] < g.M) g.partial[((size_t)s * g.M + em[r]) * g.d + ec[r]] = val[r];
-    } else if (em[r] < g.M) {
-      st_coh(&g.partial[((size_t)s * g.M + em[r]) * g.d + ec[r]], val[r]);
-    }
-  }
-  if (g.sep) return;
-  // level 1: the last of the splits of this group sums them in order
-  const int grp1 = s / g.S1;
-  const int n1 = min(g.S1, S_cb - grp1 * g.S1);  // splits in this group
-  const int n2 = (S_cb + g.S1 - 1) / g.S1;       // groups of this column block
-  if (!arrive(&g.counters[(cb * g.S2 + grp1) * COUNTER_STRIDE], (uint32_t)n1, &flag)) return;
-#pragma unroll
-  for (int r = 0; r < PER_THREAD; ++r) {
-    const bool ok = em[r] < g.M;
-    float pv[EMB_LEVEL_MAX];
-#pragma unroll
-    for (int q = 0; q < EMB_LEVEL_MAX; ++q)
-      pv[q] = (ok && q < n1) ? ld_coh(&g.partial[((size_t)(grp1 * g.S1 + q) * g.M + em[r]) * g.d + ec[r]]) : 0.f;
-    float v = 0.f;
-#pragma unroll
-    for (int q = 0; q < EMB_LEVEL_MAX; ++q) v += pv[q];
-    if (ok) st_coh(&g.gpartial[((size_t)grp1 * g.M + em[r]) * g.d + ec[r]], v);
-  }
-  // level 2: the last group sums the group sums in order and writes e and h
-  if (!arrive(&g.counters[(n_cb * g.S2 + cb) * COUNTER_STRIDE], (uint32_t)n2, &flag)) return;
-#pragma unroll
-  for (int r = 0; r < PER_THREAD; ++r) {
-    const int m = em[r], c = ec[r];
-    const bool ok = m < g.M;
-    float pv[EMB_LEVEL_MAX];
-#pragma unroll
-    for (int q = 0; q < EMB_LEVEL_MAX; ++q)
-      pv[q] = (ok && q < n2) ? ld_coh(&g.gpartial[((size_t)q * g.M + m) * g.d + c]) : 0.f;
-    if (!ok) continue;
-    float v = 0.f;
-#pragma unroll
-    for (int q = 0; q < EMB_LEVEL_MAX; ++q) v += pv[q];
-    const size_t o = (size_t)m * g.d + c;
-    float e = g.beta * v;
-    if (g.alpha != 0.f) e += g.alpha * g.e_state[o];
-    g.e_state[o] = e;
-    const float hv = e + (g.use_pos ? pos_table(m % g.K, c, g.d) : 0.f);
-    g.h[o] = hv;
-    if (g.hb) reinterpret_cast<T*>(g.hb)[o] = from_f32<T>(hv);
+    if (el < ELEMS && m < g.M)
+      g.partial[((size_t)s * g.M + m) * g.d + c0 + cl] = red[((mt * VE + t) * 4 + i) * 64 + grp * 16 + j];
   }
 }
 
-// The sum over a column block's row splits, in split order, and the epilogue
-// of embed_kernel (e, h and its copy in the storage type), one thread per
-// output; launched after embed_kernel with sep set (the kernel boundary orders
-// the partials' plain stores before these loads).
+// The sum over a column block's row splits, in split order, and the state
+// update: e = alpha e + beta sum, h = e + P, one thread per output; launched
+// after embed_kernel (the kernel boundary orders the partials' plain stores
+// before these loads).
 template <typename T>
 __global__ __launch_bounds__(256) void embed_reduce_kernel(EmbedArgs g) {
   constexpr int COLS = 16 * Vec<T>::N;
@@ -263,7 +205,6 @@ __global__ __launch_bounds__(256) void embed_reduce_kernel(EmbedArgs g) {
   g.e_state[q] = e;
   const float hv = e + (g.use_pos ? pos_table(m % g.K, c, g.d) : 0.f);
   g.h[q] = hv;
-  if (g.hb) reinterpret_cast<T*>(g.hb)[q] = from_f32<T>(hv);
 }
 
 }  // namespace fm

@@ -173,11 +173,11 @@ bool resid_ln_fused(int M, int N, int K, fm_dtype t) {
 }
 
 struct EmbedPlan {
-  int MT, n_cb, Sf, Ss, S, S1, S2, grid;
+  int MT, n_cb, Sf, Ss, grid;
 };
 
-// Column blocks of 16*VE columns and S = S1*S2 = 16 splits of V (a multiple of
-// 8 for the XCD placement); splits without rows still arrive.
+// Column blocks of 16*VE columns, each over Sf row splits of V (Ss for the
+// slower blocks; the grid is a multiple of 8 for the XCD placement).
 EmbedPlan plan_embed(int d, fm_dtype t, int M) {
   EmbedPlan p;
   p.MT = cdiv(M, 16);
@@ -188,30 +188,10 @@ EmbedPlan plan_embed(int d, fm_dtype t, int M) {
     // (256 workgroups, finishing together; 100 against 94 us streaming alone)
     p.Sf = 15;
     p.Ss = 19;
-    p.S1 = 5;
   } else {
     p.Sf = p.Ss = 16;
-    p.S1 = 4;
   }
-  p.S = p.Ss;  // at most EMB_SPLITS_MAX
-  p.S2 = cdiv(p.S, p.S1);
   p.grid = p.n_cb * p.Sf + (p.Ss - p.Sf) * (p.n_cb / 4);
-  return p;
-}
-
-struct AttnPlan {
-  int n_ranges, blocks_per_range;
-};
-
-// n_blocks 32-key blocks of one (branch, head) over ranges of a workgroup of
-// ATT_WAVES waves: about one block a wave (all of a wave's loads in flight at
-// once), but at most 6 ranges, since every further arrival at the merge costs
-// more than a second block per wave (measured at 18 and 66 blocks)
-AttnPlan plan_attention(int n_blocks) {
-  AttnPlan p;
-  const int r = std::min(std::min(6, ATT_MAX_RANGES), cdiv(n_blocks, ATT_WAVES));
-  p.blocks_per_range = cdiv(n_blocks, r);
-  p.n_ranges = cdiv(n_blocks, p.blocks_per_range);
   return p;
 }
 
@@ -223,7 +203,7 @@ int cache_positions(const fm_config& c) { return cdiv(c.C_max, ATT_BLK) * ATT_BL
 int max_blocks(const fm_config& c) { return std::max(c.max_branches, c.max_requests); }
 
 struct Layout {
-  size_t cache, mods, sched, h, hb, e_state, u_pre, act_qkv, act_d, attn_o, act_f, qkv;
+  size_t cache, mods, sched, ctx, h, e_state, u_pre, act_qkv, act_d, attn_o, act_f, qkv;
   size_t att_po, att_ml, partial, lm_part, lm_lse, counters, dsoft, logits_tmp, sm_part, vs_stats, vs_lse, vs_n,
       vs_keys, total;
 };
@@ -247,7 +227,7 @@ size_t partial_bytes(const fm_config& c) {
     }
   for (int M = 16; M <= Mb; M += 16) {
     EmbedPlan e = plan_embed(c.d, c.dtype, M);
-    mx = std::max(mx, (size_t)(e.S + e.S2) * M * d * 4);
+    mx = std::max(mx, (size_t)e.Ss * M * d * 4);
   }
   return mx;
 }
@@ -266,8 +246,8 @@ Layout make_layout(const fm_config& c) {
   L.cache = take((size_t)c.L * 2 * c.max_requests * cache_positions(c) * d * es);
   L.mods = take((size_t)c.max_steps * (6 * c.L + 2) * d * 4);
   L.sched = take(((size_t)2 * c.max_steps * 256 + 3 * (size_t)c.max_steps * d) * 4);
+  L.ctx = take((FM_MAX_REQ + 1) * 4);  // context length of each request, then the overflow flag
   L.h = take(Mb * d * 4);
-  L.hb = take(Mb * d * es);  // h in the storage type, for the fused LayerNorms
   L.e_state = take(Mb * d * 4);
   L.u_pre = take((size_t)std::max(MAX_PREFILL_ROWS, c.max_new) * d * 4);
   L.act_qkv = take((Mb + std::max(MAX_PREFILL_ROWS, c.max_new)) * d * es);
@@ -338,12 +318,17 @@ struct fm_handle {
   bool has_weights = false;
   int n_steps = 0;
   float times[8];
-  int ctx_len[FM_MAX_REQ] = {};   // context rows of each request
+  // Host mirror of the device-resident context lengths, advanced by the calls
+  // made on the host (not by graph replays; fm_context_sync reloads it).  It
+  // serves the argument checks only: kernels read the lengths on the device.
+  int ctx_len[FM_MAX_REQ] = {};
   int ctx_high[FM_MAX_REQ] = {};  // rows [0, ctx_high) have been written at least once
   int probe = FM_PROBE_NONE;
   hipEvent_t probe_start = nullptr, probe_stop = nullptr;
 
   template <typename P> P* at(size_t off) { return reinterpret_cast<P*>(ws + off); }
+  // device-resident context lengths (and the overflow flag after them)
+  int* ctx_dev() { return at<int>(lay.ctx); }
   // key / value cache of DiT block l
   // key / value cache of DiT block l, request 0 (request r at + r * req_stride())
   size_t req_stride() const { return (size_t)cache_positions(cfg) * cfg.d; }
@@ -465,7 +450,7 @@ fm_status gemm(fm_handle* h, int epi, const void* A, int lda, int M, const void*
 bool ln_fusable(const fm_config& c, int B) { return B == 1 && cdiv(c.d, gemm_chunk(c.dtype)) <= 8; }
 
 template <typename T>
-fm_status gemm_ln(fm_handle* h, int epi, const T* x, const float* shift, const float* scale, const void* A_ctx,
+fm_status gemm_ln(fm_handle* h, int epi, const float* x, const float* shift, const float* scale, const void* A_ctx,
                   int M_ctx, const void* W, int N, int K, const EpiParams& e, hipStream_t st) {
   if (cdiv(K, gemm_chunk(h->cfg.dtype)) > 8) return fail(FM_EINVAL, "fused LayerNorm needs k <= 8 chunks");
   GemmArgs a;
@@ -519,10 +504,11 @@ fm_status ln_mod(fm_handle* h, const float* x, int rows, const float* shift, con
 fm_status probe_begin(fm_handle* h, int kernel, hipStream_t st);
 fm_status probe_end(fm_handle* h, int kernel, hipStream_t st);
 
-// probe: FM_PROBE_EMBED brackets embed_kernel alone (the kernel the counters
-// and the roofline describe); -1 records nothing
+// probe: FM_PROBE_EMBED brackets embed_kernel alone (the contraction the
+// counters and the roofline describe, without its split-sum kernel); -1
+// records nothing
 template <typename T>
-fm_status embed(fm_handle* h, const void* x, int ldx, int M, float alpha, float beta, T* hb, hipStream_t st,
+fm_status embed(fm_handle* h, const void* x, int ldx, int M, float alpha, float beta, hipStream_t st,
                 int probe = -1) {
   const fm_config& c = h->cfg;
   if (M > 64) return fail(FM_EINVAL, "embedding contraction with %d rows exceeds 64", M);
@@ -536,22 +522,16 @@ fm_status embed(fm_handle* h, const void* x, int ldx, int M, float alpha, float 
   a.d = c.d;
   a.Sf = p.Sf;
   a.Ss = p.Ss;
-  a.S1 = p.S1;
-  a.S2 = p.S2;
   a.rows_split = cdiv(cdiv(c.V, p.Sf), 4 * vec_elems(c.dtype)) * 4 * vec_elems(c.dtype);
   a.rows_split_s = cdiv(cdiv(c.V, p.Ss), 4 * vec_elems(c.dtype)) * 4 * vec_elems(c.dtype);
   a.partial = h->at<float>(h->lay.partial);
-  a.gpartial = a.partial + (size_t)p.S * M * c.d;
-  a.counters = h->at<uint32_t>(h->lay.counters);
   a.e_state = h->at<float>(h->lay.e_state);
   a.h = h->at<float>(h->lay.h);
-  a.hb = hb;
   a.alpha = alpha;
   a.beta = beta;
   a.K = KB;
   a.use_pos = 1;
-  a.sep = 1;
-  if (p.S > EMB_SPLITS_MAX) return fail(FM_EINVAL, "embedding with %d row splits (at most %d)", p.S, EMB_SPLITS_MAX);
+  if (p.Ss > EMB_SPLITS_MAX) return fail(FM_EINVAL, "embedding with %d row splits (at most %d)", p.Ss, EMB_SPLITS_MAX);
   const dim3 grid(p.grid), block(EMB_WAVES * 64);
   FM_TRY(probe_begin(h, probe, st));
   switch (p.MT) {
@@ -562,20 +542,19 @@ fm_status embed(fm_handle* h, const void* x, int ldx, int M, float alpha, float 
   }
   FM_LAUNCHED("embed_kernel");
   FM_TRY(probe_end(h, probe, st));
-  if (a.sep) {
-    hipLaunchKernelGGL((embed_reduce_kernel<T>), dim3(cdiv(M * c.d, 256)), dim3(256), 0, st, a);
-    FM_LAUNCHED("embed_reduce_kernel");
-  }
+  hipLaunchKernelGGL((embed_reduce_kernel<T>), dim3(cdiv(M * c.d, 256)), dim3(256), 0, st, a);
+  FM_LAUNCHED("embed_reduce_kernel");
   return FM_OK;
 }
 
+// attention of B row blocks in DiT block l; n_new[b]: rows the call appends to
+// branch b's request (its visible context is that request's device-resident
+// length plus n_new[b]).  Grids are sized for the cache capacity; the ranges
+// in use follow the current length on the device.
 template <typename T>
-fm_status attention(fm_handle* h, int l, int B, const int* C, bool own_ctx, hipStream_t st) {
+fm_status attention(fm_handle* h, int l, int B, const int* n_new, bool own_ctx, hipStream_t st) {
   const fm_config& c = h->cfg;
   const int hd = c.d / c.n_heads;
-  int c_max = 0;
-  for (int b = 0; b < B; ++b) c_max = std::max(c_max, C[b]);
-  AttnPlan p = plan_attention(cdiv(c_max, ATT_BLK) + 1);
   AttnArgs a{};
   a.q = h->at<T>(h->lay.qkv);
   a.ldq = c.d;
@@ -583,29 +562,25 @@ fm_status attention(fm_handle* h, int l, int B, const int* C, bool own_ctx, hipS
   a.vt = h->vcache<T>(l);
   a.req_stride = h->req_stride();
   a.P = cache_positions(c);
-  for (int b = 0; b < B; ++b) a.C[b] = C[b];
+  a.ctx_len = h->ctx_dev();
+  for (int b = 0; b < B; ++b) a.n_new[b] = n_new[b];
+  a.ctx_cap = c.C_max;
   a.scratch_blk = cdiv(c.C_max, ATT_BLK);
   a.scratch_step = own_ctx ? 0 : 1;
   a.K = KB;
   a.d = c.d;
   a.nh = c.n_heads;
-  a.n_ranges = p.n_ranges;
-  a.blocks_per_range = p.blocks_per_range;
   a.part_o = h->at<float>(h->lay.att_po);
   a.part_ml = h->at<float>(h->lay.att_ml);
   a.counters = h->at<uint32_t>(h->lay.counters);
   a.out = h->at<T>(h->lay.attn_o);
   a.scale = 1.0f / std::sqrt((float)hd);
+  const int cap_blocks = cdiv(c.C_max, ATT_BLK);
   if constexpr (std::is_same<T, bf16_t>::value) {
     // four branches over one shared context: each key/value block is read once
     // per (head, range) and served to every branch from LDS
-    bool same_ctx = true;
-    for (int bb = 1; bb < B; ++bb) same_ctx = same_ctx && C[bb] == C[0];
-    if (!own_ctx && B == 4 && same_ctx && (hd == 128 || hd == 64)) {
-      const int ctx_blocks = cdiv(C[0], ATT_BLK);
-      const int r = std::min(ATT_TREE_RANGES, std::max(1, cdiv(ctx_blocks, 4)));
-      a.blocks_per_range = std::max(1, cdiv(ctx_blocks, r));
-      a.n_ranges = std::max(1, cdiv(ctx_blocks, a.blocks_per_range));
+    if (!own_ctx && B == 4 && (hd == 128 || hd == 64)) {
+      a.n_ranges = tree_max_ranges(cap_blocks);
       const int tgrid = c.n_heads * a.n_ranges;
       if (hd == 128)
         hipLaunchKernelGGL((attention_tree_kernel<128>), dim3(tgrid), dim3(512), 0, st, a);
@@ -623,7 +598,8 @@ fm_status attention(fm_handle* h, int l, int B, const int* C, bool own_ctx, hipS
       return FM_OK;
     }
   }
-  const int grid = B * c.n_heads * p.n_ranges;
+  a.n_ranges = attn_max_ranges(cap_blocks + 1, ATT_WAVES);
+  const int grid = B * c.n_heads * a.n_ranges;
   if (hd == 128)
     hipLaunchKernelGGL((attention_kernel<T, 128, ATT_WAVES>), dim3(grid), dim3(ATT_WAVES * 64), 0, st, a);
   else
@@ -649,9 +625,11 @@ struct Sampling {
 
 // probe: FM_PROBE_LM_HEAD brackets the LM head kernel alone (not the argmax
 // merge); -1 records nothing
+// cu: the draft's context update, applied by the argmax merge (the draft's
+// last kernel)
 template <typename T>
 fm_status lm_head(fm_handle* h, const void* z, int M, float* logits, int32_t* tokens, hipStream_t st,
-                  const Sampling* smp = nullptr, int probe = -1) {
+                  const Sampling* smp = nullptr, int probe = -1, const CtxUpdate& cu = CtxUpdate{}) {
   const fm_config& c = h->cfg;
   LmArgs a{};
   a.tau = smp ? smp->tau : 0.f;
@@ -701,7 +679,7 @@ fm_status lm_head(fm_handle* h, const void* z, int M, float* logits, int32_t* to
   FM_TRY(probe_end(h, probe, st));
   if (tokens) {
     hipLaunchKernelGGL(argmax_finalize_kernel, dim3(M), dim3(FIN_THREADS), 0, st, a.partial, grid, tokens,
-                       a.lse_part, smp ? smp->lse : nullptr);
+                       a.lse_part, smp ? smp->lse : nullptr, cu);
     FM_LAUNCHED("argmax_finalize_kernel");
   }
   return FM_OK;
@@ -778,6 +756,15 @@ void qkv_cache_params(fm_handle* h, int l, EpiParams& e) {
   e.scratch_pos0 = cdiv(c.C_max, ATT_BLK) * ATT_BLK;
   e.scratch_step = ATT_BLK;
   e.n_req = 1;
+  e.ctx_len = h->ctx_dev();
+  e.ctx_off = 0;
+  e.ctx_cap = c.C_max;
+}
+
+fm_status ctx_update_launch(const CtxUpdate& u, hipStream_t st) {
+  hipLaunchKernelGGL(ctx_update_kernel, dim3(1), dim3(64), 0, st, u);
+  FM_LAUNCHED("ctx_update_kernel");
+  return FM_OK;
 }
 
 template <typename T>
@@ -798,13 +785,20 @@ fm_status context_append_impl(fm_handle* h, int req, const void* feats, int n, h
       e.vcache = h->vcache<T>(l) + (size_t)req * h->req_stride();
       e.ctx_first[0] = 0;
       e.ctx_first[1] = rows;
-      e.ctx_pos0[0] = h->ctx_len[req] + r0;
+      e.ctx_len = h->ctx_dev() + req;
+      e.ctx_off = r0;
       e.col_offset = c.d;
       FM_TRY(gemm<T>(h, EPI_QKV, stage, c.d, rows, offset_rows<T>(blk(h, l, B_WQKV), (size_t)c.d * c.d), 2 * c.d,
                      c.d, e, st));
     }
   }
-  return FM_OK;
+  CtxUpdate u{};
+  u.len = h->ctx_dev();
+  u.first = req;
+  u.count = 1;
+  u.val[0] = n;
+  u.cap = c.C_max;
+  return ctx_update_launch(u, st);
 }
 
 template <typename T>
@@ -813,19 +807,21 @@ fm_status draft_impl(fm_handle* h, const void* noise, int B, const void* new_fea
                      const Batch* bt = nullptr) {
   const fm_config& c = h->cfg;
   const int d = c.d, F = c.mlp_mult * c.d, Mb = B * KB, L = c.L;
-  // visible context of each row block, and where the new context rows go
-  int C[FM_MAX_REQ];
+  // rows appended to each row block's request, and where the new context rows
+  // of each request sit below the block rows
+  int nb_new[FM_MAX_REQ];
   EpiParams ctx{};
   ctx.n_req = bt ? bt->R : 1;
   ctx.ctx_first[0] = 0;
-  for (int b = 0; b < B; ++b) {
-    const int r = bt ? b : 0;
-    C[b] = h->ctx_len[r] + (bt ? bt->n_new[b] : n_new);
-  }
-  for (int r = 0; r < ctx.n_req; ++r) {
-    ctx.ctx_pos0[r] = h->ctx_len[r];
-    ctx.ctx_first[r + 1] = ctx.ctx_first[r] + (bt ? bt->n_new[r] : n_new);
-  }
+  for (int b = 0; b < B; ++b) nb_new[b] = bt ? bt->n_new[b] : n_new;
+  for (int r = 0; r < ctx.n_req; ++r) ctx.ctx_first[r + 1] = ctx.ctx_first[r] + (bt ? bt->n_new[r] : n_new);
+  // the lengths advance in the draft's last kernel
+  CtxUpdate adv{};
+  adv.len = h->ctx_dev();
+  adv.first = 0;
+  adv.count = ctx.n_req;
+  for (int r = 0; r < ctx.n_req; ++r) adv.val[r] = bt ? bt->n_new[r] : n_new;
+  adv.cap = c.C_max;
   const bool fuse_ln = ln_fusable(c, B);
   // many rows: the reduces of W_o and fc2 also write the LayerNorm that follows
   const bool ln_in_reduce = !fuse_ln && resid_ln_fused(Mb, d, d, c.dtype) && resid_ln_fused(Mb, d, F, c.dtype);
@@ -835,9 +831,6 @@ fm_status draft_impl(fm_handle* h, const void* noise, int B, const void* new_fea
   T* attn_o = h->at<T>(h->lay.attn_o);
   T* qkv = h->at<T>(h->lay.qkv);
   float* hres = h->at<float>(h->lay.h);
-  // the fused LayerNorms read h in the storage type: its producers (embedding,
-  // the two gated residual contractions) write that copy beside h
-  T* hb = fuse_ln ? h->at<T>(h->lay.hb) : nullptr;
   const float* mods_all = h->at<float>(h->lay.mods);
 
   // context rows appended in this step: u goes below the block rows of act_qkv
@@ -847,10 +840,10 @@ fm_status draft_impl(fm_handle* h, const void* noise, int B, const void* new_fea
     const float s = h->times[j], t = h->times[j + 1];
     const float* mods = mods_all + (size_t)j * (6 * L + 2) * d;
     if (j == 0) {
-      FM_TRY(embed<T>(h, noise, c.V, Mb, 0.f, 1.f, hb, st, FM_PROBE_EMBED));
+      FM_TRY(embed<T>(h, noise, c.V, Mb, 0.f, 1.f, st, FM_PROBE_EMBED));
     } else {
       const float sp = h->times[j - 1];
-      FM_TRY(embed<T>(h, h->at<T>(h->lay.dsoft), c.V, Mb, (1.f - s) / (1.f - sp), (s - sp) / (1.f - sp), hb, st));
+      FM_TRY(embed<T>(h, h->at<T>(h->lay.dsoft), c.V, Mb, (1.f - s) / (1.f - sp), (s - sp) / (1.f - sp), st));
     }
     if (hidden) FM_TRY(trace_copy(hres, hidden + ((size_t)j * (L + 1)) * Mb * d, (size_t)Mb * d, st));
     const int m_qkv = Mb + (j == 0 ? n_new : 0);
@@ -866,10 +859,9 @@ fm_status draft_impl(fm_handle* h, const void* noise, int B, const void* new_fea
         e.scratch_step = bt ? 0 : ATT_BLK;
         e.n_req = ctx.n_req;
         std::memcpy(e.ctx_first, ctx.ctx_first, sizeof e.ctx_first);
-        std::memcpy(e.ctx_pos0, ctx.ctx_pos0, sizeof e.ctx_pos0);
         e.col_offset = 0;
         if (fuse_ln) {
-          FM_TRY(gemm_ln<T>(h, EPI_QKV, hb, mv + 0 * d, mv + 1 * d, act_qkv + (size_t)Mb * d, m_qkv - Mb,
+          FM_TRY(gemm_ln<T>(h, EPI_QKV, hres, mv + 0 * d, mv + 1 * d, act_qkv + (size_t)Mb * d, m_qkv - Mb,
                             blk(h, l, B_WQKV), 3 * d, d, e, st));
         } else {
           // block 0's rows come from the embedding; later ones were normalised by fc2's reduce
@@ -877,15 +869,13 @@ fm_status draft_impl(fm_handle* h, const void* noise, int B, const void* new_fea
           FM_TRY(gemm<T>(h, EPI_QKV, act_qkv, d, m_qkv, blk(h, l, B_WQKV), 3 * d, d, e, st));
         }
       }
-      FM_TRY(attention<T>(h, l, B, C, bt != nullptr, st));
+      FM_TRY(attention<T>(h, l, B, nb_new, bt != nullptr, st));
       {
         EpiParams e{};
         e.bias = blk(h, l, B_BO);
         e.out_f32 = hres;
         e.ld_f32 = d;
         e.gate = mv + 2 * d;
-        e.out_act = hb;
-        e.ld_act = d;
         if (ln_in_reduce) {  // LN2 for fc1
           e.ln_shift = mv + 3 * d;
           e.ln_scale = mv + 4 * d;
@@ -902,7 +892,7 @@ fm_status draft_impl(fm_handle* h, const void* noise, int B, const void* new_fea
         const int pk = (j == 0 && l == 0) ? FM_PROBE_FC1 : -1;
         if (fuse_ln) {
           FM_TRY(probe_begin(h, pk, st));
-          FM_TRY(gemm_ln<T>(h, EPI_GELU, hb, mv + 3 * d, mv + 4 * d, nullptr, 0, blk(h, l, B_W1), F, d, e, st));
+          FM_TRY(gemm_ln<T>(h, EPI_GELU, hres, mv + 3 * d, mv + 4 * d, nullptr, 0, blk(h, l, B_W1), F, d, e, st));
           FM_TRY(probe_end(h, pk, st));
         } else {
           if (!ln_in_reduce) FM_TRY(ln_mod<T>(h, hres, Mb, mv + 3 * d, mv + 4 * d, act_d, d, st));
@@ -917,8 +907,6 @@ fm_status draft_impl(fm_handle* h, const void* noise, int B, const void* new_fea
         e.out_f32 = hres;
         e.ld_f32 = d;
         e.gate = mv + 5 * d;
-        e.out_act = hb;
-        e.ld_act = d;
         if (ln_in_reduce) {  // the next block's LN1, or the final LN before the LM head
           const float* nm = mods + (size_t)6 * (l + 1) * d;
           e.ln_shift = nm;
@@ -933,7 +921,7 @@ fm_status draft_impl(fm_handle* h, const void* noise, int B, const void* new_fea
     const float* fin = mods + (size_t)6 * L * d;  // shift_f, scale_f
     if (!ln_in_reduce) FM_TRY(ln_mod<T>(h, hres, Mb, fin, fin + d, act_d, d, st));
     if (t == 1.f) {
-      FM_TRY(lm_head<T>(h, act_d, Mb, logits, tokens, st, smp, FM_PROBE_LM_HEAD));
+      FM_TRY(lm_head<T>(h, act_d, Mb, logits, tokens, st, smp, FM_PROBE_LM_HEAD, adv));
     } else {
       FM_TRY(lm_head<T>(h, act_d, Mb, h->at<float>(h->lay.logits_tmp), nullptr, st));
       FM_TRY(softmax_rows<T>(h, Mb, st));
@@ -1072,6 +1060,10 @@ fm_status fm_create(const fm_config* cfg, void* workspace, size_t ws_bytes, int 
   hipLaunchKernelGGL(zero_u32_kernel, dim3(64), dim3(256), 0, 0, h->at<uint32_t>(lay.counters),
                      (size_t)N_COUNTER_SLOTS * COUNTER_STRIDE);
   hipError_t e = hipGetLastError();
+  if (e == hipSuccess) {  // empty contexts, overflow flag clear
+    hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, 0, h->at<uint32_t>(lay.ctx), (size_t)FM_MAX_REQ + 1);
+    e = hipGetLastError();
+  }
   if (e == hipSuccess) e = hipStreamSynchronize(0);
   if (e != hipSuccess) {
     delete h;
@@ -1137,18 +1129,53 @@ fm_status fm_context_append(fm_handle* h, const void* feats, int n, void* stream
   return fm_context_append_req(h, 0, feats, n, stream);
 }
 
-fm_status fm_context_truncate_req(fm_handle* h, int req, int new_len) {
+fm_status fm_context_truncate_req(fm_handle* h, int req, int new_len, void* stream) {
   g_err.clear();
   if (!h) return fail(FM_EINVAL, "handle is NULL");
   if (req < 0 || req >= h->cfg.max_requests)
     return fail(FM_EINVAL, "request %d outside 0..%d", req, h->cfg.max_requests - 1);
   if (new_len < 0 || new_len > h->ctx_high[req])
     return fail(FM_EINVAL, "new length %d outside 0..%d (rows written so far)", new_len, h->ctx_high[req]);
+  CtxUpdate u{};
+  u.len = h->ctx_dev();
+  u.first = req;
+  u.count = 1;
+  u.val[0] = new_len;
+  u.set = 1;
+  u.cap = h->cfg.C_max;
+  FM_TRY(ctx_update_launch(u, reinterpret_cast<hipStream_t>(stream)));
   h->ctx_len[req] = new_len;
   return FM_OK;
 }
 
-fm_status fm_context_truncate(fm_handle* h, int new_len) { return fm_context_truncate_req(h, 0, new_len); }
+fm_status fm_context_truncate(fm_handle* h, int new_len, void* stream) {
+  return fm_context_truncate_req(h, 0, new_len, stream);
+}
+
+fm_status fm_context_sync(fm_handle* h, void* stream) {
+  g_err.clear();
+  if (!h) return fail(FM_EINVAL, "handle is NULL");
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  int dev[FM_MAX_REQ + 1];
+  FM_HIP(hipMemcpyAsync(dev, h->ctx_dev(), sizeof dev, hipMemcpyDeviceToHost, st));
+  FM_HIP(hipStreamSynchronize(st));
+  for (int r = 0; r < h->cfg.max_requests; ++r) {
+    h->ctx_len[r] = dev[r];
+    h->ctx_high[r] = std::max(h->ctx_high[r], dev[r]);
+  }
+  if (dev[FM_MAX_REQ]) {
+    CtxUpdate u{};  // clear the flag (the lengths stay at the capacity)
+    u.len = h->ctx_dev() + FM_MAX_REQ;
+    u.first = 0;
+    u.count = 1;
+    u.set = 1;
+    u.cap = 0;
+    FM_TRY(ctx_update_launch(u, st));
+    return fail(FM_ECAPACITY, "an append on the device passed C_max %d: the rows past it were dropped",
+                h->cfg.C_max);
+  }
+  return FM_OK;
+}
 
 int fm_context_length_req(const fm_handle* h, int req) {
   return h && req >= 0 && req < h->cfg.max_requests ? h->ctx_len[req] : -1;

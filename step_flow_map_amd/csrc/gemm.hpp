@@ -47,8 +47,11 @@ struct EpiParams {
   int scratch_step;     // 32: branches share request 0's cache, branch b's rows at +32b;
                         // 0: branch b is request b, its rows in its own cache
   int n_req;            // context row c belongs to request r with ctx_first[r] <= c <
-  int ctx_first[FM_MAX_REQ + 1];  // ctx_first[r + 1], at position ctx_pos0[r] + c - ctx_first[r]
-  int ctx_pos0[FM_MAX_REQ];
+  int ctx_first[FM_MAX_REQ + 1];  // ctx_first[r + 1], and goes to position
+                        // ctx_len[r] + ctx_off + c - ctx_first[r] of that request's cache
+  const int* ctx_len;   // device: each request's context length before the call
+  int ctx_off;          // rows the call has already appended ahead of these
+  int ctx_cap;          // positions >= ctx_cap are not written (the cache is full)
   int col_offset;       // logical qkv column of n = 0 (d for a K/V-only call)
   // EPI_RESID through gemm_reduce_ln_kernel: the LayerNorm + modulation of the
   // updated rows, written in the storage type (the next contraction's operand)
@@ -101,7 +104,8 @@ __device__ __forceinline__ void epilogue(const EpiParams& e, int m, int n, float
       req = 0;
 #pragma unroll
       for (int r = 1; r < FM_MAX_REQ; ++r) req += (r < e.n_req && c >= e.ctx_first[r]) ? 1 : 0;
-      pos = e.ctx_pos0[req] + c - e.ctx_first[req];
+      pos = e.ctx_len[req] + e.ctx_off + c - e.ctx_first[req];
+      if (pos >= e.ctx_cap) return;  // past the capacity: nothing is written
     }
     const int which = nn >= 2 * e.d;  // 0: key, 1: value
     const int col = nn - (1 + which) * e.d;
@@ -253,12 +257,11 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs g, EpiParams e) 
 
 // LayerNorm fused into the A operand (tile-group kernel): rows 0..15 of the
 // contraction are LN(h[r]) * (1 + scale) + shift rounded to the storage type,
-// computed inside the kernel from the residual rows in the storage type (the
-// copy their producer writes beside the float32 stream, which halves the rows'
-// bytes in bf16); rows 16.. come from GemmArgs::A as usual (context rows,
-// already normalised).  Statistics and normalisation are float32.
+// computed inside the kernel from the float32 residual rows (never rounded
+// before the statistics and the normalisation, which are float32); rows 16..
+// come from GemmArgs::A as usual (context rows, already normalised).
 struct LnArgs {
-  const void* h;       // [16][ldh] storage type
+  const float* h;      // [16][ldh] float32 residual stream
   int ldh;
   const float* shift;  // [K]
   const float* scale;  // [K]
@@ -333,12 +336,16 @@ __global__ __launch_bounds__(NW * 64) void gemm_tg_kernel(GemmArgs g, EpiParams 
     // ---- issue: residual rows, modulation, A rows, weights.  Addresses are
     // clamped in range and nothing here is conditional, so no load waits for
     // another one before the statistics need the residual rows.
-    VT hv[LN ? 8 : 1];
+    constexpr int HQ = LN ? VE / 4 : 1;  // float4 of residual per k run
+    float4 hv[LN ? 8 : 1][HQ];
     float4 mv[MODQ], mv2[MODQ];
     if constexpr (LN) {
-      const T* hr = reinterpret_cast<const T*>(ln.h) + (size_t)j * ln.ldh;
+      const float* hr = ln.h + (size_t)j * ln.ldh;
 #pragma unroll
-      for (int st = 0; st < 8; ++st) hv[st] = vload<T>(hr + (kok[st] ? k0 + (4 * st + grp) * VE : 0));
+      for (int st = 0; st < 8; ++st)
+#pragma unroll
+        for (int q = 0; q < HQ; ++q)
+          hv[st][q] = *reinterpret_cast<const float4*>(hr + (kok[st] ? k0 + (4 * st + grp) * VE : 0) + 4 * q);
       const int kq = g.K / 4;
 #pragma unroll
       for (int q = 0; q < MODQ; ++q) {
@@ -376,10 +383,8 @@ __global__ __launch_bounds__(NW * 64) void gemm_tg_kernel(GemmArgs g, EpiParams 
 #pragma unroll
       for (int st = 0; st < 8; ++st) {
         const float mk = kok[st] ? 1.f : 0.f;
-        float y[VE];
-        unpack_vec(hv[st], y);
 #pragma unroll
-        for (int q = 0; q < VE; q += 4) sum += mk * ((y[q] + y[q + 1]) + (y[q + 2] + y[q + 3]));
+        for (int q = 0; q < HQ; ++q) sum += mk * ((hv[st][q].x + hv[st][q].y) + (hv[st][q].z + hv[st][q].w));
       }
       sum += __shfl_xor(sum, 16, 64);
       sum += __shfl_xor(sum, 32, 64);
@@ -388,11 +393,9 @@ __global__ __launch_bounds__(NW * 64) void gemm_tg_kernel(GemmArgs g, EpiParams 
 #pragma unroll
       for (int st = 0; st < 8; ++st) {
         const float mk = kok[st] ? 1.f : 0.f;
-        float y[VE];
-        unpack_vec(hv[st], y);
 #pragma unroll
-        for (int q = 0; q < VE; q += 4) {
-          const float a = y[q] - mw, b = y[q + 1] - mw, cc = y[q + 2] - mw, d = y[q + 3] - mw;
+        for (int q = 0; q < HQ; ++q) {
+          const float a = hv[st][q].x - mw, b = hv[st][q].y - mw, cc = hv[st][q].z - mw, d = hv[st][q].w - mw;
           m2 += mk * ((a * a + b * b) + (cc * cc + d * d));
         }
       }
@@ -419,7 +422,13 @@ __global__ __launch_bounds__(NW * 64) void gemm_tg_kernel(GemmArgs g, EpiParams 
       for (int st = 0; st < 8; ++st) {
         const int k = kok[st] ? k0 + (4 * st + grp) * VE : 0;
         float x[VE], y[VE];
-        unpack_vec(hv[st], x);
+#pragma unroll
+        for (int q = 0; q < HQ; ++q) {
+          x[4 * q + 0] = hv[st][q].x;
+          x[4 * q + 1] = hv[st][q].y;
+          x[4 * q + 2] = hv[st][q].z;
+          x[4 * q + 3] = hv[st][q].w;
+        }
 #pragma unroll
         for (int q = 0; q < VE / 4; ++q) {
           const float4 sc = *reinterpret_cast<const float4*>(&smod[k + 4 * q]);

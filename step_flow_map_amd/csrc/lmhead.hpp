@@ -356,6 +356,35 @@ __global__ __launch_bounds__(NW * 64) void lmhead_ks_kernel(LmArgs g) {
   }
 }
 
+// Context lengths on the device (in the handle's workspace): len[r] for each
+// request, then at len[FM_MAX_REQ] a sticky flag set when an append would pass
+// the capacity (the length then stops at the capacity and the rows past it are
+// not written).  A call that appends rows advances the lengths in its last
+// kernel, after every kernel that reads them, so a captured graph advances the
+// context on every replay.
+struct CtxUpdate {
+  int* len;              // null: no update
+  int first, count;      // requests first .. first + count - 1
+  int val[FM_MAX_REQ];   // rows appended (set == 0), or the new length (set == 1)
+  int set;
+  int cap;
+};
+__device__ __forceinline__ void ctx_update(const CtxUpdate& u) {
+  if (!u.len) return;
+  for (int i = 0; i < u.count; ++i) {
+    const int r = u.first + i;
+    int v = u.set ? u.val[i] : u.len[r] + u.val[i];
+    if (v > u.cap) {
+      v = u.cap;
+      u.len[FM_MAX_REQ] = 1;
+    }
+    u.len[r] = v;
+  }
+}
+__global__ __launch_bounds__(64) void ctx_update_kernel(CtxUpdate u) {
+  if (threadIdx.x == 0) ctx_update(u);
+}
+
 // tokens[m] = index of max over the G workgroup keys of row m, and with
 // lse_part given lse[m] = log sum_g s_g exp(m_g) over the row's G workgroup
 // (max, sum) states.
@@ -363,12 +392,14 @@ __global__ __launch_bounds__(NW * 64) void lmhead_ks_kernel(LmArgs g) {
 // contiguous; every thread folds its strided share, then waves and the
 // workgroup combine in a fixed order (keys by max, states by log-sum-exp).
 constexpr int FIN_THREADS = 256;
+// The first workgroup also applies the context update `cu` of the draft.
 __global__ __launch_bounds__(FIN_THREADS) void argmax_finalize_kernel(const uint64_t* partial, int G,
                                                                      int32_t* tokens, const float2* lse_part,
-                                                                     float* lse) {
+                                                                     float* lse, CtxUpdate cu) {
   __shared__ uint64_t sk[FIN_THREADS / 64];
   __shared__ float2 ss[FIN_THREADS / 64];
   const int m = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  if (m == 0 && t == 0) ctx_update(cu);
   const uint64_t* pk = partial + (size_t)m * G;
   const float2* pe = lse_part ? lse_part + (size_t)m * G : nullptr;
   uint64_t k = 0ull;
