@@ -286,6 +286,24 @@ fm_status fm_verify_sample(fm_handle *h, const void *target_logits, fm_dtype dty
                            float temperature, uint64_t seed, int32_t *emitted, int32_t *accept,
                            void *stream);
 
+/* fm_verify_sample for callers that cannot allocate device memory or hold a
+ * handle (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation): the same verification, bit for bit, with its scratch
+ * in a static device array of the library (160 KB per GPU, held until the
+ * process ends) instead of a handle's workspace.
+ *   K         must be 16; V >= 1 the vocabulary size of the logits
+ *   B         1 <= B <= 4 branches (more: FM_ECAPACITY, nothing enqueued)
+ *   other arguments as fm_verify_sample
+ * The stream must belong to the current device.  The first call on a device
+ * looks up that device's copy of the array.  Every call on one GPU shares it:
+ * calls that overlap on one GPU (several streams or threads) race.  Nothing
+ * in the array needs clearing between calls.  Errors: FM_EINVAL,
+ * FM_ECAPACITY, FM_EHIP. */
+fm_status fm_verify_sample_noalloc(const void *target_logits, fm_dtype dtype, int B, int K, int V,
+                                   const float *draft_logits, const float *draft_lse, const int32_t *draft,
+                                   float temperature, uint64_t seed, int32_t *emitted, int32_t *accept,
+                                   void *stream);
+
 /* Kernels a probe can bracket. */
 typedef enum fm_probe_kernel {
   FM_PROBE_NONE = 0,

@@ -93,6 +93,8 @@ def lib() -> ctypes.CDLL:
     L.fm_draft_sample.restype = st
     L.fm_verify_sample.argtypes = [vp, vp, i, i, vp, vp, vp, f32, u64, vp, vp, vp]
     L.fm_verify_sample.restype = st
+    L.fm_verify_sample_noalloc.argtypes = [vp, i, i, i, i, vp, vp, vp, f32, u64, vp, vp, vp]
+    L.fm_verify_sample_noalloc.restype = st
     L.fm_set_probe.argtypes = [vp, i, vp, vp]
     L.fm_set_probe.restype = st
     L.fm_last_error.argtypes = []
@@ -244,6 +246,18 @@ def fm_verify_sample(h, target_logits, draft_logits, draft_lse, draft, temperatu
                                   _ptr(draft_logits), _ptr(draft_lse), _ptr(draft), float(temperature),
                                   int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(emitted), _ptr(accept),
                                   _stream(stream)))
+
+
+def fm_verify_sample_noalloc(target_logits, draft_logits, draft_lse, draft, temperature, seed, emitted, accept,
+                             stream=None):
+    """fm_verify_sample with the library's static scratch (no handle):
+    target_logits [B][K+1][V], draft_logits [B][K][V], draft_lse [B][K],
+    draft [B][K]; outputs emitted [B][K+1] and accept [B] int32."""
+    B, K1, V = (int(s) for s in target_logits.shape)
+    _check(lib().fm_verify_sample_noalloc(_ptr(target_logits), dtype_code(target_logits.dtype), B, K1 - 1, V,
+                                          _ptr(draft_logits), _ptr(draft_lse), _ptr(draft), float(temperature),
+                                          int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(emitted), _ptr(accept),
+                                          _stream(stream)))
 
 
 def fm_verify(target_logits, draft, emitted, accept, best, stream=None):

@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <type_traits>
 #include <string>
 #include <vector>
@@ -26,6 +27,14 @@
 
 using namespace fm;
 
+// Scratch of fm_verify_sample_noalloc, for callers that cannot allocate device
+// memory (code under graph capture, tight serving loops): one copy per GPU,
+// held until the process ends.  Host code must not pass the array's name to a
+// kernel (on the host it is a stand-in, not a device address): the address of
+// each device's copy comes from hipGetSymbolAddress, once per device.
+constexpr int NOALLOC_MAX_B = 4;  // branches (of K = 16 rows) one call may verify
+static __device__ __align__(256) unsigned char scratch[160 * 1024];
+
 namespace {
 
 thread_local std::string g_err;
@@ -38,6 +47,26 @@ fm_status fail(fm_status st, const char* fmt, ...) {
   va_end(ap);
   g_err = buf;
   return st;
+}
+
+// this device's copy of `scratch`, looked up once per device (device current)
+fm_status scratch_ptr(char** out) {
+  constexpr int MAX_DEV = 64;
+  static std::mutex mu;
+  static char* ptr[MAX_DEV] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(FM_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= MAX_DEV) return fail(FM_EINVAL, "device %d outside 0..%d", dev, MAX_DEV - 1);
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return fail(FM_EHIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    ptr[dev] = static_cast<char*>(p);
+  }
+  *out = ptr[dev];
+  return FM_OK;
 }
 
 #define FM_HIP(call)                                                                   \
@@ -76,6 +105,33 @@ int vec_elems(fm_dtype t) { return t == FM_BF16 ? 8 : 4; }
 int gemm_chunk(fm_dtype t) { return 32 * vec_elems(t); }  // k elements per streamed chunk
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+// scratch of the probabilistic verifier: slice states, row normalisers, the
+// accepted prefixes and row n's slice keys
+struct VsScratch {
+  float2* stats;     // [B*(K+1)][VS_MAX_SLICES]
+  float* lse_rows;   // [B*(K+1)]
+  int32_t* n_acc;    // [B]
+  uint64_t* keys;    // [B][VS_MAX_SLICES][2]
+};
+
+// bytes of VsScratch for B branches of K rows, carved from one 256-byte-aligned base
+size_t vs_scratch_bytes(int B, int K) {
+  return align256((size_t)B * (K + 1) * VS_MAX_SLICES * 8) + align256((size_t)B * (K + 1) * 4) +
+         align256((size_t)B * 4) + align256((size_t)B * VS_MAX_SLICES * 16);
+}
+VsScratch vs_scratch_at(char* base, int B, int K) {
+  VsScratch s;
+  s.stats = reinterpret_cast<float2*>(base);
+  base += align256((size_t)B * (K + 1) * VS_MAX_SLICES * 8);
+  s.lse_rows = reinterpret_cast<float*>(base);
+  base += align256((size_t)B * (K + 1) * 4);
+  s.n_acc = reinterpret_cast<int32_t*>(base);
+  base += align256((size_t)B * 4);
+  s.keys = reinterpret_cast<uint64_t*>(base);
+  return s;
+}
+
 
 struct GemmPlan {
   int S, k_split, n_groups, grid, waves;
@@ -204,8 +260,7 @@ int max_blocks(const fm_config& c) { return std::max(c.max_branches, c.max_reque
 
 struct Layout {
   size_t cache, mods, sched, ctx, h, e_state, u_pre, act_qkv, act_d, attn_o, act_f, qkv;
-  size_t att_po, att_ml, partial, lm_part, lm_lse, counters, dsoft, logits_tmp, sm_part, vs_stats, vs_lse, vs_n,
-      vs_keys, total;
+  size_t att_po, att_ml, partial, lm_part, lm_lse, counters, dsoft, logits_tmp, sm_part, vs, total;
 };
 
 int max_rows(const fm_config& c) { return max_blocks(c) * KB; }
@@ -261,10 +316,7 @@ Layout make_layout(const fm_config& c) {
   L.partial = take(partial_bytes(c));
   L.lm_part = take((size_t)LM_GRID * Mb * 8);
   L.lm_lse = take((size_t)LM_GRID * Mb * 8);
-  L.vs_stats = take((size_t)max_blocks(c) * (KB + 1) * VS_MAX_SLICES * 8);
-  L.vs_lse = take((size_t)max_blocks(c) * (KB + 1) * 4);
-  L.vs_n = take((size_t)max_blocks(c) * 4);
-  L.vs_keys = take((size_t)max_blocks(c) * VS_MAX_SLICES * 16);
+  L.vs = take(vs_scratch_bytes(c.max_branches, KB));
   L.counters = take((size_t)N_COUNTER_SLOTS * COUNTER_STRIDE * 4);
   if (c.max_steps > 1) {
     L.dsoft = take(Mb * (size_t)c.V * es);
@@ -976,10 +1028,9 @@ fm_status verify_impl(const void* tl, int B, int K, int V, const int32_t* draft,
 }
 
 template <typename T>
-fm_status verify_sample_impl(fm_handle* h, const void* tl, int B, const float* Q, const float* lseQ,
+fm_status verify_sample_impl(const VsScratch& sc, int V, const void* tl, int B, const float* Q, const float* lseQ,
                              const int32_t* draft, float tau, uint64_t seed, int32_t* emitted, int32_t* accept,
                              hipStream_t st) {
-  const fm_config& c = h->cfg;
   VsArgs a{};
   a.T = tl;
   a.Q = Q;
@@ -987,16 +1038,16 @@ fm_status verify_sample_impl(fm_handle* h, const void* tl, int B, const float* Q
   a.draft = draft;
   a.B = B;
   a.K = KB;
-  a.V = c.V;
-  a.S = std::min(VS_MAX_SLICES, cdiv(c.V, VS_SLICE));
-  a.slice = cdiv(c.V, a.S);
+  a.V = V;
+  a.S = std::min(VS_MAX_SLICES, cdiv(V, VS_SLICE));
+  a.slice = cdiv(V, a.S);
   a.tau = tau;
   a.seed_lo = (uint32_t)(seed & 0xFFFFFFFFu);
   a.seed_hi = (uint32_t)(seed >> 32);
-  a.stats = h->at<float2>(h->lay.vs_stats);
-  a.lse_rows = h->at<float>(h->lay.vs_lse);
-  a.n_acc = h->at<int32_t>(h->lay.vs_n);
-  a.keys = h->at<uint64_t>(h->lay.vs_keys);
+  a.stats = sc.stats;
+  a.lse_rows = sc.lse_rows;
+  a.n_acc = sc.n_acc;
+  a.keys = sc.keys;
   a.emitted = emitted;
   a.accept = accept;
   hipLaunchKernelGGL((vs_stats_kernel<T>), dim3(a.S, B * (KB + 1)), dim3(VS_THREADS), 0, st, a);
@@ -1007,6 +1058,22 @@ fm_status verify_sample_impl(fm_handle* h, const void* tl, int B, const float* Q
   FM_LAUNCHED("vs_keys_kernel");
   hipLaunchKernelGGL(vs_final_kernel, dim3(B), dim3(64), 0, st, a);
   FM_LAUNCHED("vs_final_kernel");
+  return FM_OK;
+}
+
+// argument checks shared by the two probabilistic verifiers
+fm_status check_verify_sample(const void* target_logits, fm_dtype dtype, int B, const float* draft_logits,
+                              const float* draft_lse, const int32_t* draft, float temperature, int32_t* emitted,
+                              int32_t* accept) {
+  if (!target_logits || !draft_logits || !draft_lse || !draft || !emitted || !accept)
+    return fail(FM_EINVAL, "a pointer argument is NULL");
+  if (dtype != FM_BF16 && dtype != FM_F32) return fail(FM_EINVAL, "dtype must be FM_BF16 or FM_F32");
+  if (B < 1) return fail(FM_EINVAL, "B must be >= 1");
+  if (!(temperature > 0.f) || !std::isfinite(temperature))
+    return fail(FM_EINVAL, "temperature must be finite and > 0");
+  if (reinterpret_cast<uintptr_t>(target_logits) % esize(dtype) || reinterpret_cast<uintptr_t>(draft_logits) % 4 ||
+      reinterpret_cast<uintptr_t>(draft_lse) % 4)
+    return fail(FM_EINVAL, "a logits array is not aligned to its element size");
   return FM_OK;
 }
 
@@ -1285,20 +1352,34 @@ fm_status fm_verify_sample(fm_handle* h, const void* target_logits, fm_dtype dty
                            int32_t* emitted, int32_t* accept, void* stream) {
   g_err.clear();
   if (!h) return fail(FM_EINVAL, "handle is NULL");
-  if (!target_logits || !draft_logits || !draft_lse || !draft || !emitted || !accept)
-    return fail(FM_EINVAL, "a pointer argument is NULL");
-  if (dtype != FM_BF16 && dtype != FM_F32) return fail(FM_EINVAL, "dtype must be FM_BF16 or FM_F32");
-  if (B < 1) return fail(FM_EINVAL, "B must be >= 1");
+  FM_TRY(check_verify_sample(target_logits, dtype, B, draft_logits, draft_lse, draft, temperature, emitted, accept));
   if (B > h->cfg.max_branches) return fail(FM_ECAPACITY, "B %d exceeds max_branches %d", B, h->cfg.max_branches);
-  if (!(temperature > 0.f) || !std::isfinite(temperature))
-    return fail(FM_EINVAL, "temperature must be finite and > 0");
-  if (reinterpret_cast<uintptr_t>(target_logits) % esize(dtype) || reinterpret_cast<uintptr_t>(draft_logits) % 4 ||
-      reinterpret_cast<uintptr_t>(draft_lse) % 4)
-    return fail(FM_EINVAL, "a logits array is not aligned to its element size");
+  const VsScratch sc = vs_scratch_at(h->at<char>(h->lay.vs), h->cfg.max_branches, KB);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  return dtype == FM_BF16 ? verify_sample_impl<bf16_t>(h, target_logits, B, draft_logits, draft_lse, draft,
+  return dtype == FM_BF16 ? verify_sample_impl<bf16_t>(sc, h->cfg.V, target_logits, B, draft_logits, draft_lse,
+                                                       draft, temperature, seed, emitted, accept, st)
+                          : verify_sample_impl<float>(sc, h->cfg.V, target_logits, B, draft_logits, draft_lse,
+                                                      draft, temperature, seed, emitted, accept, st);
+}
+
+fm_status fm_verify_sample_noalloc(const void* target_logits, fm_dtype dtype, int B, int K, int V,
+                                   const float* draft_logits, const float* draft_lse, const int32_t* draft,
+                                   float temperature, uint64_t seed, int32_t* emitted, int32_t* accept,
+                                   void* stream) {
+  g_err.clear();
+  FM_TRY(check_verify_sample(target_logits, dtype, B, draft_logits, draft_lse, draft, temperature, emitted, accept));
+  if (K != KB) return fail(FM_EINVAL, "K must be 16 (got %d)", K);
+  if (V < 1) return fail(FM_EINVAL, "V must be >= 1");
+  if (B > NOALLOC_MAX_B || vs_scratch_bytes(B, K) > sizeof(scratch))
+    return fail(FM_ECAPACITY, "B %d exceeds the %d branches the static scratch (%zu bytes) holds", B, NOALLOC_MAX_B,
+                sizeof(scratch));
+  char* base = nullptr;
+  FM_TRY(scratch_ptr(&base));
+  const VsScratch sc = vs_scratch_at(base, B, K);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  return dtype == FM_BF16 ? verify_sample_impl<bf16_t>(sc, V, target_logits, B, draft_logits, draft_lse, draft,
                                                        temperature, seed, emitted, accept, st)
-                          : verify_sample_impl<float>(h, target_logits, B, draft_logits, draft_lse, draft,
+                          : verify_sample_impl<float>(sc, V, target_logits, B, draft_logits, draft_lse, draft,
                                                       temperature, seed, emitted, accept, st);
 }
 
