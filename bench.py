@@ -2,8 +2,8 @@
 """Benchmark one FlashMap drafting step + greedy verify on one MI355X.
 
 A step is fm_draft (one flow-map jump from a 16 x V Gaussian noise block to a
-16-token draft, with 8 new context rows fused in) followed by fm_verify
-against target logits [17][V].  Inputs are seeded synthetic tensors of the
+16-token draft, with 8 new context rows fused in) followed by greedy
+verification (fm_verify_greedy) against target logits [17][V].  Inputs are seeded synthetic tensors of the
 Qwen3-8B-shaped drafter, resident in HBM before the timed region.  Steps are
 replayed from HIP graphs (one per planted target-logit set) and timed with HIP
 events; the dominant kernel is timed live with events recorded around its
@@ -223,13 +223,13 @@ def main():
     def draft_and_verify(T, seed):
         if R > 1:
             dr.draft_batch(x, new_feats=new, n_new=[cfg.n_new] * R, tokens=tokens)
-            fm.fm_verify(T, tokens, emitted, accept, best)
+            dr.verify(T, tokens, emitted, accept, best)
         elif temp > 0:
             fm.fm_draft_sample(dr.handle, x, temp, seed, tokens, logits_q, lse_q, new_feats=new)
             fm.fm_verify_sample(dr.handle, T, logits_q, lse_q, tokens, temp, seed, emitted, accept)
         else:
             dr.draft(x, new_feats=new, tokens=tokens)
-            fm.fm_verify(T, tokens, emitted, accept, best)
+            dr.verify(T, tokens, emitted, accept, best)
 
     sets = []   # (target logits, seed, planted accept lengths or None)
     if temp > 0:

@@ -261,6 +261,21 @@ fm_status fm_verify(const void *target_logits, fm_dtype dtype, int B, int K, int
                     const int32_t *draft, int32_t *emitted, int32_t *accept, int32_t *best,
                     void *stream);
 
+/* The same greedy verification for a handle's drafts (K = 16, V of the
+ * handle's configuration), with each target row read by 16 workgroups at once
+ * instead of one: the per-slice maxima go to the handle's verifier scratch and
+ * one more launch merges them, so the result is the one fm_verify gives on the
+ * same arguments (first maximum of each row; logits without NaN).  Rows that
+ * do not start on a 16-byte boundary take fm_verify's path.  Shares the
+ * scratch with fm_verify_sample: calls on one handle are ordered on one stream.
+ *   target_logits [B][17][V] (dtype), draft [B][16], emitted [B][17],
+ *   accept [B], best [1]: as for fm_verify.
+ * Requires 1 <= B <= max(max_branches, max_requests) (branches of one
+ * request, or requests).  Errors: FM_EINVAL, FM_ECAPACITY, FM_EHIP. */
+fm_status fm_verify_greedy(fm_handle *h, const void *target_logits, fm_dtype dtype, int B,
+                           const int32_t *draft, int32_t *emitted, int32_t *accept, int32_t *best,
+                           void *stream);
+
 /* Probabilistic verification at temperature > 0 (alphasignal.ai, "Why
  * drafting still costs time": lossless verification leaves the distribution
  * of the target's samples unchanged).  The speculative-sampling rule, with
@@ -279,8 +294,9 @@ fm_status fm_verify(const void *target_logits, fm_dtype dtype, int B, int K, int
  * Branches are verified independently (no branch selection: choosing among
  * sampled branches would change the output distribution).  K and V are the
  * handle's; scratch lives in the handle's workspace, so calls on one handle
- * must not overlap.  Errors: FM_EINVAL, FM_ECAPACITY (B > max_branches),
- * FM_EHIP. */
+ * must not overlap.  B counts branches of one request or, on a handle of
+ * several requests, requests.  Errors: FM_EINVAL, FM_ECAPACITY (B above
+ * max(max_branches, max_requests)), FM_EHIP. */
 fm_status fm_verify_sample(fm_handle *h, const void *target_logits, fm_dtype dtype, int B,
                            const float *draft_logits, const float *draft_lse, const int32_t *draft,
                            float temperature, uint64_t seed, int32_t *emitted, int32_t *accept,

@@ -88,6 +88,8 @@ def lib() -> ctypes.CDLL:
     L.fm_draft.restype = st
     L.fm_verify.argtypes = [vp, i, i, i, i, vp, vp, vp, vp, vp]
     L.fm_verify.restype = st
+    L.fm_verify_greedy.argtypes = [vp, vp, i, i, vp, vp, vp, vp, vp]
+    L.fm_verify_greedy.restype = st
     f32, u64 = ctypes.c_float, ctypes.c_uint64
     L.fm_draft_sample.argtypes = [vp, vp, i, vp, i, f32, u64, vp, vp, vp, vp]
     L.fm_draft_sample.restype = st
@@ -268,6 +270,15 @@ def fm_verify(target_logits, draft, emitted, accept, best, stream=None):
                            _ptr(draft), _ptr(emitted), _ptr(accept), _ptr(best), _stream(stream)))
 
 
+def fm_verify_greedy(h, target_logits, draft, emitted, accept, best, stream=None):
+    """fm_verify for a handle's drafts, each target row read by several
+    workgroups: target_logits [B][17][V]; draft [B][16] int32; outputs
+    emitted [B][17], accept [B], best [1] int32."""
+    B = int(target_logits.shape[0])
+    _check(lib().fm_verify_greedy(h, _ptr(target_logits), dtype_code(target_logits.dtype), B, _ptr(draft),
+                                  _ptr(emitted), _ptr(accept), _ptr(best), _stream(stream)))
+
+
 def fm_set_probe(h, kernel: int, ev_start=None, ev_stop=None):
     """ev_start/ev_stop: torch.cuda.Event(enable_timing=True) objects or raw
     hipEvent_t integers."""
@@ -344,6 +355,10 @@ class Drafter:
         lse = torch.empty(B, K, dtype=torch.float32, device=self.device)
         fm_draft_sample(self.handle, noise, temperature, seed, tokens, logits, lse, new_feats, stream)
         return tokens, logits, lse
+
+    def verify(self, target_logits, draft, emitted, accept, best, stream=None):
+        """Greedy verification through the handle (fm_verify_greedy)."""
+        fm_verify_greedy(self.handle, target_logits, draft, emitted, accept, best, stream)
 
     def verify_sample(self, target_logits, draft_logits, draft_lse, draft, temperature, seed, stream=None):
         """Returns (emitted, accept) of probabilistic verification."""

@@ -316,7 +316,7 @@ Layout make_layout(const fm_config& c) {
   L.partial = take(partial_bytes(c));
   L.lm_part = take((size_t)LM_GRID * Mb * 8);
   L.lm_lse = take((size_t)LM_GRID * Mb * 8);
-  L.vs = take(vs_scratch_bytes(c.max_branches, KB));
+  L.vs = take(vs_scratch_bytes(max_blocks(c), KB));  // branches of one request, or requests
   L.counters = take((size_t)N_COUNTER_SLOTS * COUNTER_STRIDE * 4);
   if (c.max_steps > 1) {
     L.dsoft = take(Mb * (size_t)c.V * es);
@@ -1027,6 +1027,24 @@ fm_status verify_impl(const void* tl, int B, int K, int V, const int32_t* draft,
   return FM_OK;
 }
 
+// greedy verification with VSL_SLICES workgroups per target row; the slice
+// keys live in the handle's verifier scratch (its slice-state area, which
+// holds at least VSL_SLICES 8-byte words per row)
+template <typename T>
+fm_status verify_sliced_impl(uint64_t* keys, const void* tl, int B, int K, int V, const int32_t* draft,
+                             int32_t* emitted, int32_t* accept, int32_t* best, hipStream_t st) {
+  static_assert(VS_MAX_SLICES >= VSL_SLICES, "slice keys overflow the verifier scratch");
+  const int VE = (int)(16 / sizeof(T));
+  const int slice = cdiv(cdiv(V, VSL_SLICES), VE) * VE;
+  hipLaunchKernelGGL((verify_slice_kernel<T>), dim3(VSL_SLICES, B * (K + 1)), dim3(VSL_THREADS), 0, st,
+                     reinterpret_cast<const T*>(tl), V, slice, keys);
+  FM_LAUNCHED("verify_slice_kernel");
+  hipLaunchKernelGGL(verify_merge_kernel, dim3(1), dim3(1024), 0, st, keys, VSL_SLICES, draft, B, K, emitted, accept,
+                     best);
+  FM_LAUNCHED("verify_merge_kernel");
+  return FM_OK;
+}
+
 template <typename T>
 fm_status verify_sample_impl(const VsScratch& sc, int V, const void* tl, int B, const float* Q, const float* lseQ,
                              const int32_t* draft, float tau, uint64_t seed, int32_t* emitted, int32_t* accept,
@@ -1347,14 +1365,40 @@ fm_status fm_verify(const void* target_logits, fm_dtype dtype, int B, int K, int
                           : verify_impl<float>(target_logits, B, K, V, draft, emitted, accept, best, st);
 }
 
+fm_status fm_verify_greedy(fm_handle* h, const void* target_logits, fm_dtype dtype, int B, const int32_t* draft,
+                           int32_t* emitted, int32_t* accept, int32_t* best, void* stream) {
+  g_err.clear();
+  if (!h) return fail(FM_EINVAL, "handle is NULL");
+  if (!target_logits || !draft || !emitted || !accept || !best)
+    return fail(FM_EINVAL, "a pointer argument is NULL");
+  if (dtype != FM_BF16 && dtype != FM_F32) return fail(FM_EINVAL, "dtype must be FM_BF16 or FM_F32");
+  if (B < 1 || B > 64) return fail(FM_EINVAL, "B must be in 1..64 (got %d)", B);
+  if (B > max_blocks(h->cfg))
+    return fail(FM_ECAPACITY, "B %d exceeds the handle's %d row blocks", B, max_blocks(h->cfg));
+  const int V = h->cfg.V;
+  if (reinterpret_cast<uintptr_t>(target_logits) % esize(dtype))
+    return fail(FM_EINVAL, "target_logits is not aligned to its element size");
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  // the sliced kernels read whole 16-byte vectors: every row must start on a
+  // 16-byte boundary; otherwise the one-workgroup-per-row path gives the same result
+  const bool vec_ok = reinterpret_cast<uintptr_t>(target_logits) % 16 == 0 && ((size_t)V * esize(dtype)) % 16 == 0;
+  if (!vec_ok)
+    return dtype == FM_BF16 ? verify_impl<bf16_t>(target_logits, B, KB, V, draft, emitted, accept, best, st)
+                            : verify_impl<float>(target_logits, B, KB, V, draft, emitted, accept, best, st);
+  uint64_t* keys = reinterpret_cast<uint64_t*>(vs_scratch_at(h->at<char>(h->lay.vs), max_blocks(h->cfg), KB).stats);
+  return dtype == FM_BF16 ? verify_sliced_impl<bf16_t>(keys, target_logits, B, KB, V, draft, emitted, accept, best, st)
+                          : verify_sliced_impl<float>(keys, target_logits, B, KB, V, draft, emitted, accept, best, st);
+}
+
 fm_status fm_verify_sample(fm_handle* h, const void* target_logits, fm_dtype dtype, int B, const float* draft_logits,
                            const float* draft_lse, const int32_t* draft, float temperature, uint64_t seed,
                            int32_t* emitted, int32_t* accept, void* stream) {
   g_err.clear();
   if (!h) return fail(FM_EINVAL, "handle is NULL");
   FM_TRY(check_verify_sample(target_logits, dtype, B, draft_logits, draft_lse, draft, temperature, emitted, accept));
-  if (B > h->cfg.max_branches) return fail(FM_ECAPACITY, "B %d exceeds max_branches %d", B, h->cfg.max_branches);
-  const VsScratch sc = vs_scratch_at(h->at<char>(h->lay.vs), h->cfg.max_branches, KB);
+  if (B > max_blocks(h->cfg))
+    return fail(FM_ECAPACITY, "B %d exceeds the handle's %d row blocks", B, max_blocks(h->cfg));
+  const VsScratch sc = vs_scratch_at(h->at<char>(h->lay.vs), max_blocks(h->cfg), KB);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   return dtype == FM_BF16 ? verify_sample_impl<bf16_t>(sc, h->cfg.V, target_logits, B, draft_logits, draft_lse,
                                                        draft, temperature, seed, emitted, accept, st)

@@ -99,6 +99,105 @@ __global__ __launch_bounds__(64) void verify_prefix_kernel(const int32_t* draft,
 }
 
 
+// ------------------------------------------------- greedy, several workgroups per row
+// The same verification with each target row split into S contiguous slices
+// of `slice` elements (a multiple of the vector width; the caller guarantees
+// 16-byte aligned rows and V a multiple of the vector width): workgroup
+// (s, row) writes the slice's best 64-bit key to keys[row][s]; then one
+// workgroup merges each row's keys (max of the keys: independent of order)
+// and runs the prefix, emitted tokens, accept and best branch.  Each thread
+// keeps its first maximum as the one-workgroup argmax does, so both agree on
+// every input without NaN.
+constexpr int VSL_THREADS = 256;
+constexpr int VSL_SLICES = 16;
+template <typename T>
+__global__ __launch_bounds__(VSL_THREADS) void verify_slice_kernel(const T* logits, int V, int slice,
+                                                                   uint64_t* keys) {
+  typedef typename Vec<T>::type VT;
+  constexpr int VE = Vec<T>::N;
+  constexpr int U = 4;  // 16-byte loads in flight per thread
+  __shared__ uint64_t wk[VSL_THREADS / 64];
+  const int s = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
+  const T* row = logits + (size_t)r * V;
+  const int v0 = s * slice, v1 = min(V, v0 + slice);
+  const int nvec = v1 > v0 ? (v1 - v0) / VE : 0;
+  const VT* body = reinterpret_cast<const VT*>(row + v0);
+  float bv = -INFINITY;
+  int bi = -1;
+  auto visit = [&](float v, int idx) {
+    if (bi < 0 || v > bv) {
+      bv = v;
+      bi = idx;
+    }
+  };
+  int i = tid;
+  for (; i + (U - 1) * VSL_THREADS < nvec; i += U * VSL_THREADS) {
+    VT v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = body[i + u * VSL_THREADS];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int base = v0 + (i + u * VSL_THREADS) * VE;
+#pragma unroll
+      for (int e = 0; e < VE; ++e) visit(velem(v[u], e), base + e);
+    }
+  }
+  for (; i < nvec; i += VSL_THREADS) {
+    const VT v = body[i];
+    const int base = v0 + i * VE;
+#pragma unroll
+    for (int e = 0; e < VE; ++e) visit(velem(v, e), base + e);
+  }
+  uint64_t best = bi >= 0 ? argmax_key(bv, (uint32_t)bi) : 0ull;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) best = umax64(best, shfl_xor_u64(best, o));
+  const int lane = tid & 63, wave = tid >> 6;
+  if (lane == 0) wk[wave] = best;
+  __syncthreads();
+  if (tid == 0) {
+    uint64_t k = 0ull;
+    for (int w = 0; w < VSL_THREADS / 64; ++w) k = umax64(k, wk[w]);
+    keys[(size_t)r * VSL_SLICES + s] = k;
+  }
+}
+
+// One workgroup: lane group of 16 per target row merges that row's slice keys
+// (rows r, r + 64, ...), then one thread per branch runs the prefix.
+__global__ __launch_bounds__(1024) void verify_merge_kernel(const uint64_t* keys, int S, const int32_t* draft, int B,
+                                                            int K, int32_t* emitted, int32_t* accept, int32_t* best) {
+  __shared__ int32_t y[64 * 65];
+  __shared__ int ns[64];
+  const int t = threadIdx.x, rows = B * (K + 1);
+  for (int r = t / 16; r < rows; r += 1024 / 16) {
+    uint64_t k = (t % 16) < S ? keys[(size_t)r * VSL_SLICES + (t % 16)] : 0ull;
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) k = umax64(k, shfl_xor_u64(k, o));
+    if (t % 16 == 0) y[r] = (int32_t)argmax_key_index(k);
+  }
+  __syncthreads();
+  if (t < 64) {
+    int n = -1;
+    if (t < B) {
+      const int32_t* yr = y + t * (K + 1);
+      const int32_t* dr = draft + (size_t)t * K;
+      n = 0;
+      while (n < K && dr[n] == yr[n]) ++n;
+      int32_t* row = emitted + (size_t)t * (K + 1);
+      for (int i = 0; i <= K; ++i) row[i] = i < n ? dr[i] : (i == n ? yr[n] : -1);
+      accept[t] = n;
+    }
+    ns[t] = n;
+  }
+  __syncthreads();
+  if (t == 0) {
+    int bi = 0;
+    for (int i = 1; i < B; ++i)
+      if (ns[i] > ns[bi]) bi = i;
+    best[0] = bi;
+  }
+}
+
+
 // ------------------------------------------------------------ temperature > 0
 // Probabilistic verification (speculative sampling) of B branches:
 //   p_j = softmax(T_j / tau) for target rows j = 0..K, q_i = softmax(Q_i / tau)

@@ -68,6 +68,7 @@ def test_null_and_range_checks_return_einval():
     assert L.fm_draft(null, dummy, 1, null, 0, dummy, null, null, null) == fm.FM_EINVAL
     assert L.fm_verify_sample(null, dummy, fm.FM_BF16, 1, dummy, dummy, dummy, 1.0, 0, dummy, dummy,
                               null) == fm.FM_EINVAL
+    assert L.fm_verify_greedy(null, dummy, fm.FM_BF16, 1, dummy, dummy, dummy, dummy, null) == fm.FM_EINVAL
     assert L.fm_context_length(null) == -1
     assert L.fm_context_truncate(null, 0, null) == fm.FM_EINVAL
     assert L.fm_context_truncate_req(null, 0, 0, null) == fm.FM_EINVAL

@@ -1,4 +1,5 @@
-"""GPU parity of fm_verify against the oracle's verifier (bit-exact)."""
+"""GPU parity of fm_verify and fm_verify_greedy against the oracle's verifier
+(bit-exact)."""
 import itertools
 import json
 import os
@@ -13,7 +14,7 @@ import synth
 pytestmark = pytest.mark.gpu
 
 fm = pytest.importorskip("step_flow_map_amd")
-from gpu_util import to_dev  # noqa: E402
+from gpu_util import make_drafter, to_dev  # noqa: E402
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "new_york.json")
 
@@ -92,3 +93,79 @@ def test_ties_and_signed_zero():
     T = synth.make_target_logits(cfg, 1)
     T[0, :, ::3] = T[0, :, 0:1]               # heavy ties at the row value of column 0
     _assert_same(T, np.zeros((1, 16), dtype=np.int64))
+
+
+# ---------------------------------------------------------------- fm_verify_greedy
+# The handle's sliced verifier (16 workgroups per target row) against the
+# oracle and, bit for bit, against fm_verify on the same buffers.
+
+def _greedy_drafter(V, dtype, B=4):
+    cfg = synth.CONFIGS["tiny"].with_(V=V, dtype=dtype, B=B)
+    return cfg, make_drafter(cfg, synth.make_weights(cfg), C_max=32, max_branches=B)
+
+
+def _greedy_vs_both(dr, Td, drafts):
+    B, K1, _ = Td.shape
+    d = torch.from_numpy(drafts.astype(np.int32)).cuda()
+    em = torch.full((B, K1), -7, dtype=torch.int32, device="cuda")
+    acc = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+    best = torch.full((1,), -7, dtype=torch.int32, device="cuda")
+    dr.verify(Td, d, em, acc, best)
+    e1, a1, b1 = fm.verify(Td, d)
+    torch.cuda.synchronize()
+    assert torch.equal(em, e1) and torch.equal(acc, a1) and torch.equal(best, b1)
+    re, ra, rb = _ref(Td.float().cpu().numpy(), drafts)
+    assert np.array_equal(acc.cpu().numpy(), ra) and np.array_equal(em.cpu().numpy(), re)
+    assert int(best.cpu()[0]) == rb
+
+
+# 151936 bf16: 16 slices of 9496; 1000: slices of 64 with the last one
+# short; 24 bf16 and 20 f32: slices of one vector, most of them empty
+@pytest.mark.parametrize("V,dtype", [(151936, "bf16"), (151936, "f32"), (1000, "bf16"), (1000, "f32"),
+                                     (24, "bf16"), (20, "f32")])
+def test_greedy_sliced_matches_fm_verify(V, dtype):
+    print(f"[verify_greedy] V={V} {dtype}", flush=True)
+    cfg, dr = _greedy_drafter(V, dtype)
+    rng = np.random.default_rng(V + 7)
+    for B, accepts in ((4, (0, 16, 9, 16)), (1, (5,)), (3, (16, 2, 16))):
+        T = synth.make_target_logits(cfg, B)
+        drafts = rng.integers(0, V, (B, cfg.K))
+        for b, n in enumerate(accepts):
+            T[b] = synth.plant(T[b], drafts[b], n)
+        _greedy_vs_both(dr, to_dev(T), drafts)
+
+
+def test_greedy_sliced_ties_across_slices():
+    cfg, dr = _greedy_drafter(151936, "bf16", B=2)
+    T = synth.make_target_logits(cfg, 2)
+    # every third column ties the row's column-0 value, and row maxima planted
+    # at equal values in two slices: the lowest index must win across slices
+    T[0, :, ::3] = T[0, :, 0:1]
+    lo, hi = synth.to_bf16_bits(np.float32([-1.0, 4.0]))
+    T[1, :, :] = lo
+    T[1, :, 150000] = hi
+    T[1, :, 9500] = hi
+    T[1, 5, 3] = hi
+    drafts = np.zeros((2, 16), dtype=np.int64)
+    drafts[1, :] = 9500
+    _greedy_vs_both(dr, to_dev(T), drafts)
+
+
+def test_greedy_unaligned_view_takes_the_one_workgroup_path():
+    cfg, dr = _greedy_drafter(1000, "bf16", B=2)
+    T = synth.make_target_logits(cfg, 2)
+    flat = torch.empty(2 * 17 * 1000 + 1, dtype=torch.bfloat16, device="cuda")
+    view = flat[1:].view(2, 17, 1000)    # 2-byte aligned only
+    view.copy_(to_dev(T))
+    drafts = np.random.default_rng(3).integers(0, 1000, (2, 16))
+    _greedy_vs_both(dr, view, drafts)
+
+
+def test_greedy_rejects_more_branches_than_the_handle():
+    cfg, dr = _greedy_drafter(1000, "bf16", B=2)
+    T = to_dev(synth.make_target_logits(cfg, 3))
+    d = torch.zeros(3, 16, dtype=torch.int32, device="cuda")
+    out = torch.empty(3, 17, dtype=torch.int32, device="cuda")
+    with pytest.raises(fm.FlashMapError) as e:
+        dr.verify(T, d, out, out[:, 0].contiguous(), out[0, :1].contiguous())
+    assert e.value.status == fm.FM_ECAPACITY
