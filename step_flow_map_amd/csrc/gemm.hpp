@@ -276,10 +276,15 @@ struct LnArgs {
 // waves then reduce through LDS in wave order and run the epilogue.
 //
 // With LN the k range is at most NW chunks, so each wave holds one chunk of
-// the 16 residual rows; it computes the mean and the sum of squared deviations
-// of its columns per row, the workgroup combines the waves' pairs in wave
-// order (pairwise update of Chan, Golub and LeVeque), and every wave then
-// normalises, modulates and rounds its own fragments.
+// the 16 residual rows.  It loads the chunk coalesced (a 1 KB row piece per
+// instruction for bf16 storage, two 512-byte row pieces for float32: every
+// lane holds 4 consecutive columns of one row), sums its columns per row for
+// the mean and then for the sum of squared deviations (through its LDS tile,
+// in lane order, so each value has one summation order), the workgroup
+// combines the waves' pairs in wave order (pairwise update of Chan, Golub and
+// LeVeque), and every wave then normalises and modulates its values, rounds
+// them to the storage type into its LDS tile in the weights' layout, and
+// reads its MFMA fragments back from there.
 template <typename T, int MT, int NW, int TT, int EPI, bool LN>
 __global__ __launch_bounds__(NW * 64) void gemm_tg_kernel(GemmArgs g, EpiParams e, LnArgs ln) {
   typedef typename Vec<T>::type VT;
@@ -288,11 +293,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_tg_kernel(GemmArgs g, EpiParams 
   constexpr int ELEMS = TT * MT * 256;  // outputs: TT tiles x MT*16 rows x 16 columns
   constexpr int RED_U4 = NW * ELEMS / 4;
   constexpr int TILE_U4 = NW * 512;
-  constexpr int KMAX = NW * KC;                            // LN: longest k range
-  constexpr int MODQ = LN ? (KMAX / 4 + NW * 64 - 1) / (NW * 64) : 1;  // float4 of scale (and shift) per thread
-  constexpr int SHIFT_OFF = MODQ * NW * 64 * 4;
   __shared__ uint4 smem[TILE_U4 > RED_U4 ? TILE_U4 : RED_U4];
-  __shared__ __align__(16) float smod[LN ? 2 * MODQ * NW * 64 * 4 : 1];  // scale, then shift at SHIFT_OFF
   __shared__ float sstat[LN ? NW : 1][16][2];              // per wave and row: mean, M2
   // LN with context rows: their fragments wait in LDS (wave-private) rather
   // than in registers while the weights are in flight
@@ -336,23 +337,20 @@ __global__ __launch_bounds__(NW * 64) void gemm_tg_kernel(GemmArgs g, EpiParams 
     // ---- issue: residual rows, modulation, A rows, weights.  Addresses are
     // clamped in range and nothing here is conditional, so no load waits for
     // another one before the statistics need the residual rows.
-    constexpr int HQ = LN ? VE / 4 : 1;  // float4 of residual per k run
-    float4 hv[LN ? 8 : 1][HQ];
-    float4 mv[MODQ], mv2[MODQ];
+    // LN: float4 element i of the lane covers row hrow(i), columns
+    // k0 + hcol .. + 3 of the chunk (the same columns in every row it holds)
+    constexpr int HN = LN ? KC / 16 : 1;  // float4 per lane: 16 rows x KC floats / (64 lanes x 4)
+    const int hcol = (lane * 4) % KC;
+    auto hrow = [&](int i) { return (i * 256 + lane * 4) / KC; };
+    const bool hok = has && k0 + hcol < k_end;
+    float4 hv[HN];
+    float4 msc = float4{0.f, 0.f, 0.f, 0.f}, msh = float4{0.f, 0.f, 0.f, 0.f};
     if constexpr (LN) {
-      const float* hr = ln.h + (size_t)j * ln.ldh;
+      const int kc = hok ? k0 + hcol : 0;
 #pragma unroll
-      for (int st = 0; st < 8; ++st)
-#pragma unroll
-        for (int q = 0; q < HQ; ++q)
-          hv[st][q] = *reinterpret_cast<const float4*>(hr + (kok[st] ? k0 + (4 * st + grp) * VE : 0) + 4 * q);
-      const int kq = g.K / 4;
-#pragma unroll
-      for (int q = 0; q < MODQ; ++q) {
-        const int idx = min(tid + q * NW * 64, kq - 1);
-        mv[q] = reinterpret_cast<const float4*>(ln.scale)[idx];
-        mv2[q] = reinterpret_cast<const float4*>(ln.shift)[idx];
-      }
+      for (int i = 0; i < HN; ++i) hv[i] = *reinterpret_cast<const float4*>(ln.h + (size_t)hrow(i) * ln.ldh + kc);
+      msc = *reinterpret_cast<const float4*>(ln.scale + kc);
+      msh = *reinterpret_cast<const float4*>(ln.shift + kc);
     }
     VT af[MT][8];
 #pragma unroll
@@ -371,41 +369,56 @@ __global__ __launch_bounds__(NW * 64) void gemm_tg_kernel(GemmArgs g, EpiParams 
 #pragma unroll
         for (int st = 0; st < 8; ++st) sctx[wave][st][lane] = __builtin_bit_cast(uint4, af[1][st]);
       }
-      // smod holds exactly MODQ float4 of each per thread: entries past K are never read
+      const float mk = hok ? 1.f : 0.f;
+      // Row sums of the wave's columns: every lane writes its per-row partials
+      // (a sum of its 4 columns) into the wave's tile, rows LPR + 4 floats
+      // apart, and lane r (< 16) adds row r's partials in lane order.  The
+      // results reach every lane by readlane.
+      constexpr int LPR = KC / 4;  // lanes holding one row
+      float* red = reinterpret_cast<float*>(wt);
+      const int pos = lane % LPR;
+      auto row_sums = [&](const float (&v)[HN]) -> float {
 #pragma unroll
-      for (int q = 0; q < MODQ; ++q) {
-        *reinterpret_cast<float4*>(&smod[4 * (tid + q * NW * 64)]) = mv[q];
-        *reinterpret_cast<float4*>(&smod[SHIFT_OFF + 4 * (tid + q * NW * 64)]) = mv2[q];
-      }
-      // this wave's columns of row j: mean and sum of squared deviations
-      const int nw = has ? min(KC, g.K - k0) : 0;
-      float sum = 0.f;
+        for (int i = 0; i < HN; ++i) red[hrow(i) * (LPR + 4) + pos] = v[i];
+        wave_lds_sync();
+        const float4* rr4 = reinterpret_cast<const float4*>(red + (lane & 15) * (LPR + 4));
+        float acc = 0.f;
 #pragma unroll
-      for (int st = 0; st < 8; ++st) {
-        const float mk = kok[st] ? 1.f : 0.f;
-#pragma unroll
-        for (int q = 0; q < HQ; ++q) sum += mk * ((hv[st][q].x + hv[st][q].y) + (hv[st][q].z + hv[st][q].w));
-      }
-      sum += __shfl_xor(sum, 16, 64);
-      sum += __shfl_xor(sum, 32, 64);
-      const float mw = sum / (float)max(nw, 1);
-      float m2 = 0.f;
-#pragma unroll
-      for (int st = 0; st < 8; ++st) {
-        const float mk = kok[st] ? 1.f : 0.f;
-#pragma unroll
-        for (int q = 0; q < HQ; ++q) {
-          const float a = hv[st][q].x - mw, b = hv[st][q].y - mw, cc = hv[st][q].z - mw, d = hv[st][q].w - mw;
-          m2 += mk * ((a * a + b * b) + (cc * cc + d * d));
+        for (int q = 0; q < LPR / 4; ++q) {
+          const float4 t = rr4[q];
+          acc += ((t.x + t.y) + (t.z + t.w));
         }
+        wave_lds_sync();
+        return acc;
+      };
+      // value i of this lane belongs to row hrow(i): bf16 i, float32 2i + (lane >> 5)
+      auto bcast = [&](float x, int i) -> float {
+        if constexpr (LPR == 64) {
+          return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), i));
+        } else {
+          const float lo = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 2 * i));
+          const float hi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 2 * i + 1));
+          return (lane >> 5) ? hi : lo;
+        }
+      };
+      const int nw = has ? min(KC, g.K - k0) : 0;
+      float part[HN];
+#pragma unroll
+      for (int i = 0; i < HN; ++i) part[i] = mk * ((hv[i].x + hv[i].y) + (hv[i].z + hv[i].w));
+      const float mw_row = row_sums(part) / (float)max(nw, 1);  // lane r: wave mean of row r
+#pragma unroll
+      for (int i = 0; i < HN; ++i) {
+        const float m = bcast(mw_row, i);
+        const float a = hv[i].x - m, b = hv[i].y - m, cc = hv[i].z - m, d = hv[i].w - m;
+        part[i] = mk * ((a * a + b * b) + (cc * cc + d * d));
       }
-      m2 += __shfl_xor(m2, 16, 64);
-      m2 += __shfl_xor(m2, 32, 64);
-      if (grp == 0) {
-        sstat[wave][j][0] = mw;
-        sstat[wave][j][1] = m2;
+      const float m2_row = row_sums(part);
+      if (lane < 16) {
+        sstat[wave][lane][0] = mw_row;
+        sstat[wave][lane][1] = m2_row;
       }
       lds_barrier();  // the weight loads stay in flight
+      // lane j (< 16) combines row j over the waves; the others mirror it
       float mean = 0.f, M2 = 0.f, n = 0.f;
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
@@ -418,28 +431,32 @@ __global__ __launch_bounds__(NW * 64) void gemm_tg_kernel(GemmArgs g, EpiParams 
         n = nn;
       }
       const float rstd = 1.f / sqrtf(M2 / (float)g.K + ln.eps);
+      // normalise, modulate, round, and place in the wave's tile as the
+      // weights' chunk layout (piece p of row r at r * 32 + (p ^ r))
 #pragma unroll
-      for (int st = 0; st < 8; ++st) {
-        const int k = kok[st] ? k0 + (4 * st + grp) * VE : 0;
-        float x[VE], y[VE];
-#pragma unroll
-        for (int q = 0; q < HQ; ++q) {
-          x[4 * q + 0] = hv[st][q].x;
-          x[4 * q + 1] = hv[st][q].y;
-          x[4 * q + 2] = hv[st][q].z;
-          x[4 * q + 3] = hv[st][q].w;
+      for (int i = 0; i < HN; ++i) {
+        const int rr = hrow(i);
+        const float m_r = bcast(mean, i), s_r = bcast(rstd, i);
+        const float y0 = ((hv[i].x - m_r) * s_r) * (1.f + msc.x) + msh.x;
+        const float y1 = ((hv[i].y - m_r) * s_r) * (1.f + msc.y) + msh.y;
+        const float y2 = ((hv[i].z - m_r) * s_r) * (1.f + msc.z) + msh.z;
+        const float y3 = ((hv[i].w - m_r) * s_r) * (1.f + msc.w) + msh.w;
+        if constexpr (sizeof(T) == 2) {
+          const int pc = lane >> 1;  // 16-byte piece of 8 columns; this lane holds half of it
+          uint2 u;
+          u.x = (uint32_t)f32_to_bf16(y0) | ((uint32_t)f32_to_bf16(y1) << 16);
+          u.y = (uint32_t)f32_to_bf16(y2) | ((uint32_t)f32_to_bf16(y3) << 16);
+          reinterpret_cast<uint2*>(wt + rr * 32 + (pc ^ rr))[lane & 1] = u;
+        } else {
+          const int pc = lane & 31;
+          wt[rr * 32 + (pc ^ rr)] = make_uint4(__float_as_uint(y0), __float_as_uint(y1), __float_as_uint(y2),
+                                               __float_as_uint(y3));
         }
-#pragma unroll
-        for (int q = 0; q < VE / 4; ++q) {
-          const float4 sc = *reinterpret_cast<const float4*>(&smod[k + 4 * q]);
-          const float4 sh = *reinterpret_cast<const float4*>(&smod[SHIFT_OFF + k + 4 * q]);
-          y[4 * q + 0] = ((x[4 * q + 0] - mean) * rstd) * (1.f + sc.x) + sh.x;
-          y[4 * q + 1] = ((x[4 * q + 1] - mean) * rstd) * (1.f + sc.y) + sh.y;
-          y[4 * q + 2] = ((x[4 * q + 2] - mean) * rstd) * (1.f + sc.z) + sh.z;
-          y[4 * q + 3] = ((x[4 * q + 3] - mean) * rstd) * (1.f + sc.w) + sh.w;
-        }
-        af[0][st] = pack_vec<T>(y);
       }
+      wave_lds_sync();
+#pragma unroll
+      for (int st = 0; st < 8; ++st) af[0][st] = as_vec<T>(chunk_frag(wt, st));
+      wave_lds_sync();
     }
     if (!has) break;
 #pragma unroll

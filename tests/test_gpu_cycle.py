@@ -5,7 +5,13 @@ target token).  The context length lives on the device, so every replay writes
 its new context rows after the previous ones and attends over the grown
 context; each cycle is matched against the oracle drafting over every row so
 far.  Each cycle appends n + 1 rows for the n = 7 tokens its target logits
-accept, plus the target's own token."""
+accept, plus the target's own token.
+
+Every replay is one draft: its logits are held to the contract and the
+regression bound, and its tokens must match the oracle's except at near-ties
+inside the fixed window, at most one per draft.  (The single-draft parity
+tests also re-run a case with a near-tie on the next noise draw; four chained
+drafts would make that re-run itself a coin toss at the bf16 error level.)"""
 import numpy as np
 import pytest
 import torch
@@ -16,7 +22,7 @@ import synth
 pytestmark = pytest.mark.gpu
 
 fm = pytest.importorskip("step_flow_map_amd")
-from gpu_util import check_logits, check_tokens, exact_or_reseed, make_drafter, to_dev  # noqa: E402
+from gpu_util import check_logits, check_tokens, make_drafter, to_dev  # noqa: E402
 
 TINY = synth.CONFIGS["tiny"]
 ACCEPT = 7            # planted accepted prefix of every cycle
@@ -58,7 +64,7 @@ def test_one_graph_serves_a_growing_context(cfg):
     accept = torch.empty(1, dtype=torch.int32, device=dev)
     best = torch.empty(1, dtype=torch.int32, device=dev)
 
-    def case(draw):
+    def run(draw):
         dr.truncate(0)
         dr.append(to_dev(feats[:cfg.c_prefill]))
         torch.cuda.synchronize()
@@ -69,7 +75,6 @@ def test_one_graph_serves_a_growing_context(cfg):
         # the capture ran nothing: reload the host mirror from the device
         dr.sync_context()
         assert dr.context_length == cfg.c_prefill
-        ties = []
         for k in range(CYCLES):
             C = cfg.c_prefill + (k + 1) * ROWS
             noise = synth.make_noise(cfg, 1, 1 + CYCLES * draw + k)
@@ -83,7 +88,7 @@ def test_one_graph_serves_a_growing_context(cfg):
             lg, tk = logits.cpu().numpy()[0], tok.cpu().numpy()[0]
             rel = check_logits(lg, ref["logits"], cfg.dtype, f"cycle {k}:")
             cyc = check_tokens(tk, lg, ref["logits"], ref["tokens"], cfg.dtype)
-            ties += [(k,) + t for t in cyc]
+            assert len(cyc) <= 1, f"cycle {k}: {len(cyc)} near-ties in one draft: {cyc}"
             # the verifier on the same replay: the oracle's outcome for the GPU's draft
             n, em = oracle.verify(T, tk)
             assert int(accept.cpu()[0]) == n and emitted.cpu().numpy()[0, :n + 1].tolist() == em
@@ -91,7 +96,8 @@ def test_one_graph_serves_a_growing_context(cfg):
                 assert n == ACCEPT
             dr.sync_context()
             assert dr.context_length == C
-            print(f"  draw {draw} cycle {k}: context {C}, logit error {rel:.2e}, accepted {n}", flush=True)
+            print(f"  draw {draw} cycle {k}: context {C}, logit error {rel:.2e}, accepted {n}, "
+                  f"near-ties {cyc}", flush=True)
         # one more replay passes the capacity: the length stops at C_max, the rows
         # past it are dropped, and the sync reports it
         g.replay()
@@ -100,6 +106,5 @@ def test_one_graph_serves_a_growing_context(cfg):
         assert e.value.status == fm.FM_ECAPACITY
         assert dr.context_length == C_max
         dr.sync_context()   # the flag was cleared
-        return ties
 
-    exact_or_reseed(case, cfg.name)
+    run(0)
