@@ -153,12 +153,13 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs g, EpiParams e) 
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // With one row tile a chunk's weights and the matching A fragments are
-  // loaded together, one chunk ahead of the MFMAs, so neither latency is
-  // exposed; more row tiles load A at use, which keeps the register count low
-  // enough for two workgroups per CU.
+  // With one row tile a chunk's weights and the matching A rows are loaded
+  // together (both coalesced), one chunk ahead of the MFMAs, so neither
+  // latency is exposed; the A rows reach their fragment layout through the
+  // wave's tile before the weights do.  More row tiles load A fragments at
+  // use, which keeps the register count low enough for two workgroups per CU.
   constexpr bool PRE_A = MT == 1;
-  constexpr int AF = PRE_A ? MT : 1;
+  constexpr int AF = PRE_A ? 8 : 1;
   // A values outside [k_begin, k_end) or rows >= M are zeroed at use (this also
   // neutralises the clamped weight columns beyond the k range)
   auto a_ok = [&](int mt, int k0, int st) { return (k0 + (4 * st + grp) * VE) < k_end && aok[mt]; };
@@ -166,18 +167,21 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs g, EpiParams e) 
     const int k = k0 + (4 * st + grp) * VE;
     return vload<T>(arow[mt] + (a_ok(mt, k0, st) ? k : 0));
   };
-  auto load = [&](uint4 (&r)[8], VT (&af)[AF][8], int c) {
+  auto load = [&](uint4 (&r)[8], uint4 (&ra)[AF], int c) {
     const int k0 = k_begin + c * KC;
+    if constexpr (PRE_A) chunk_load_act<T>(ra, A, g.lda, 0, g.M, k0, k_end);
     chunk_load<T>(r, W, g.ldw, n0, g.N, k0, k_end);
-    if (PRE_A) {
-#pragma unroll
-      for (int st = 0; st < 8; ++st)
-#pragma unroll
-        for (int mt = 0; mt < AF; ++mt) af[mt][st] = a_load(mt, k0, st);
-    }
   };
-  auto process = [&](const uint4 (&r)[8], const VT (&af)[AF][8], int c) {
+  auto process = [&](const uint4 (&r)[8], const uint4 (&ra)[AF], int c) {
     const int k0 = k_begin + c * KC;
+    VT af[PRE_A ? 8 : 1];
+    if constexpr (PRE_A) {
+      chunk_to_lds(ra, wt);
+      wave_lds_sync();
+#pragma unroll
+      for (int st = 0; st < 8; ++st) af[st] = as_vec<T>(chunk_frag(wt, st));
+      wave_lds_sync();
+    }
     chunk_to_lds(r, wt);
     wave_lds_sync();
 #pragma unroll
@@ -185,7 +189,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs g, EpiParams e) 
       const VT b = as_vec<T>(chunk_frag(wt, st));
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const VT av = PRE_A ? af[PRE_A ? mt : 0][st] : a_load(mt, k0, st);
+        const VT av = PRE_A ? af[PRE_A ? st : 0] : a_load(mt, k0, st);
         mma(acc[mt], a_ok(mt, k0, st) ? av : vzero<VT>(), b);
       }
     }
@@ -193,7 +197,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs g, EpiParams e) 
   };
 
   uint4 r0[8], r1[8];
-  VT a0[AF][8], a1[AF][8];
+  uint4 a0[AF], a1[AF];
   if (wave < nch) load(r0, a0, wave);
   for (int c = wave; c < nch; c += 2 * NW) {
     if (c + NW < nch) load(r1, a1, c + NW);
@@ -295,11 +299,11 @@ __global__ __launch_bounds__(NW * 64) void gemm_tg_kernel(GemmArgs g, EpiParams 
   constexpr int TILE_U4 = NW * 512;
   __shared__ uint4 smem[TILE_U4 > RED_U4 ? TILE_U4 : RED_U4];
   __shared__ float sstat[LN ? NW : 1][16][2];              // per wave and row: mean, M2
-  // LN with context rows: their fragments wait in LDS (wave-private) rather
-  // than in registers while the weights are in flight
+  // LN with context rows: their chunk waits in LDS (a wave-private tile in
+  // the weights' layout) rather than as fragments in registers
   static_assert(!LN || MT <= 2, "fused LayerNorm supports at most 16 further rows");
   constexpr bool CTX_LDS = LN && MT == 2;
-  __shared__ uint4 sctx[CTX_LDS ? NW : 1][CTX_LDS ? 8 : 1][64];
+  __shared__ uint4 sctx[CTX_LDS ? NW : 1][CTX_LDS ? 512 : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int j = lane & 15, grp = lane >> 4;
@@ -314,14 +318,9 @@ __global__ __launch_bounds__(NW * 64) void gemm_tg_kernel(GemmArgs g, EpiParams 
 
   // rows of A: with LN, row tile 0 is computed and tiles 1.. read A rows 0..
   constexpr int MT0 = LN ? 1 : 0;
-  const T* arow[MT];
   bool aok[MT];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int m = mt * 16 + j;
-    aok[mt] = m < g.M;
-    arow[mt] = A + (size_t)(aok[mt] && mt >= MT0 ? m - 16 * MT0 : 0) * g.lda;
-  }
+  for (int mt = 0; mt < MT; ++mt) aok[mt] = mt * 16 + j < g.M;
   f32x4 acc[TT][MT];
 #pragma unroll
   for (int t = 0; t < TT; ++t)
@@ -352,23 +351,19 @@ __global__ __launch_bounds__(NW * 64) void gemm_tg_kernel(GemmArgs g, EpiParams 
       msc = *reinterpret_cast<const float4*>(ln.scale + kc);
       msh = *reinterpret_cast<const float4*>(ln.shift + kc);
     }
+    // A rows of the chunk in the weights' pattern; their fragments come back
+    // through LDS below
+    uint4 ra[MT][8];
+#pragma unroll
+    for (int mt = MT0; mt < MT; ++mt) chunk_load_act<T>(ra[mt], A, g.lda, (mt - MT0) * 16, g.M - 16 * MT0, k0, k_end);
     VT af[MT][8];
-#pragma unroll
-    for (int st = 0; st < 8; ++st) {
-      const int k = kok[st] ? k0 + (4 * st + grp) * VE : 0;
-#pragma unroll
-      for (int mt = MT0; mt < MT; ++mt) af[mt][st] = vload<T>(arow[mt] + k);
-    }
     uint4 r[TT][8];
 #pragma unroll
     for (int t = 0; t < TT; ++t) chunk_load<T>(r[t], W, g.ldw, n0 + 16 * t, g.N, k0, k_end);
     if constexpr (LN) {
       // every load above is issued before the statistics consume the first one
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (CTX_LDS) {
-#pragma unroll
-        for (int st = 0; st < 8; ++st) sctx[wave][st][lane] = __builtin_bit_cast(uint4, af[1][st]);
-      }
+      if constexpr (CTX_LDS) chunk_to_lds(ra[1], sctx[wave]);
       const float mk = hok ? 1.f : 0.f;
       // Row sums of the wave's columns: every lane writes its per-row partials
       // (a sum of its 4 columns) into the wave's tile, rows LPR + 4 floats
@@ -457,6 +452,15 @@ __global__ __launch_bounds__(NW * 64) void gemm_tg_kernel(GemmArgs g, EpiParams 
 #pragma unroll
       for (int st = 0; st < 8; ++st) af[0][st] = as_vec<T>(chunk_frag(wt, st));
       wave_lds_sync();
+    } else {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        chunk_to_lds(ra[mt], wt);
+        wave_lds_sync();
+#pragma unroll
+        for (int st = 0; st < 8; ++st) af[mt][st] = as_vec<T>(chunk_frag(wt, st));
+        wave_lds_sync();
+      }
     }
     if (!has) break;
 #pragma unroll
@@ -468,7 +472,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_tg_kernel(GemmArgs g, EpiParams 
         const VT b = as_vec<T>(chunk_frag(wt, st));
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-          const VT a = (CTX_LDS && mt == 1) ? as_vec<T>(sctx[wave][st][lane]) : af[mt][st];
+          const VT a = (CTX_LDS && mt == 1) ? as_vec<T>(chunk_frag(sctx[wave], st)) : af[mt][st];
           mma(acc[t][mt], (kok[st] && aok[mt]) ? a : vzero<VT>(), b);
         }
       }

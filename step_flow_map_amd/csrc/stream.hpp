@@ -8,7 +8,9 @@
 // of row r at slot r*32 + (p ^ r) (the XOR keeps the fragment reads free of
 // bank conflicts), and reads MFMA fragments back: step s (0..7) gives lane
 // (j, g) piece 4s+g of row j, i.e. k = (4s+g)*VE .. +VE-1 of weight row j.
-// The A operand of step s must use the same k.
+// The A operand of step s must use the same k; activation rows are staged
+// through the same tile layout (chunk_load_act), so both operands come from
+// coalesced loads.
 #pragma once
 #include "common.hpp"
 
@@ -44,6 +46,24 @@ __device__ __forceinline__ void chunk_load(uint4 (&r)[8], const T* W, size_t ldw
   for (int i = 0; i < 8; ++i) {
     const int row = n0 + 2 * i + half;
     r[i] = ldg_stream(W + (size_t)(row < N ? row : 0) * ldw + kc);
+  }
+}
+
+// The same pattern for activation rows r0.. of A (R rows, row stride lda),
+// with ordinary cached loads: every workgroup reads the same A.  Rows >= R
+// read row 0 and columns >= K read column 0 (both masked by the consumer).
+template <typename T>
+__device__ __forceinline__ void chunk_load_act(uint4 (&r)[8], const T* A, size_t lda, int r0, int R, int k0, int K) {
+  constexpr int VE = ChunkT<T>::VE;
+  const int lane = threadIdx.x & 63;
+  const int half = lane >> 5, p = lane & 31;
+  const int kk = k0 + p * VE;
+  const int kc = kk < K ? kk : 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int row = r0 + 2 * i + half;
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(A + (size_t)(row < R ? row : 0) * lda + kc);
+    r[i] = make_uint4(v[0], v[1], v[2], v[3]);
   }
 }
 
