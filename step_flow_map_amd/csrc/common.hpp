@@ -229,11 +229,15 @@ __device__ __forceinline__ bool arrive(uint32_t* counter, uint32_t expected, int
 constexpr int COUNTER_STRIDE = 32;
 
 // Ordering point between a wave's LDS writes and its reads of other lanes'
-// data.  No fence is needed: the compiler cannot prove the per-lane addresses
-// differ, so it keeps the accesses in program order, and the LDS executes one
-// wave's accesses in order.  (A release fence here would also wait for every
-// outstanding global load, draining the next chunk's prefetch.)
-__device__ __forceinline__ void wave_lds_sync() {}
+// data.  The LDS executes one wave's accesses in order, so the hardware needs
+// no wait; the wavefront-scope fence keeps the compiler from moving LDS
+// accesses across this point (it emits no instruction and, unlike a
+// workgroup-scope fence, waits for no outstanding global load), and the wave
+// barrier keeps the scheduler from doing so.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
 
 // Workgroup barrier that orders LDS accesses only.  __syncthreads() also waits
 // for every outstanding global load of the wave, which would drain loads that

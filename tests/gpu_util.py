@@ -35,6 +35,36 @@ def to_dev(a: np.ndarray, device="cuda") -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
 
 
+# Canary words around output buffers: every guarded output is allocated with
+# GUARD elements before and after it, filled with CANARY, and check_guards
+# asserts after the call that no kernel wrote outside the buffer.
+GUARD = 64
+CANARY = 0x5AA5C33C
+
+
+def guarded(*shape, dtype=torch.float32, device="cuda") -> torch.Tensor:
+    """Output buffer of `shape` (4-byte dtype) between two canary regions."""
+    n = int(np.prod(shape)) if shape else 1
+    raw = torch.full((n + 2 * GUARD,), CANARY, dtype=torch.int32, device=device)
+    body = raw[GUARD:GUARD + n]
+    if dtype != torch.int32:
+        body = body.view(dtype)
+    t = body.view(*shape)
+    t._canary_raw = raw
+    return t
+
+
+def check_guards(*tensors):
+    for t in tensors:
+        if t is None:
+            continue
+        raw = t._canary_raw.cpu().numpy()
+        lo, hi = raw[:GUARD], raw[-GUARD:]
+        assert (lo == CANARY).all() and (hi == CANARY).all(), (
+            f"a kernel wrote outside a {tuple(t.shape)} output: "
+            f"{int((lo != CANARY).sum())} words before it, {int((hi != CANARY).sum())} after")
+
+
 def binding_weights(w: dict, device="cuda") -> dict:
     out = {}
     for k, v in w.items():
@@ -60,12 +90,14 @@ def run_draft(dr: fm.Drafter, cfg, noise: np.ndarray, feats: np.ndarray, prefill
     new = to_dev(feats[prefill:]) if feats.shape[0] > prefill else None
     x = to_dev(noise)
     B = noise.shape[0]
-    logits = torch.empty(B, cfg.K, cfg.V, dtype=torch.float32, device=dev)
+    logits = guarded(B, cfg.K, cfg.V, device=dev)
+    tok = guarded(B, cfg.K, dtype=torch.int32, device=dev)
     hidden = None
     if want_hidden:
-        hidden = torch.empty(cfg.num_steps, cfg.L + 1, B, cfg.K, cfg.d, dtype=torch.float32, device=dev)
-    tok = dr.draft(x, new_feats=new, logits=logits, hidden=hidden)
+        hidden = guarded(cfg.num_steps, cfg.L + 1, B, cfg.K, cfg.d, device=dev)
+    dr.draft(x, new_feats=new, logits=logits, hidden=hidden, tokens=tok)
     torch.cuda.synchronize()
+    check_guards(logits, tok, hidden)
     return (tok.cpu().numpy(), logits.cpu().numpy(),
             None if hidden is None else hidden.cpu().numpy())
 

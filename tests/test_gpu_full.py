@@ -13,8 +13,8 @@ import synth
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
 fm = pytest.importorskip("step_flow_map_amd")
-from gpu_util import (binding_weights, check_logits, check_tokens, exact_or_reseed, make_drafter,  # noqa: E402
-                      to_dev)
+from gpu_util import (binding_weights, check_guards, check_logits, check_tokens, exact_or_reseed, guarded,  # noqa: E402
+                      make_drafter, to_dev)
 
 
 @pytest.mark.parametrize("name", ["qwen3_8b", "qwen3_4b", "qwen3_8b_2step", "qwen3_8b_tree4"])
@@ -31,9 +31,11 @@ def test_full_size_draft_and_verify(name):
         noise = synth.make_noise(cfg, draw=draw)
         dr.truncate(0)
         dr.append(to_dev(feats[:cfg.c_prefill]))
-        logits = torch.empty(cfg.B, cfg.K, cfg.V, device="cuda")
-        tok = dr.draft(to_dev(noise), new_feats=to_dev(feats[cfg.c_prefill:]), logits=logits)
+        logits = guarded(cfg.B, cfg.K, cfg.V)
+        tok = guarded(cfg.B, cfg.K, dtype=torch.int32)
+        dr.draft(to_dev(noise), new_feats=to_dev(feats[cfg.c_prefill:]), logits=logits, tokens=tok)
         torch.cuda.synchronize()
+        check_guards(logits, tok)
         tok, logits = tok.cpu().numpy(), logits.cpu().numpy()
         ties, worst, refs = [], 0.0, []
         for b in range(cfg.B):
@@ -81,9 +83,11 @@ def test_full_size_batch_of_four_requests():
             dr.truncate_req(r, 0)
             dr.append_req(r, to_dev(feats[r][:cfg.c_prefill]))
         new = np.concatenate([feats[r][cfg.c_prefill:] for r in range(R)])
-        logits = torch.empty(R, cfg.K, cfg.V, device="cuda")
-        tok = dr.draft_batch(to_dev(noise), new_feats=to_dev(new), n_new=[cfg.n_new] * R, logits=logits)
+        logits = guarded(R, cfg.K, cfg.V)
+        tok = guarded(R, cfg.K, dtype=torch.int32)
+        dr.draft_batch(to_dev(noise), new_feats=to_dev(new), n_new=[cfg.n_new] * R, logits=logits, tokens=tok)
         torch.cuda.synchronize()
+        check_guards(logits, tok)
         tok, logits = tok.cpu().numpy(), logits.cpu().numpy()
         for r in range(R):
             assert dr.context_length_req(r) == cfg.C

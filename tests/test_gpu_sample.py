@@ -18,8 +18,8 @@ import synth
 pytestmark = pytest.mark.gpu
 
 fm = pytest.importorskip("step_flow_map_amd")
-from gpu_util import (check_logits, check_sampled_tokens, exact_or_reseed, is_near_tie, make_drafter,  # noqa: E402
-                      ref_verify_sample, to_dev)
+from gpu_util import (check_guards, check_logits, check_sampled_tokens, exact_or_reseed, guarded,  # noqa: E402
+                      is_near_tie, make_drafter, ref_verify_sample, to_dev)
 
 S = oracle.sampling
 TINY = synth.CONFIGS["tiny"]
@@ -40,8 +40,12 @@ def _run_sample(cfg, tau, seed, B=1, draw=0):
     dr.set_schedule(cfg.times)
     dr.append(to_dev(feats[:cfg.c_prefill]))
     new = to_dev(feats[cfg.c_prefill:]) if feats.shape[0] > cfg.c_prefill else None
-    tok, logits, lse = dr.draft_sample(to_dev(noise), tau, seed, new_feats=new)
+    tok = guarded(B, cfg.K, dtype=torch.int32)
+    logits = guarded(B, cfg.K, cfg.V)
+    lse = guarded(B, cfg.K)
+    fm.fm_draft_sample(dr.handle, to_dev(noise), tau, seed, tok, logits, lse, new_feats=new)
     torch.cuda.synchronize()
+    check_guards(tok, logits, lse)
     return cfg, w, feats, noise, dr, tok, logits, lse
 
 
@@ -105,11 +109,12 @@ def _verify_handle(V, max_branches=4):
 
 def _gpu_verify_sample(h, T, Q, lseQ, d, tau, seed):
     B, K1, V = T.shape
-    emitted = torch.empty(B, K1, dtype=torch.int32, device="cuda")
-    accept = torch.empty(B, dtype=torch.int32, device="cuda")
+    emitted = guarded(B, K1, dtype=torch.int32)
+    accept = guarded(B, dtype=torch.int32)
     fm.fm_verify_sample(h, to_dev(T), to_dev(Q), to_dev(lseQ), torch.from_numpy(d.astype(np.int32)).cuda(),
                         tau, seed, emitted, accept)
     torch.cuda.synchronize()
+    check_guards(emitted, accept)
     return emitted.cpu().numpy(), accept.cpu().numpy()
 
 

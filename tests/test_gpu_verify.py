@@ -14,14 +14,19 @@ import synth
 pytestmark = pytest.mark.gpu
 
 fm = pytest.importorskip("step_flow_map_amd")
-from gpu_util import make_drafter, to_dev  # noqa: E402
+from gpu_util import check_guards, guarded, make_drafter, to_dev  # noqa: E402
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "new_york.json")
 
 
 def _gpu_verify(T: np.ndarray, drafts: np.ndarray):
-    e, a, b = fm.verify(to_dev(T), torch.from_numpy(drafts.astype(np.int32)).cuda())
+    B, K1, _ = T.shape
+    e = guarded(B, K1, dtype=torch.int32)
+    a = guarded(B, dtype=torch.int32)
+    b = guarded(1, dtype=torch.int32)
+    fm.fm_verify(to_dev(T), torch.from_numpy(drafts.astype(np.int32)).cuda(), e, a, b)
     torch.cuda.synchronize()
+    check_guards(e, a, b)
     return e.cpu().numpy(), a.cpu().numpy(), int(b.cpu().numpy()[0])
 
 
@@ -107,12 +112,13 @@ def _greedy_drafter(V, dtype, B=4):
 def _greedy_vs_both(dr, Td, drafts):
     B, K1, _ = Td.shape
     d = torch.from_numpy(drafts.astype(np.int32)).cuda()
-    em = torch.full((B, K1), -7, dtype=torch.int32, device="cuda")
-    acc = torch.full((B,), -7, dtype=torch.int32, device="cuda")
-    best = torch.full((1,), -7, dtype=torch.int32, device="cuda")
+    em = guarded(B, K1, dtype=torch.int32)
+    acc = guarded(B, dtype=torch.int32)
+    best = guarded(1, dtype=torch.int32)
     dr.verify(Td, d, em, acc, best)
     e1, a1, b1 = fm.verify(Td, d)
     torch.cuda.synchronize()
+    check_guards(em, acc, best)
     assert torch.equal(em, e1) and torch.equal(acc, a1) and torch.equal(best, b1)
     re, ra, rb = _ref(Td.float().cpu().numpy(), drafts)
     assert np.array_equal(acc.cpu().numpy(), ra) and np.array_equal(em.cpu().numpy(), re)
