@@ -246,6 +246,20 @@ fm_status fm_draft_sample(fm_handle *h, const void *noise, int B, const void *ne
 fm_status fm_draft_batch(fm_handle *h, const void *noise, int R, const void *new_feats, const int *n_new,
                          int32_t *tokens, float *logits, void *stream);
 
+/* fm_draft_batch at temperature > 0 (the probabilistic draft-sampling mode of
+ * feinterview.poetries.top, deployment list of the last section, for a batch
+ * of requests): request r samples its rows exactly as fm_draft_sample would
+ * for that request alone with seed seeds[r] and one branch, i.e. Gumbel noise
+ * of Philox counter (v, i, 0, 0) under key seeds[r].
+ *   temperature  > 0 and finite (host value)
+ *   seeds        HOST [R] 64-bit seeds, one per request
+ *   logits [R][K][V] and lse [R][K] float32 outputs, as for fm_draft_sample
+ * Other arguments and errors as for fm_draft_batch; FM_EINVAL also for a
+ * bad temperature or NULL seeds, logits or lse. */
+fm_status fm_draft_batch_sample(fm_handle *h, const void *noise, int R, const void *new_feats,
+                                const int *n_new, float temperature, const uint64_t *seeds,
+                                int32_t *tokens, float *logits, float *lse, void *stream);
+
 /* Greedy verification (feinterview.poetries.top, first section;
  * wire.sakhanda.co, "Что такое FlashMap?"; alphasignal.ai, "Why drafting
  * still costs time").  Stateless; needs no handle.
@@ -301,6 +315,20 @@ fm_status fm_verify_sample(fm_handle *h, const void *target_logits, fm_dtype dty
                            const float *draft_logits, const float *draft_lse, const int32_t *draft,
                            float temperature, uint64_t seed, int32_t *emitted, int32_t *accept,
                            void *stream);
+
+/* fm_verify_sample for the requests of a batch (alphasignal.ai, "Why
+ * drafting still costs time": the verification rule leaves each request's
+ * sampled output distribution unchanged): request r is verified exactly as
+ * fm_verify_sample would verify it alone with seed seeds[r] as branch 0
+ * (counters (0, i, 0, 2) and (v, n, 0, 1) under key seeds[r]).
+ *   R         requests, 1 <= R <= max_requests; arrays as for fm_verify_sample
+ *             with B = R
+ *   seeds     HOST [R] 64-bit seeds, one per request
+ * Errors as for fm_verify_sample; FM_EINVAL also for NULL seeds. */
+fm_status fm_verify_sample_batch(fm_handle *h, const void *target_logits, fm_dtype dtype, int R,
+                                 const float *draft_logits, const float *draft_lse, const int32_t *draft,
+                                 float temperature, const uint64_t *seeds, int32_t *emitted,
+                                 int32_t *accept, void *stream);
 
 /* fm_verify_sample for callers that cannot allocate device memory or hold a
  * handle (code under HIP graph capture, tight serving loops, harnesses that

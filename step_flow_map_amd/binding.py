@@ -95,6 +95,11 @@ def lib() -> ctypes.CDLL:
     L.fm_draft_sample.restype = st
     L.fm_verify_sample.argtypes = [vp, vp, i, i, vp, vp, vp, f32, u64, vp, vp, vp]
     L.fm_verify_sample.restype = st
+    u64p = ctypes.POINTER(ctypes.c_uint64)
+    L.fm_draft_batch_sample.argtypes = [vp, vp, i, vp, ctypes.POINTER(ctypes.c_int), f32, u64p, vp, vp, vp, vp]
+    L.fm_draft_batch_sample.restype = st
+    L.fm_verify_sample_batch.argtypes = [vp, vp, i, i, vp, vp, vp, f32, u64p, vp, vp, vp]
+    L.fm_verify_sample_batch.restype = st
     L.fm_verify_sample_noalloc.argtypes = [vp, i, i, i, i, vp, vp, vp, f32, u64, vp, vp, vp]
     L.fm_verify_sample_noalloc.restype = st
     L.fm_set_probe.argtypes = [vp, i, vp, vp]
@@ -248,6 +253,35 @@ def fm_verify_sample(h, target_logits, draft_logits, draft_lse, draft, temperatu
                                   _ptr(draft_logits), _ptr(draft_lse), _ptr(draft), float(temperature),
                                   int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(emitted), _ptr(accept),
                                   _stream(stream)))
+
+
+def _seeds(seeds):
+    arr = (ctypes.c_uint64 * len(seeds))(*[int(x) & 0xFFFFFFFFFFFFFFFF for x in seeds])
+    return arr
+
+
+def fm_draft_batch_sample(h, noise, temperature, seeds, tokens, logits, lse, new_feats=None, n_new=None,
+                          stream=None):
+    """Temperature > 0 batch draft: request r samples with seeds[r]; tokens
+    [R][K] int32, logits [R][K][V] and lse [R][K] float32 outputs."""
+    R = int(noise.shape[0])
+    if len(seeds) != R:
+        raise ValueError("one seed per request")
+    nn = (ctypes.c_int * R)(*([0] * R if n_new is None else [int(x) for x in n_new]))
+    _check(lib().fm_draft_batch_sample(h, _ptr(noise), R, _ptr(new_feats), nn, float(temperature), _seeds(seeds),
+                                       _ptr(tokens), _ptr(logits), _ptr(lse), _stream(stream)))
+
+
+def fm_verify_sample_batch(h, target_logits, draft_logits, draft_lse, draft, temperature, seeds, emitted, accept,
+                           stream=None):
+    """Probabilistic verify of the requests of a batch, request r with
+    seeds[r]: shapes as for fm_verify_sample with B = R."""
+    R = int(target_logits.shape[0])
+    if len(seeds) != R:
+        raise ValueError("one seed per request")
+    _check(lib().fm_verify_sample_batch(h, _ptr(target_logits), dtype_code(target_logits.dtype), R,
+                                        _ptr(draft_logits), _ptr(draft_lse), _ptr(draft), float(temperature),
+                                        _seeds(seeds), _ptr(emitted), _ptr(accept), _stream(stream)))
 
 
 def fm_verify_sample_noalloc(target_logits, draft_logits, draft_lse, draft, temperature, seed, emitted, accept,

@@ -675,8 +675,31 @@ struct Batch {
 struct Sampling {
   float tau;
   uint64_t seed;
-  float* lse;  // [M]
+  float* lse;                           // [M]
+  const uint64_t* req_seeds = nullptr;  // host [R]: one seed per request of a batch
+  int R = 0;
 };
+
+// the Philox keys of a draft's row blocks, or of a batch's requests
+BlockRng rng_shared(uint64_t seed) {
+  BlockRng r{};
+  r.lo[0] = (uint32_t)(seed & 0xFFFFFFFFu);
+  r.hi[0] = (uint32_t)(seed >> 32);
+  r.per_request = 0;
+  return r;
+}
+BlockRng rng_per_request(const uint64_t* seeds, int R) {
+  BlockRng r{};
+  for (int i = 0; i < R && i < 4; ++i) {
+    r.lo[i] = (uint32_t)(seeds[i] & 0xFFFFFFFFu);
+    r.hi[i] = (uint32_t)(seeds[i] >> 32);
+  }
+  r.per_request = 1;
+  return r;
+}
+BlockRng rng_of(const Sampling& smp) {
+  return smp.req_seeds ? rng_per_request(smp.req_seeds, smp.R) : rng_shared(smp.seed);
+}
 
 // probe: FM_PROBE_LM_HEAD brackets the LM head kernel alone (not the argmax
 // merge); -1 records nothing
@@ -688,8 +711,7 @@ fm_status lm_head(fm_handle* h, const void* z, int M, float* logits, int32_t* to
   const fm_config& c = h->cfg;
   LmArgs a{};
   a.tau = smp ? smp->tau : 0.f;
-  a.seed_lo = smp ? (uint32_t)(smp->seed & 0xFFFFFFFFu) : 0u;
-  a.seed_hi = smp ? (uint32_t)(smp->seed >> 32) : 0u;
+  a.rng = smp ? rng_of(*smp) : BlockRng{};
   a.K = KB;
   a.lse_part = smp ? h->at<float2>(h->lay.lm_lse) : nullptr;
   a.z = z;
@@ -1050,8 +1072,8 @@ fm_status verify_sliced_impl(uint64_t* keys, const void* tl, int B, int K, int V
 
 template <typename T>
 fm_status verify_sample_impl(const VsScratch& sc, int V, const void* tl, int B, const float* Q, const float* lseQ,
-                             const int32_t* draft, float tau, uint64_t seed, int32_t* emitted, int32_t* accept,
-                             hipStream_t st) {
+                             const int32_t* draft, float tau, const BlockRng& rng, int32_t* emitted,
+                             int32_t* accept, hipStream_t st) {
   VsArgs a{};
   a.T = tl;
   a.Q = Q;
@@ -1063,8 +1085,7 @@ fm_status verify_sample_impl(const VsScratch& sc, int V, const void* tl, int B, 
   a.S = std::min(VS_MAX_SLICES, cdiv(V, VS_SLICE));
   a.slice = cdiv(V, a.S);
   a.tau = tau;
-  a.seed_lo = (uint32_t)(seed & 0xFFFFFFFFu);
-  a.seed_hi = (uint32_t)(seed >> 32);
+  a.rng = rng;
   a.stats = sc.stats;
   a.lse_rows = sc.lse_rows;
   a.n_acc = sc.n_acc;
@@ -1297,9 +1318,9 @@ static fm_status draft_checked(fm_handle* h, const void* noise, int B, const voi
   return s;
 }
 
-fm_status fm_draft_batch(fm_handle* h, const void* noise, int R, const void* new_feats, const int* n_new,
-                         int32_t* tokens, float* logits, void* stream) {
-  g_err.clear();
+static fm_status draft_batch_checked(fm_handle* h, const void* noise, int R, const void* new_feats,
+                                     const int* n_new, int32_t* tokens, float* logits, void* stream,
+                                     const Sampling* smp) {
   if (!h) return fail(FM_EINVAL, "handle is NULL");
   const fm_config& c = h->cfg;
   if (!noise || !tokens) return fail(FM_EINVAL, "noise and tokens must not be NULL");
@@ -1325,14 +1346,34 @@ fm_status fm_draft_batch(fm_handle* h, const void* noise, int R, const void* new
   if (h->n_steps < 1) return fail(FM_ESTATE, "fm_draft_batch before fm_set_schedule");
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   fm_status s = c.dtype == FM_BF16
-                    ? draft_impl<bf16_t>(h, noise, R, new_feats, total, tokens, logits, nullptr, st, nullptr, &bt)
-                    : draft_impl<float>(h, noise, R, new_feats, total, tokens, logits, nullptr, st, nullptr, &bt);
+                    ? draft_impl<bf16_t>(h, noise, R, new_feats, total, tokens, logits, nullptr, st, smp, &bt)
+                    : draft_impl<float>(h, noise, R, new_feats, total, tokens, logits, nullptr, st, smp, &bt);
   if (s == FM_OK)
     for (int r = 0; r < R; ++r) {
       h->ctx_len[r] += bt.n_new[r];
       h->ctx_high[r] = std::max(h->ctx_high[r], h->ctx_len[r]);
     }
   return s;
+}
+
+fm_status fm_draft_batch(fm_handle* h, const void* noise, int R, const void* new_feats, const int* n_new,
+                         int32_t* tokens, float* logits, void* stream) {
+  g_err.clear();
+  return draft_batch_checked(h, noise, R, new_feats, n_new, tokens, logits, stream, nullptr);
+}
+
+fm_status fm_draft_batch_sample(fm_handle* h, const void* noise, int R, const void* new_feats, const int* n_new,
+                                float temperature, const uint64_t* seeds, int32_t* tokens, float* logits, float* lse,
+                                void* stream) {
+  g_err.clear();
+  if (!(temperature > 0.f) || !std::isfinite(temperature))
+    return fail(FM_EINVAL, "temperature must be finite and > 0");
+  if (!logits || !lse) return fail(FM_EINVAL, "logits and lse must not be NULL when sampling");
+  if (!seeds) return fail(FM_EINVAL, "seeds is NULL");
+  Sampling smp{temperature, 0, lse};
+  smp.req_seeds = seeds;
+  smp.R = R;
+  return draft_batch_checked(h, noise, R, new_feats, n_new, tokens, logits, stream, &smp);
 }
 
 fm_status fm_draft(fm_handle* h, const void* noise, int B, const void* new_feats, int n_new, int32_t* tokens,
@@ -1404,9 +1445,28 @@ fm_status fm_verify_sample(fm_handle* h, const void* target_logits, fm_dtype dty
   const VsScratch sc = vs_scratch_at(h->at<char>(h->lay.vs), max_blocks(h->cfg), KB);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   return dtype == FM_BF16 ? verify_sample_impl<bf16_t>(sc, h->cfg.V, target_logits, B, draft_logits, draft_lse,
-                                                       draft, temperature, seed, emitted, accept, st)
+                                                       draft, temperature, rng_shared(seed), emitted, accept, st)
                           : verify_sample_impl<float>(sc, h->cfg.V, target_logits, B, draft_logits, draft_lse,
-                                                      draft, temperature, seed, emitted, accept, st);
+                                                      draft, temperature, rng_shared(seed), emitted, accept, st);
+}
+
+fm_status fm_verify_sample_batch(fm_handle* h, const void* target_logits, fm_dtype dtype, int R,
+                                 const float* draft_logits, const float* draft_lse, const int32_t* draft,
+                                 float temperature, const uint64_t* seeds, int32_t* emitted, int32_t* accept,
+                                 void* stream) {
+  g_err.clear();
+  if (!h) return fail(FM_EINVAL, "handle is NULL");
+  if (!seeds) return fail(FM_EINVAL, "seeds is NULL");
+  FM_TRY(check_verify_sample(target_logits, dtype, R, draft_logits, draft_lse, draft, temperature, emitted, accept));
+  if (R > h->cfg.max_requests)
+    return fail(FM_ECAPACITY, "R %d exceeds max_requests %d", R, h->cfg.max_requests);
+  const VsScratch sc = vs_scratch_at(h->at<char>(h->lay.vs), max_blocks(h->cfg), KB);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const BlockRng rng = rng_per_request(seeds, R);
+  return dtype == FM_BF16 ? verify_sample_impl<bf16_t>(sc, h->cfg.V, target_logits, R, draft_logits, draft_lse,
+                                                       draft, temperature, rng, emitted, accept, st)
+                          : verify_sample_impl<float>(sc, h->cfg.V, target_logits, R, draft_logits, draft_lse,
+                                                      draft, temperature, rng, emitted, accept, st);
 }
 
 fm_status fm_verify_sample_noalloc(const void* target_logits, fm_dtype dtype, int B, int K, int V,
@@ -1425,9 +1485,9 @@ fm_status fm_verify_sample_noalloc(const void* target_logits, fm_dtype dtype, in
   const VsScratch sc = vs_scratch_at(base, B, K);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   return dtype == FM_BF16 ? verify_sample_impl<bf16_t>(sc, V, target_logits, B, draft_logits, draft_lse, draft,
-                                                       temperature, seed, emitted, accept, st)
+                                                       temperature, rng_shared(seed), emitted, accept, st)
                           : verify_sample_impl<float>(sc, V, target_logits, B, draft_logits, draft_lse, draft,
-                                                      temperature, seed, emitted, accept, st);
+                                                      temperature, rng_shared(seed), emitted, accept, st);
 }
 
 fm_status fm_set_probe(fm_handle* h, fm_probe_kernel kernel, void* ev_start, void* ev_stop) {

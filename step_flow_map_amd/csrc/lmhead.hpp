@@ -14,8 +14,9 @@
 // argmax_finalize_kernel reduces them.
 //
 // Temperature tau > 0 (draft sampling): the key of logit l at (row m, token
-// v) is l / tau + G, G the Gumbel noise of Philox counter (v, m % K, m / K,
-// stream 0), so the row's winner is a sample of softmax(l / tau); each
+// v) is l / tau + G, G the Gumbel noise of Philox counter (v, m % K, branch
+// word of block m / K, stream 0) under that block's key, so the row's winner
+// is a sample of softmax(l / tau); each
 // workgroup also writes the row's (max, sum of exp(l / tau - max)) and the
 // finalize kernel merges them into log sum_v exp(l_v / tau).
 #pragma once
@@ -33,7 +34,7 @@ struct LmArgs {
   float* logits;      // [M][V] or null
   uint64_t* partial;  // [M][gridDim.x]
   float tau;          // 0: greedy argmax; > 0: sampling at this temperature
-  uint32_t seed_lo, seed_hi;
+  BlockRng rng;       // key and branch word of each row block (tau > 0)
   int K;              // rows per branch
   float2* lse_part;   // [M][gridDim.x] (tau > 0)
 };
@@ -71,8 +72,9 @@ __device__ __forceinline__ void lm_visit(const LmArgs& g, float v, int m, int n,
   if (g.tau > 0.f) {
     const float x = v / g.tau;
     lse_add(lm, ls, x);
-    key = x + gumbel_of(philox_x0((uint32_t)n, (uint32_t)(m % g.K), (uint32_t)(m / g.K), RNG_DRAFT, g.seed_lo,
-                                  g.seed_hi));
+    uint32_t k0, k1, bw;
+    block_rng(g.rng, m / g.K, k0, k1, bw);
+    key = x + gumbel_of(philox_x0((uint32_t)n, (uint32_t)(m % g.K), bw, RNG_DRAFT, k0, k1));
   }
   best = umax64(best, argmax_key(key, (uint32_t)n));
   if (write && g.logits) g.logits[(size_t)m * g.V + n] = v;

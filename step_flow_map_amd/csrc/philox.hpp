@@ -55,6 +55,27 @@ __device__ __forceinline__ float gumbel_of(uint32_t x) {
   return -logf(e);
 }
 
+// Key and branch word of row block b.  The branches of one draft share the
+// caller's seed and differ in the branch word (the block index); the requests
+// of a batch each bring their own seed and draw with branch word 0, exactly
+// as each would drafted or verified alone.
+struct BlockRng {
+  uint32_t lo[4], hi[4];  // per request (per_request), else entry 0 for every block
+  int per_request;
+};
+__device__ __forceinline__ void block_rng(const BlockRng& r, int b, uint32_t& k0, uint32_t& k1, uint32_t& bw) {
+  if (!r.per_request) {
+    k0 = r.lo[0];
+    k1 = r.hi[0];
+    bw = (uint32_t)b;
+    return;
+  }
+  // selects, not a runtime index into the argument block
+  k0 = b == 0 ? r.lo[0] : b == 1 ? r.lo[1] : b == 2 ? r.lo[2] : r.lo[3];
+  k1 = b == 0 ? r.hi[0] : b == 1 ? r.hi[1] : b == 2 ? r.hi[2] : r.hi[3];
+  bw = 0u;
+}
+
 // Uniform in (0, 1) from the top 24 bits of the draw (exact in float32).
 __device__ __forceinline__ float uniform_of(uint32_t x) { return ((float)(x >> 8) + 0.5f) * 5.9604644775390625e-8f; }
 

@@ -219,7 +219,7 @@ struct VsArgs {
   const int32_t* draft;   // [B][K]
   int B, K, V, S, slice;  // S vocabulary slices of `slice` tokens
   float tau;
-  uint32_t seed_lo, seed_hi;
+  BlockRng rng;           // key and branch word of each branch
   float2* stats;          // [B*(K+1)][S]
   float* lse_rows;        // [B*(K+1)] log sum_v exp(T / tau) of every target row
   int32_t* n_acc;         // [B] accepted prefix
@@ -306,7 +306,9 @@ __global__ __launch_bounds__(VS_ACCEPT_THREADS) void vs_accept_kernel(VsArgs g) 
     if (tester) {
       const float lp = t_d / g.tau - slse[lane];
       const float lq = q_d / g.tau - lseq;
-      const float u = uniform_of(philox_x0(0u, (uint32_t)lane, (uint32_t)b, RNG_ACCEPT, g.seed_lo, g.seed_hi));
+      uint32_t k0, k1, bw;
+      block_rng(g.rng, b, k0, k1, bw);
+      const float u = uniform_of(philox_x0(0u, (uint32_t)lane, bw, RNG_ACCEPT, k0, k1));
       reject = !(u * expf(lq) < expf(lp));
     }
     const uint64_t rej = __ballot(reject);
@@ -339,6 +341,8 @@ __device__ __forceinline__ void block_max2(uint64_t& a, uint64_t& b) {
 template <typename T>
 __global__ __launch_bounds__(VS_THREADS) void vs_keys_kernel(VsArgs g) {
   const int s = blockIdx.x, b = blockIdx.y;
+  uint32_t rk0, rk1, bw;  // this branch's Philox key and branch word
+  block_rng(g.rng, b, rk0, rk1, bw);
   const int n = g.n_acc[b];
   const int r = b * (g.K + 1) + n;
   const float lseP = g.lse_rows[r];
@@ -361,7 +365,7 @@ __global__ __launch_bounds__(VS_THREADS) void vs_keys_kernel(VsArgs g) {
       const int v = base + u * VS_THREADS;
       if (v >= v1) continue;
       const float lp = x[u] / g.tau - lseP;
-      const float G = gumbel_of(philox_x0((uint32_t)v, (uint32_t)n, (uint32_t)b, RNG_CORRECT, g.seed_lo, g.seed_hi));
+      const float G = gumbel_of(philox_x0((uint32_t)v, (uint32_t)n, bw, RNG_CORRECT, rk0, rk1));
       k2 = umax64(k2, argmax_key(lp + G, (uint32_t)v));
       if (bonus) {
         k1 = umax64(k1, argmax_key(lp + G, (uint32_t)v));

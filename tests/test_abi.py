@@ -69,6 +69,12 @@ def test_null_and_range_checks_return_einval():
     assert L.fm_verify_sample(null, dummy, fm.FM_BF16, 1, dummy, dummy, dummy, 1.0, 0, dummy, dummy,
                               null) == fm.FM_EINVAL
     assert L.fm_verify_greedy(null, dummy, fm.FM_BF16, 1, dummy, dummy, dummy, dummy, null) == fm.FM_EINVAL
+    seeds = (ctypes.c_uint64 * 2)(1, 2)
+    counts = (ctypes.c_int * 2)(0, 0)
+    assert L.fm_draft_batch_sample(null, dummy, 2, null, counts, 1.0, seeds, dummy, dummy, dummy,
+                                   null) == fm.FM_EINVAL
+    assert L.fm_verify_sample_batch(null, dummy, fm.FM_BF16, 2, dummy, dummy, dummy, 1.0, seeds, dummy, dummy,
+                                    null) == fm.FM_EINVAL
     assert L.fm_context_length(null) == -1
     assert L.fm_context_truncate(null, 0, null) == fm.FM_EINVAL
     assert L.fm_context_truncate_req(null, 0, 0, null) == fm.FM_EINVAL

@@ -14,7 +14,8 @@ import synth
 pytestmark = pytest.mark.gpu
 
 fm = pytest.importorskip("step_flow_map_amd")
-from gpu_util import binding_weights, check_logits, check_tokens, exact_or_reseed, to_dev  # noqa: E402
+from gpu_util import (binding_weights, check_guards, check_logits, check_sampled_tokens, check_tokens,  # noqa: E402
+                      exact_or_reseed, guarded, is_near_tie, ref_verify_sample, to_dev)
 
 TINY = synth.CONFIGS["tiny"]
 MID_BF16 = TINY.with_(name="mid_bf16", dtype="bf16", V=2000, d=384, nh=3, H=520, c_prefill=300)
@@ -37,9 +38,12 @@ def _run(cfg, w, prefill, new, noise, feats, seed_dr=None):
             dr.append_req(r, to_dev(feats[r][:prefill[r]]))
     rows = [feats[r][prefill[r]:prefill[r] + new[r]] for r in range(R)]
     cat = np.concatenate(rows) if sum(new) else None
-    logits = torch.empty(R, cfg.K, cfg.V, dtype=torch.float32, device="cuda")
-    tok = dr.draft_batch(to_dev(noise), new_feats=None if cat is None else to_dev(cat), n_new=new, logits=logits)
+    logits = guarded(R, cfg.K, cfg.V)
+    tok = guarded(R, cfg.K, dtype=torch.int32)
+    dr.draft_batch(to_dev(noise), new_feats=None if cat is None else to_dev(cat), n_new=new, logits=logits,
+                   tokens=tok)
     torch.cuda.synchronize()
+    check_guards(logits, tok)
     for r in range(R):
         assert dr.context_length_req(r) == prefill[r] + new[r]
     return tok.cpu().numpy(), logits.cpu().numpy(), dr
@@ -150,3 +154,72 @@ def test_batch_verify_is_per_request():
     for r in range(R):
         n, em = oracle.verify(T[r], tok[r])
         assert e.cpu().numpy()[r, :n + 1].tolist() == em
+
+
+@pytest.mark.parametrize("cfg", [TINY, MID_BF16], ids=["tiny_f32", "mid_bf16"])
+def test_batch_sample_uses_each_requests_seed(cfg):
+    """Three requests (different context lengths, one without appended rows)
+    sampled together at temperature 0.8, each with its own seed: request r's
+    logits match the oracle's draft of that request alone and its tokens are
+    the oracle's sample under seeds[r] as branch 0 (near-ties excepted).
+    fm_verify_sample_batch then verifies request r as the oracle verifies it
+    alone with seeds[r], against target logits near the drafter's."""
+    print(f"[batch sample] {cfg.name}", flush=True)
+    tau, seeds = 0.8, [1001, 2002, 3003]
+    R = 3
+    prefill, new = [cfg.c_prefill, 5, 0], [4, 0, 7]
+    w = synth.make_weights(cfg)
+    W = oracle.Weights.from_storage(w)
+    feats = [synth.make_features(cfg, rows=prefill[r] + new[r], request=r) for r in range(R)]
+    S = oracle.sampling
+
+    def case(draw):
+        noise = synth.make_noise(cfg, R, draw)
+        dr = _handle(cfg, w, R, C_max=max(p + n for p, n in zip(prefill, new)) + 8)
+        dr.set_schedule(cfg.times)
+        for r in range(R):
+            if prefill[r]:
+                dr.append_req(r, to_dev(feats[r][:prefill[r]]))
+        cat = np.concatenate([feats[r][prefill[r]:] for r in range(R)])
+        tok = guarded(R, cfg.K, dtype=torch.int32)
+        logits = guarded(R, cfg.K, cfg.V)
+        lse = guarded(R, cfg.K)
+        fm.fm_draft_batch_sample(dr.handle, to_dev(noise), tau, seeds, tok, logits, lse, new_feats=to_dev(cat),
+                                 n_new=new)
+        torch.cuda.synchronize()
+        check_guards(tok, logits, lse)
+        tk, lg, ls = tok.cpu().numpy(), logits.cpu().numpy(), lse.cpu().numpy()
+        ties = []
+        for r in range(R):
+            ref = oracle.draft(W, cfg, noise[r], feats[r])["logits"]
+            check_logits(lg[r], ref, cfg.dtype, f"request {r}:")
+            own = S.logsumexp_rows(lg[r].astype(np.float64), tau)
+            assert np.abs(ls[r] - own).max() <= 1e-5 * (1 + np.abs(own).max())
+            ties += [(r,) + t for t in check_sampled_tokens(tk[r:r + 1], lg[r:r + 1], [ref], tau, seeds[r],
+                                                            cfg.dtype)]
+        # probabilistic verification of every request with its own seed
+        rng = np.random.default_rng(11 + draw)
+        T = np.concatenate([lg + 0.2 * rng.standard_normal(lg.shape), rng.standard_normal((R, 1, cfg.V))], axis=1)
+        if cfg.dtype == "bf16":
+            T_vals = oracle.round_bf16(T)
+            T_dev = to_dev(synth.to_bf16_bits(T_vals.astype(np.float32)))
+        else:
+            T_vals = T.astype(np.float32).astype(np.float64)
+            T_dev = to_dev(T.astype(np.float32))
+        em = guarded(R, cfg.K + 1, dtype=torch.int32)
+        acc = guarded(R, dtype=torch.int32)
+        fm.fm_verify_sample_batch(dr.handle, T_dev, logits, lse, tok, tau, seeds, em, acc)
+        torch.cuda.synchronize()
+        check_guards(em, acc)
+        e, a = em.cpu().numpy(), acc.cpu().numpy()
+        for r in range(R):
+            re, ra, rs = ref_verify_sample(T_vals[r:r + 1], lg[r:r + 1], tk[r:r + 1], tau, seeds[r])
+            if a[r] != ra[0] or not np.array_equal(e[r], re[0]):
+                assert is_near_tie(T_vals[r:r + 1], lg[r:r + 1], tk[r:r + 1], tau, seeds[r], 0, int(a[r]), rs[0]), (
+                    r, a[r], ra[0])
+                ties.append((r, "verify"))
+        print(f"  draw {draw}: accepted {a.tolist()}, near-ties {ties}", flush=True)
+        dr.close()
+        return ties
+
+    exact_or_reseed(case, f"batch sample {cfg.name}")
