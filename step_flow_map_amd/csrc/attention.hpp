@@ -365,10 +365,10 @@ __global__ __launch_bounds__(NW * 64) void attention_kernel(AttnArgs g) {
 }
 
 
-// Attention of the four branches of one tree over their shared context (bf16
-// storage).  A workgroup of 8 waves takes a (head, range of context blocks);
-// wave w serves branch w / 2 and stream w % 2, and the two streams take the
-// range's blocks alternately.  A block's keys and values (32 x HD each) are
+// Attention of the BR (2..4) branches of one tree over their shared context
+// (bf16 storage).  A workgroup of 8 waves takes a (head, range of context
+// blocks); wave w serves branch w / 2 (if below BR) and stream w % 2, and the
+// two streams take the range's blocks alternately.  A block's keys and values (32 x HD each) are
 // read from HBM once per workgroup: every wave loads a part of the next two
 // blocks into registers while the current two are computed, writes it into
 // the other half of a double-buffered LDS stage, and one barrier per step
@@ -378,14 +378,17 @@ __global__ __launch_bounds__(NW * 64) void attention_kernel(AttnArgs g) {
 // block) are read by the branch's stream-0 wave of the last range straight
 // from HBM.  The waves of a branch merge through LDS; with several ranges the
 // ranges' partial states go to memory and attention_merge_kernel combines
-// them (spread over many workgroups: one workgroup merging all four
+// them (spread over many workgroups: one workgroup merging all the
 // branches of a head would be bound by the bytes one CU can take in).
-// All branches see the same context length (g.C[0]).
-template <int HD>
+// All branches see the same context length (that of request 0).
+template <int HD, int BR>
 __global__ __launch_bounds__(512) void attention_tree_kernel(AttnArgs g) {
   typedef bf16_t T;
   typedef AttnTile<T, HD> Tile;
-  constexpr int NW = 8, BR = 4, WPB = NW / BR;
+  // 8 waves load every step; waves 2b and 2b + 1 compute branch b < BR (the
+  // others only load), so one read of a key/value block serves every branch
+  constexpr int NW = 8, WPB = 2;
+  static_assert(BR >= 1 && BR * WPB <= NW, "at most four branches");
   constexpr int QS = Tile::QS, OT = Tile::OT, VE = Tile::VE;
   constexpr int KP = HD / VE;                          // 16-byte pieces per key row
   constexpr int PART_U4 = 32 * KP;                     // a block's keys (= its values) in uint4
@@ -405,6 +408,7 @@ __global__ __launch_bounds__(512) void attention_tree_kernel(AttnArgs g) {
   const int j = lane & 15, grp = lane >> 4;
   const int range = blockIdx.x % g.n_ranges, head = blockIdx.x / g.n_ranges;
   const int b = wave / WPB, stream = wave % WPB;
+  const bool computes = b < BR;
   const int C = visible_ctx(g, 0);
   const int ctx_blocks = (C + ATT_BLK - 1) / ATT_BLK;
   int n_ranges, per_range;
@@ -418,7 +422,7 @@ __global__ __launch_bounds__(512) void attention_tree_kernel(AttnArgs g) {
 
   uint4 qf[QS];
   {
-    const T* qrow = reinterpret_cast<const T*>(g.q) + (size_t)(b * g.K + j) * g.ldq + head * HD;
+    const T* qrow = reinterpret_cast<const T*>(g.q) + (size_t)((computes ? b : 0) * g.K + j) * g.ldq + head * HD;
 #pragma unroll
     for (int s = 0; s < QS; ++s) qf[s] = vload<T>(qrow + (4 * s + grp) * VE);
   }
@@ -495,7 +499,7 @@ __global__ __launch_bounds__(512) void attention_tree_kernel(AttnArgs g) {
           pf[k][u] = *reinterpret_cast<const u32x4_t*>(src[u] + (size_t)(bi0 < bhi ? bi0 : blo) * BLK_STRIDE_U4);
         }
         const int bi = blo + st * WPB + stream;
-        if (bi < bhi) {
+        if (computes && bi < bhi) {
           Tile t;
           frags(t, half);
           attn_block<T, HD>(t, qf, min(ATT_BLK, C - ATT_BLK * bi), g.scale, m_run, l_run, o);
@@ -507,7 +511,7 @@ __global__ __launch_bounds__(512) void attention_tree_kernel(AttnArgs g) {
     }
   }
   // the branch's own block rows: the last range, the branch's stream-0 wave
-  if (range == n_ranges - 1 && stream == 0) {
+  if (computes && range == n_ranges - 1 && stream == 0) {
     Tile t;
     const int pb = g.scratch_blk + b;
 #pragma unroll
@@ -535,27 +539,28 @@ __global__ __launch_bounds__(512) void attention_tree_kernel(AttnArgs g) {
   __syncthreads();
   // thread lt of branch mb's 128 handles column lt of all 16 rows, so every
   // row's stores and loads below are contiguous across the lanes
-  constexpr int TPB = NW * 64 / BR;  // threads per branch (= HD at HD 128)
+  constexpr int TPB = 128;  // threads per branch (= HD at HD 128); those of branches >= BR idle
   static_assert(TPB % HD == 0 || HD % TPB == 0, "columns split evenly");
   constexpr int CPT = HD / TPB > 0 ? HD / TPB : 1;  // columns per thread
   const int mb = tid / TPB, lt = tid % TPB, w0 = mb * WPB;
   const int bh = mb * g.nh + head;
-  const bool col_ok = lt < HD;  // HD < TPB: the surplus threads idle
+  const bool col_ok = lt < HD && mb < BR;  // HD < TPB: the surplus threads idle
   float acc[KB_ROWS][CPT], Mr[KB_ROWS], Lr[KB_ROWS];
 #pragma unroll
   for (int row = 0; row < KB_ROWS; ++row) {
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < WPB; ++w) M = fmaxf(M, sm[w0 + w][row]);
+    for (int w = 0; w < WPB; ++w) M = fmaxf(M, sm[min(w0 + w, NW - 1)][row]);
     float Lsum = 0.f;
 #pragma unroll
     for (int c = 0; c < CPT; ++c) acc[row][c] = 0.f;
 #pragma unroll
     for (int w = 0; w < WPB; ++w) {
-      const float wt = M == -INFINITY ? 0.f : expf(sm[w0 + w][row] - M);
-      Lsum += wt * sl[w0 + w][row];
+      const int ww = min(w0 + w, NW - 1);
+      const float wt = M == -INFINITY ? 0.f : expf(sm[ww][row] - M);
+      Lsum += wt * sl[ww][row];
 #pragma unroll
-      for (int c = 0; c < CPT; ++c) acc[row][c] += wt * (col_ok ? so[w0 + w][row][c * TPB + lt] : 0.f);
+      for (int c = 0; c < CPT; ++c) acc[row][c] += wt * (col_ok ? so[ww][row][c * TPB + lt] : 0.f);
     }
     Mr[row] = M;
     Lr[row] = Lsum;
@@ -581,7 +586,7 @@ __global__ __launch_bounds__(512) void attention_tree_kernel(AttnArgs g) {
       for (int c = 0; c < CPT; ++c) g.part_o[pr * HD + c * TPB + lt] = acc[row][c];
     }
   }
-  if (lt < KB_ROWS) {
+  if (lt < KB_ROWS && mb < BR) {
     const size_t pr = ((size_t)bh * g.n_ranges + range) * KB_ROWS + lt;
     float m = 0.f, l = 0.f;
 #pragma unroll

@@ -632,15 +632,20 @@ fm_status attention(fm_handle* h, int l, int B, const int* n_new, bool own_ctx, 
   a.scale = 1.0f / std::sqrt((float)hd);
   const int cap_blocks = cdiv(c.C_max, ATT_BLK);
   if constexpr (std::is_same<T, bf16_t>::value) {
-    // four branches over one shared context: each key/value block is read once
-    // per (head, range) and served to every branch from LDS
-    if (!own_ctx && B == 4 && (hd == 128 || hd == 64)) {
+    // 2..4 branches over one shared context: each key/value block is read
+    // once per (head, range) and served to every branch from LDS
+    if (!own_ctx && B >= 2 && B <= 4 && (hd == 128 || hd == 64)) {
       a.n_ranges = tree_max_ranges(cap_blocks);
-      const int tgrid = c.n_heads * a.n_ranges;
-      if (hd == 128)
-        hipLaunchKernelGGL((attention_tree_kernel<128>), dim3(tgrid), dim3(512), 0, st, a);
-      else
-        hipLaunchKernelGGL((attention_tree_kernel<64>), dim3(tgrid), dim3(512), 0, st, a);
+      const dim3 tgrid(c.n_heads * a.n_ranges), tblock(512);
+      if (hd == 128) {
+        if (B == 2) hipLaunchKernelGGL((attention_tree_kernel<128, 2>), tgrid, tblock, 0, st, a);
+        else if (B == 3) hipLaunchKernelGGL((attention_tree_kernel<128, 3>), tgrid, tblock, 0, st, a);
+        else hipLaunchKernelGGL((attention_tree_kernel<128, 4>), tgrid, tblock, 0, st, a);
+      } else {
+        if (B == 2) hipLaunchKernelGGL((attention_tree_kernel<64, 2>), tgrid, tblock, 0, st, a);
+        else if (B == 3) hipLaunchKernelGGL((attention_tree_kernel<64, 3>), tgrid, tblock, 0, st, a);
+        else hipLaunchKernelGGL((attention_tree_kernel<64, 4>), tgrid, tblock, 0, st, a);
+      }
       FM_LAUNCHED("attention_tree_kernel");
       if (a.n_ranges > 1) {
         const int mgrid = B * c.n_heads * (KB / 2);

@@ -181,6 +181,16 @@ def test_tree_shared_context_lengths(prefill):
     _parity(cfg, f"tree C {cfg.C}", B=4)
 
 
+@pytest.mark.parametrize("B", [2, 3])
+@pytest.mark.parametrize("prefill", [0, 25, 1500])
+def test_tree_of_two_or_three_shares_the_context(B, prefill):
+    """Two or three bf16 branches through the shared-context kernel (the
+    waves of the absent branches only load): no context, one key block plus
+    one row, and 48 blocks over 12 ranges merged by the separate pass."""
+    cfg = MID_BF16.with_(name=f"mid_tree{B}_c{prefill}", B=B, c_prefill=prefill)
+    _parity(cfg, f"tree of {B}, C {cfg.C}", B=B)
+
+
 @pytest.mark.parametrize("cfg", [TINY, SMALL_BF16, MID_BF16, WIDE_F32, W2048_BF16],
                          ids=["tiny_f32", "small_bf16", "mid_bf16", "wide_f32", "w2048_bf16"])
 def test_draft_tree_of_four(cfg):
