@@ -225,6 +225,32 @@ __device__ __forceinline__ bool arrive(uint32_t* counter, uint32_t expected, int
   return *lds_flag != 0;
 }
 
+// ------------------------------------------------ row statistics of 16 lanes
+// DPP move within a row of 16 lanes (no LDS traffic)
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+// Sum over the 16 lanes of a DPP row: neighbours 1 and 2 (quad permutes), then
+// the mirrored half and the mirrored row.  Every step adds two equal-order
+// partial sums of symmetric partners, so all 16 lanes end with the same bits.
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp_mov<0xB1>(x);   // quad_perm [1, 0, 3, 2]
+  x += dpp_mov<0x4E>(x);   // quad_perm [2, 3, 0, 1]
+  x += dpp_mov<0x141>(x);  // row_half_mirror
+  x += dpp_mov<0x140>(x);  // row_mirror
+  return x;
+}
+// A row's statistics over 16 consecutive columns, held one per lane by the 16
+// lanes of a DPP row (every lane of the wave calls this): mean and sum of
+// squared deviations, two passes; the row's first lane stores them when ok.
+__device__ __forceinline__ void row16_stats(float x, bool ok, float2* dst) {
+  const float mean = row16_sum(x) * 0.0625f;
+  const float dv = x - mean;
+  const float m2 = row16_sum(dv * dv);
+  if (ok && (threadIdx.x & 15) == 0) *dst = make_float2(mean, m2);
+}
+
 // counters live 32 words (128 bytes) apart so contended lines never share
 constexpr int COUNTER_STRIDE = 32;
 

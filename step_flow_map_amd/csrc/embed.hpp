@@ -45,6 +45,8 @@ struct EmbedArgs {
   float alpha, beta;  // alpha == 0: e_state is not read
   int K;              // positions per branch (rows m use position m % K)
   int use_pos;
+  float2* ln_part;    // or null: per-16-column (mean, M2) of h for the LayerNorm
+  int ln_part_ld;     // fused into the next contraction, at [m * ln_part_ld + c / 16]
 };
 
 // P[k][c] = sin(k w_c) for c < d/2, cos(k w_{c-d/2}) otherwise,
@@ -189,8 +191,9 @@ __global__ __launch_bounds__(NW * 64) void embed_kernel(EmbedArgs g) {
 template <typename T>
 __global__ __launch_bounds__(256) void embed_reduce_kernel(EmbedArgs g) {
   constexpr int COLS = 16 * Vec<T>::N;
-  const int q = blockIdx.x * 256 + threadIdx.x;
-  if (q >= g.M * g.d) return;
+  const int q0 = blockIdx.x * 256 + threadIdx.x;
+  const bool ok = q0 < g.M * g.d;  // uniform over 16 lanes: M * d is a multiple of 16
+  const int q = ok ? q0 : 0;
   const int m = q / g.d, c = q % g.d, cb = c / COLS;
   const int S_cb = (g.Ss > g.Sf && (cb & 3) == 1) ? g.Ss : g.Sf;
   // every split's load in flight at once, then the sum in split order
@@ -202,9 +205,13 @@ __global__ __launch_bounds__(256) void embed_reduce_kernel(EmbedArgs g) {
   for (int s = 0; s < EMB_SPLITS_MAX; ++s) v += pv[s];
   float e = g.beta * v;
   if (g.alpha != 0.f) e += g.alpha * g.e_state[q];
-  g.e_state[q] = e;
   const float hv = e + (g.use_pos ? pos_table(m % g.K, c, g.d) : 0.f);
-  g.h[q] = hv;
+  if (ok) {
+    g.e_state[q] = e;
+    g.h[q] = hv;
+  }
+  // 16 consecutive lanes hold 16 consecutive columns of one row (d % 16 == 0)
+  if (g.ln_part) row16_stats(hv, ok, g.ln_part + (size_t)m * g.ln_part_ld + (c >> 4));
 }
 
 }  // namespace fm

@@ -263,7 +263,7 @@ int max_blocks(const fm_config& c) { return std::max(c.max_branches, c.max_reque
 
 struct Layout {
   size_t cache, mods, sched, ctx, h, e_state, u_pre, act_qkv, act_d, attn_o, act_f, qkv;
-  size_t att_po, att_ml, partial, lm_part, lm_lse, counters, dsoft, logits_tmp, sm_part, vs, total;
+  size_t att_po, att_ml, partial, lm_part, lm_lse, counters, dsoft, logits_tmp, sm_part, vs, lnpart, total;
 };
 
 int max_rows(const fm_config& c) { return max_blocks(c) * KB; }
@@ -320,6 +320,7 @@ Layout make_layout(const fm_config& c) {
   L.lm_part = take((size_t)LM_GRID * Mb * 8);
   L.lm_lse = take((size_t)LM_GRID * Mb * 8);
   L.vs = take(vs_scratch_bytes(max_blocks(c), KB));  // branches of one request, or requests
+  L.lnpart = take((size_t)KB * LN_PART_MAX * sizeof(float2));  // row statistics for the fused LayerNorms
   L.counters = take((size_t)N_COUNTER_SLOTS * COUNTER_STRIDE * 4);
   if (c.max_steps > 1) {
     L.dsoft = take(Mb * (size_t)c.V * es);
@@ -508,6 +509,7 @@ template <typename T>
 fm_status gemm_ln(fm_handle* h, int epi, const float* x, const float* shift, const float* scale, const void* A_ctx,
                   int M_ctx, const void* W, int N, int K, const EpiParams& e, hipStream_t st) {
   if (cdiv(K, gemm_chunk(h->cfg.dtype)) > 8) return fail(FM_EINVAL, "fused LayerNorm needs k <= 8 chunks");
+  if (K % 16 || K / 16 > LN_PART_MAX) return fail(FM_EINVAL, "fused LayerNorm row of %d columns", K);
   GemmArgs a;
   a.A = A_ctx;
   a.lda = K;
@@ -526,6 +528,8 @@ fm_status gemm_ln(fm_handle* h, int epi, const float* x, const float* shift, con
   l.shift = shift;
   l.scale = scale;
   l.eps = 1e-6f;
+  l.part = h->at<float2>(h->lay.lnpart);  // written by the kernel that produced x
+  l.part_ld = LN_PART_MAX;
   const dim3 grid(cdiv(cdiv(N, 16), 2)), block(8 * 64);
   const bool two = a.M > 16;
   if (epi == EPI_QKV && two)
@@ -562,9 +566,11 @@ fm_status probe_end(fm_handle* h, int kernel, hipStream_t st);
 // probe: FM_PROBE_EMBED brackets embed_kernel alone (the contraction the
 // counters and the roofline describe, without its split-sum kernel); -1
 // records nothing
+// ln_part: where the reduce also writes h's per-16-column row statistics for
+// a fused LayerNorm that follows, or null
 template <typename T>
 fm_status embed(fm_handle* h, const void* x, int ldx, int M, float alpha, float beta, hipStream_t st,
-                int probe = -1) {
+                int probe = -1, float2* ln_part = nullptr) {
   const fm_config& c = h->cfg;
   if (M > 64) return fail(FM_EINVAL, "embedding contraction with %d rows exceeds 64", M);
   EmbedPlan p = plan_embed(c.d, c.dtype, M);
@@ -586,6 +592,8 @@ fm_status embed(fm_handle* h, const void* x, int ldx, int M, float alpha, float 
   a.beta = beta;
   a.K = KB;
   a.use_pos = 1;
+  a.ln_part = ln_part;
+  a.ln_part_ld = LN_PART_MAX;
   if (p.Ss > EMB_SPLITS_MAX) return fail(FM_EINVAL, "embedding with %d row splits (at most %d)", p.Ss, EMB_SPLITS_MAX);
   const dim3 grid(p.grid), block(EMB_WAVES * 64);
   FM_TRY(probe_begin(h, probe, st));
@@ -905,6 +913,9 @@ fm_status draft_impl(fm_handle* h, const void* noise, int B, const void* new_fea
   for (int r = 0; r < ctx.n_req; ++r) adv.val[r] = bt ? bt->n_new[r] : n_new;
   adv.cap = c.C_max;
   const bool fuse_ln = ln_fusable(c, B);
+  // with fused LayerNorms, the producers of h (the embedding's reduce, W_o and
+  // fc2) also write its per-16-column row statistics
+  float2* lnp = fuse_ln ? h->at<float2>(h->lay.lnpart) : nullptr;
   // many rows: the reduces of W_o and fc2 also write the LayerNorm that follows
   const bool ln_in_reduce = !fuse_ln && resid_ln_fused(Mb, d, d, c.dtype) && resid_ln_fused(Mb, d, F, c.dtype);
   T* act_qkv = h->at<T>(h->lay.act_qkv);
@@ -922,10 +933,11 @@ fm_status draft_impl(fm_handle* h, const void* noise, int B, const void* new_fea
     const float s = h->times[j], t = h->times[j + 1];
     const float* mods = mods_all + (size_t)j * (6 * L + 2) * d;
     if (j == 0) {
-      FM_TRY(embed<T>(h, noise, c.V, Mb, 0.f, 1.f, st, FM_PROBE_EMBED));
+      FM_TRY(embed<T>(h, noise, c.V, Mb, 0.f, 1.f, st, FM_PROBE_EMBED, lnp));
     } else {
       const float sp = h->times[j - 1];
-      FM_TRY(embed<T>(h, h->at<T>(h->lay.dsoft), c.V, Mb, (1.f - s) / (1.f - sp), (s - sp) / (1.f - sp), st));
+      FM_TRY(embed<T>(h, h->at<T>(h->lay.dsoft), c.V, Mb, (1.f - s) / (1.f - sp), (s - sp) / (1.f - sp), st, -1,
+                      lnp));
     }
     if (hidden) FM_TRY(trace_copy(hres, hidden + ((size_t)j * (L + 1)) * Mb * d, (size_t)Mb * d, st));
     const int m_qkv = Mb + (j == 0 ? n_new : 0);
@@ -958,6 +970,8 @@ fm_status draft_impl(fm_handle* h, const void* noise, int B, const void* new_fea
         e.out_f32 = hres;
         e.ld_f32 = d;
         e.gate = mv + 2 * d;
+        e.ln_part = lnp;  // LN2, fused into fc1
+        e.ln_part_ld = LN_PART_MAX;
         if (ln_in_reduce) {  // LN2 for fc1
           e.ln_shift = mv + 3 * d;
           e.ln_scale = mv + 4 * d;
@@ -989,6 +1003,8 @@ fm_status draft_impl(fm_handle* h, const void* noise, int B, const void* new_fea
         e.out_f32 = hres;
         e.ld_f32 = d;
         e.gate = mv + 5 * d;
+        e.ln_part = l + 1 < L ? lnp : nullptr;  // the next block's LN1, fused into its QKV
+        e.ln_part_ld = LN_PART_MAX;
         if (ln_in_reduce) {  // the next block's LN1, or the final LN before the LM head
           const float* nm = mods + (size_t)6 * (l + 1) * d;
           e.ln_shift = nm;

@@ -59,6 +59,10 @@ struct EpiParams {
   const float* ln_scale;
   void* ln_out;
   int ln_ldo;
+  // EPI_RESID: per-16-column statistics (mean, M2) of the updated rows for the
+  // LayerNorm fused into the next contraction, at ln_part[m * ln_part_ld + n / 16]
+  float2* ln_part;
+  int ln_part_ld;
 };
 
 constexpr int GEMM_SPLIT_MAX = 8;  // k splits per tile (= arrivals per counter)
@@ -74,11 +78,13 @@ struct GemmArgs {
   uint32_t* counters;  // one per 16-row tile, COUNTER_STRIDE apart; zero on entry and exit
 };
 
+// returns the stored residual value for EPI_RESID (0 otherwise)
 template <typename T, int EPI>
-__device__ __forceinline__ void epilogue(const EpiParams& e, int m, int n, float v) {
+__device__ __forceinline__ float epilogue(const EpiParams& e, int m, int n, float v) {
   if (e.bias) v += to_f32<T>(reinterpret_cast<const T*>(e.bias)[n]);
   if (EPI == EPI_F32) {
     e.out_f32[(size_t)m * e.ld_f32 + n] = v;
+    return 0.f;
   } else if (EPI == EPI_ACT) {
     reinterpret_cast<T*>(e.out_act)[(size_t)m * e.ld_act + n] = from_f32<T>(v);
   } else if (EPI == EPI_GELU) {
@@ -88,24 +94,25 @@ __device__ __forceinline__ void epilogue(const EpiParams& e, int m, int n, float
     const float r = *p + e.gate[n] * v;
     *p = r;
     if (e.out_act) reinterpret_cast<T*>(e.out_act)[(size_t)m * e.ld_act + n] = from_f32<T>(r);
+    return r;
   } else {  // EPI_QKV
     const int nn = n + e.col_offset;
     int pos, req;
     if (m < e.rows_block) {
       if (nn < e.d) {
         reinterpret_cast<T*>(e.out_act)[(size_t)m * e.ld_act + nn] = from_f32<T>(v);
-        return;
+        return 0.f;
       }
       pos = e.scratch_pos0 + e.scratch_step * (m >> 4) + (m & 15);
       req = e.scratch_step ? 0 : (m >> 4);
     } else {
-      if (nn < e.d) return;  // queries of context rows are not needed
+      if (nn < e.d) return 0.f;  // queries of context rows are not needed
       const int c = m - e.rows_block;
       req = 0;
 #pragma unroll
       for (int r = 1; r < FM_MAX_REQ; ++r) req += (r < e.n_req && c >= e.ctx_first[r]) ? 1 : 0;
       pos = e.ctx_len[req] + e.ctx_off + c - e.ctx_first[req];
-      if (pos >= e.ctx_cap) return;  // past the capacity: nothing is written
+      if (pos >= e.ctx_cap) return 0.f;  // past the capacity: nothing is written
     }
     const int which = nn >= 2 * e.d;  // 0: key, 1: value
     const int col = nn - (1 + which) * e.d;
@@ -116,6 +123,19 @@ __device__ __forceinline__ void epilogue(const EpiParams& e, int m, int n, float
     else
       reinterpret_cast<T*>(e.vcache)[rb + (((size_t)head * (e.P >> 5) + (pos >> 5)) * e.hd + c) * 32 +
                                      vt_slot<T>(pos & 31)] = from_f32<T>(v);
+  }
+  return 0.f;
+}
+
+// The epilogue of output (m, n) when ok, then (EPI_RESID with ln_part) the
+// statistics of the updated row over the tile's 16 columns, which the 16
+// lanes of a DPP row hold (row m, columns 16 (n / 16) ..): every lane calls it.
+template <typename T, int EPI>
+__device__ __forceinline__ void epilogue_out(const EpiParams& e, int m, int n, float v, bool ok) {
+  float r = 0.f;
+  if (ok) r = epilogue<T, EPI>(e, m, n, v);
+  if constexpr (EPI == EPI_RESID) {
+    if (e.ln_part) row16_stats(r, ok, e.ln_part + (size_t)(ok ? m : 0) * e.ln_part_ld + (n >> 4));
   }
 }
 
@@ -236,8 +256,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs g, EpiParams e) 
 
   if (g.S == 1) {
 #pragma unroll
-    for (int r = 0; r < PER_THREAD; ++r)
-      if (em[r] < g.M && en[r] < g.N) epilogue<T, EPI>(e, em[r], en[r], val[r]);
+    for (int r = 0; r < PER_THREAD; ++r) epilogue_out<T, EPI>(e, em[r], en[r], val[r], em[r] < g.M && en[r] < g.N);
     return;
   }
 #pragma unroll
@@ -255,7 +274,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs g, EpiParams e) 
     float v = 0.f;
 #pragma unroll
     for (int ss = 0; ss < GEMM_SPLIT_MAX; ++ss) v += pv[ss];
-    if (ok) epilogue<T, EPI>(e, em[r], en[r], v);
+    epilogue_out<T, EPI>(e, em[r], en[r], v, ok);
   }
 }
 
@@ -270,7 +289,12 @@ struct LnArgs {
   const float* shift;  // [K]
   const float* scale;  // [K]
   float eps;
+  // per-16-column (mean, M2) of every row of h, written by the kernel that
+  // produced h: [16][part_ld], K / 16 entries per row
+  const float2* part;
+  int part_ld;
 };
+constexpr int LN_PART_MAX = 128;  // K / 16 for K up to 2048, the fused LayerNorm's longest row
 
 // Tile-group variant for wide layers (many 16-row tiles, a k range of at most
 // NW chunks): a workgroup owns TT adjacent tiles and wave w takes chunks w,
@@ -298,10 +322,11 @@ __global__ __launch_bounds__(NW * 64) void gemm_tg_kernel(GemmArgs g, EpiParams 
   constexpr int RED_U4 = NW * ELEMS / 4;
   constexpr int TILE_U4 = NW * 512;
   __shared__ uint4 smem[TILE_U4 > RED_U4 ? TILE_U4 : RED_U4];
-  __shared__ float sstat[LN ? NW : 1][16][2];              // per wave and row: mean, M2
+  __shared__ float sstat[16][2];                           // LN: per row mean, 1 / std
   // LN with context rows: their chunk waits in LDS (a wave-private tile in
   // the weights' layout) rather than as fragments in registers
   static_assert(!LN || MT <= 2, "fused LayerNorm supports at most 16 further rows");
+  static_assert(!LN || NW == 8, "fused LayerNorm: 32 threads per row of statistics");
   constexpr bool CTX_LDS = LN && MT == 2;
   __shared__ uint4 sctx[CTX_LDS ? NW : 1][CTX_LDS ? 512 : 1];
 
@@ -344,7 +369,15 @@ __global__ __launch_bounds__(NW * 64) void gemm_tg_kernel(GemmArgs g, EpiParams 
     const bool hok = has && k0 + hcol < k_end;
     float4 hv[HN];
     float4 msc = float4{0.f, 0.f, 0.f, 0.f}, msh = float4{0.f, 0.f, 0.f, 0.f};
+    // LN: thread t takes row t / 32 and its statistics partials (t % 32) + 32u,
+    // loaded first so that the row statistics are ready before the rows
+    constexpr int PU = LN ? LN_PART_MAX / 32 : 1;
+    const int prow = tid >> 5, psub = tid & 31, np = g.K >> 4;
+    float2 pp[PU];
     if constexpr (LN) {
+#pragma unroll
+      for (int u = 0; u < PU; ++u)  // unconditional (clamped) loads: the count masks the unused ones
+        pp[u] = ln.part[(size_t)prow * ln.part_ld + min(psub + 32 * u, np - 1)];
       const int kc = hok ? k0 + hcol : 0;
 #pragma unroll
       for (int i = 0; i < HN; ++i) hv[i] = *reinterpret_cast<const float4*>(ln.h + (size_t)hrow(i) * ln.ldh + kc);
@@ -363,75 +396,44 @@ __global__ __launch_bounds__(NW * 64) void gemm_tg_kernel(GemmArgs g, EpiParams 
     if constexpr (LN) {
       // every load above is issued before the statistics consume the first one
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (CTX_LDS) chunk_to_lds(ra[1], sctx[wave]);
-      const float mk = hok ? 1.f : 0.f;
-      // Row sums of the wave's columns: every lane writes its per-row partials
-      // (a sum of its 4 columns) into the wave's tile, rows LPR + 4 floats
-      // apart, and lane r (< 16) adds row r's partials in lane order.  The
-      // results reach every lane by readlane.
-      constexpr int LPR = KC / 4;  // lanes holding one row
-      float* red = reinterpret_cast<float*>(wt);
-      const int pos = lane % LPR;
-      auto row_sums = [&](const float (&v)[HN]) -> float {
-#pragma unroll
-        for (int i = 0; i < HN; ++i) red[hrow(i) * (LPR + 4) + pos] = v[i];
-        wave_lds_sync();
-        const float4* rr4 = reinterpret_cast<const float4*>(red + (lane & 15) * (LPR + 4));
-        float acc = 0.f;
-#pragma unroll
-        for (int q = 0; q < LPR / 4; ++q) {
-          const float4 t = rr4[q];
-          acc += ((t.x + t.y) + (t.z + t.w));
-        }
-        wave_lds_sync();
-        return acc;
-      };
-      // value i of this lane belongs to row hrow(i): bf16 i, float32 2i + (lane >> 5)
-      auto bcast = [&](float x, int i) -> float {
-        if constexpr (LPR == 64) {
-          return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), i));
-        } else {
-          const float lo = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 2 * i));
-          const float hi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 2 * i + 1));
-          return (lane >> 5) ? hi : lo;
-        }
-      };
-      const int nw = has ? min(KC, g.K - k0) : 0;
-      float part[HN];
-#pragma unroll
-      for (int i = 0; i < HN; ++i) part[i] = mk * ((hv[i].x + hv[i].y) + (hv[i].z + hv[i].w));
-      const float mw_row = row_sums(part) / (float)max(nw, 1);  // lane r: wave mean of row r
-#pragma unroll
-      for (int i = 0; i < HN; ++i) {
-        const float m = bcast(mw_row, i);
-        const float a = hv[i].x - m, b = hv[i].y - m, cc = hv[i].z - m, d = hv[i].w - m;
-        part[i] = mk * ((a * a + b * b) + (cc * cc + d * d));
-      }
-      const float m2_row = row_sums(part);
-      if (lane < 16) {
-        sstat[wave][lane][0] = mw_row;
-        sstat[wave][lane][1] = m2_row;
-      }
-      lds_barrier();  // the weight loads stay in flight
-      // lane j (< 16) combines row j over the waves; the others mirror it
-      float mean = 0.f, M2 = 0.f, n = 0.f;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        const float nb = (float)max(0, min(KC, g.K - w * KC));
-        const float mb = sstat[w][j][0], m2b = sstat[w][j][1];
+      // Row statistics: thread t merges its partials of row t / 32 in order
+      // (pairwise update of Chan, Golub and LeVeque; every partial covers 16
+      // columns), the 32 threads of the row merge in a fixed tree (a DPP row,
+      // then its two halves), and thread 32r publishes row r's mean and
+      // 1 / std through LDS.
+      float n = 0.f, mean = 0.f, M2 = 0.f;
+      auto merge = [&](float nb, float mb, float m2b) {
         const float nn = n + nb, delta = mb - mean;
         const float f = nb > 0.f ? nb / nn : 0.f;
         mean += delta * f;
         M2 += nb > 0.f ? m2b + delta * delta * (n * f) : 0.f;
         n = nn;
+      };
+#pragma unroll
+      for (int u = 0; u < PU; ++u) merge(psub + 32 * u < np ? 16.f : 0.f, pp[u].x, pp[u].y);
+      {
+        float on = dpp_mov<0xB1>(n), om = dpp_mov<0xB1>(mean), o2 = dpp_mov<0xB1>(M2);
+        merge(on, om, o2);
+        on = dpp_mov<0x4E>(n), om = dpp_mov<0x4E>(mean), o2 = dpp_mov<0x4E>(M2);
+        merge(on, om, o2);
+        on = dpp_mov<0x141>(n), om = dpp_mov<0x141>(mean), o2 = dpp_mov<0x141>(M2);
+        merge(on, om, o2);
+        on = dpp_mov<0x140>(n), om = dpp_mov<0x140>(mean), o2 = dpp_mov<0x140>(M2);
+        merge(on, om, o2);
+        on = __shfl_xor(n, 16, 64), om = __shfl_xor(mean, 16, 64), o2 = __shfl_xor(M2, 16, 64);
+        merge(on, om, o2);
       }
-      const float rstd = 1.f / sqrtf(M2 / (float)g.K + ln.eps);
+      if (psub == 0) {
+        sstat[prow][0] = mean;
+        sstat[prow][1] = 1.f / sqrtf(M2 / (float)g.K + ln.eps);
+      }
+      lds_barrier();  // the rows and the weights stay in flight
       // normalise, modulate, round, and place in the wave's tile as the
       // weights' chunk layout (piece p of row r at r * 32 + (p ^ r))
 #pragma unroll
       for (int i = 0; i < HN; ++i) {
         const int rr = hrow(i);
-        const float m_r = bcast(mean, i), s_r = bcast(rstd, i);
+        const float m_r = sstat[rr][0], s_r = sstat[rr][1];
         const float y0 = ((hv[i].x - m_r) * s_r) * (1.f + msc.x) + msh.x;
         const float y1 = ((hv[i].y - m_r) * s_r) * (1.f + msc.y) + msh.y;
         const float y2 = ((hv[i].z - m_r) * s_r) * (1.f + msc.z) + msh.z;
@@ -452,6 +454,8 @@ __global__ __launch_bounds__(NW * 64) void gemm_tg_kernel(GemmArgs g, EpiParams 
 #pragma unroll
       for (int st = 0; st < 8; ++st) af[0][st] = as_vec<T>(chunk_frag(wt, st));
       wave_lds_sync();
+      // the context rows (issued after the residual rows) wait in their tile
+      if constexpr (CTX_LDS) chunk_to_lds(ra[1], sctx[wave]);
     } else {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
@@ -510,8 +514,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_tg_kernel(GemmArgs g, EpiParams 
   }
   if (g.S == 1) {
 #pragma unroll
-    for (int r = 0; r < PER_THREAD; ++r)
-      if (em[r] < g.M && en[r] < g.N) epilogue<T, EPI>(e, em[r], en[r], val[r]);
+    for (int r = 0; r < PER_THREAD; ++r) epilogue_out<T, EPI>(e, em[r], en[r], val[r], em[r] < g.M && en[r] < g.N);
     return;
   }
   // ---- split k: publish, the last split of the tile group sums in split order
@@ -530,7 +533,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_tg_kernel(GemmArgs g, EpiParams 
     float v = 0.f;
 #pragma unroll
     for (int ss = 0; ss < GEMM_SPLIT_MAX; ++ss) v += pv[ss];
-    if (ok) epilogue<T, EPI>(e, em[r], en[r], v);
+    epilogue_out<T, EPI>(e, em[r], en[r], v, ok);
   }
 }
 
