@@ -47,6 +47,16 @@ struct EmbedArgs {
   int use_pos;
   float2* ln_part;    // or null: per-16-column (mean, M2) of h for the LayerNorm
   int ln_part_ld;     // fused into the next contraction, at [m * ln_part_ld + c / 16]
+  // context rows fused in this call, normalised by the reduce (the plain
+  // LayerNorm of the fusion) instead of a launch of their own: n_u rows of
+  // u_pre [n_u][d] (float32) with their per-16-column statistics u_part, written
+  // in the storage type to u_out [n_u][d]; n_u = 0: none
+  const float* u_pre;
+  const float2* u_part;
+  int u_part_ld;
+  void* u_out;
+  int n_u;
+  float eps;
 };
 
 // P[k][c] = sin(k w_c) for c < d/2, cos(k w_{c-d/2}) otherwise,
@@ -184,13 +194,64 @@ __global__ __launch_bounds__(NW * 64) void embed_kernel(EmbedArgs g) {
   }
 }
 
+// Workgroups past the M x d outputs of the reduce each normalise one fused
+// context row (plain LayerNorm, biased variance): wave 0 merges the row's
+// per-16-column statistics (two a lane in column order, then a fixed tree
+// over the lanes), and every thread writes its columns.
+template <typename T>
+__device__ __forceinline__ void norm_context_row(const EmbedArgs& g, int r) {
+  __shared__ float mr[2];
+  const int tid = threadIdx.x, lane = tid & 63;
+  if (tid < 64) {
+    const int np = g.d >> 4;
+    float n = 0.f, mean = 0.f, M2 = 0.f;
+    auto merge = [&](float nb, float mb, float m2b) {
+      const float nn = n + nb, delta = mb - mean;
+      const float f = nb > 0.f ? nb / nn : 0.f;
+      mean += delta * f;
+      M2 += nb > 0.f ? m2b + delta * delta * (n * f) : 0.f;
+      n = nn;
+    };
+    const float2* pr = g.u_part + (size_t)r * g.u_part_ld;
+    const float2 a = pr[min(lane, np - 1)], b = pr[min(lane + 64, np - 1)];
+    merge(lane < np ? 16.f : 0.f, a.x, a.y);
+    merge(lane + 64 < np ? 16.f : 0.f, b.x, b.y);
+    float on = dpp_mov<0xB1>(n), om = dpp_mov<0xB1>(mean), o2 = dpp_mov<0xB1>(M2);
+    merge(on, om, o2);
+    on = dpp_mov<0x4E>(n), om = dpp_mov<0x4E>(mean), o2 = dpp_mov<0x4E>(M2);
+    merge(on, om, o2);
+    on = dpp_mov<0x141>(n), om = dpp_mov<0x141>(mean), o2 = dpp_mov<0x141>(M2);
+    merge(on, om, o2);
+    on = dpp_mov<0x140>(n), om = dpp_mov<0x140>(mean), o2 = dpp_mov<0x140>(M2);
+    merge(on, om, o2);
+    on = __shfl_xor(n, 16, 64), om = __shfl_xor(mean, 16, 64), o2 = __shfl_xor(M2, 16, 64);
+    merge(on, om, o2);
+    on = __shfl_xor(n, 32, 64), om = __shfl_xor(mean, 32, 64), o2 = __shfl_xor(M2, 32, 64);
+    merge(on, om, o2);
+    if (lane == 0) {
+      mr[0] = mean;
+      mr[1] = 1.f / sqrtf(M2 / (float)g.d + g.eps);  // biased variance
+    }
+  }
+  __syncthreads();
+  const float mean = mr[0], rstd = mr[1];
+  const float* u = g.u_pre + (size_t)r * g.d;
+  T* o = reinterpret_cast<T*>(g.u_out) + (size_t)r * g.d;
+  for (int c = tid; c < g.d; c += 256) o[c] = from_f32<T>((u[c] - mean) * rstd);
+}
+
 // The sum over a column block's row splits, in split order, and the state
 // update: e = alpha e + beta sum, h = e + P, one thread per output; launched
 // after embed_kernel (the kernel boundary orders the partials' plain stores
-// before these loads).
+// before these loads).  n_u further workgroups normalise the fused context rows.
 template <typename T>
 __global__ __launch_bounds__(256) void embed_reduce_kernel(EmbedArgs g) {
   constexpr int COLS = 16 * Vec<T>::N;
+  const int n_main = (g.M * g.d + 255) / 256;
+  if ((int)blockIdx.x >= n_main) {
+    norm_context_row<T>(g, (int)blockIdx.x - n_main);
+    return;
+  }
   const int q0 = blockIdx.x * 256 + threadIdx.x;
   const bool ok = q0 < g.M * g.d;  // uniform over 16 lanes: M * d is a multiple of 16
   const int q = ok ? q0 : 0;

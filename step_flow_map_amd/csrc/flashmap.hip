@@ -263,7 +263,7 @@ int max_blocks(const fm_config& c) { return std::max(c.max_branches, c.max_reque
 
 struct Layout {
   size_t cache, mods, sched, ctx, h, e_state, u_pre, act_qkv, act_d, attn_o, act_f, qkv;
-  size_t att_po, att_ml, partial, lm_part, lm_lse, counters, dsoft, logits_tmp, sm_part, vs, lnpart, total;
+  size_t att_po, att_ml, partial, lm_part, lm_lse, counters, dsoft, logits_tmp, sm_part, vs, lnpart, lnpart_u, total;
 };
 
 int max_rows(const fm_config& c) { return max_blocks(c) * KB; }
@@ -321,6 +321,7 @@ Layout make_layout(const fm_config& c) {
   L.lm_lse = take((size_t)LM_GRID * Mb * 8);
   L.vs = take(vs_scratch_bytes(max_blocks(c), KB));  // branches of one request, or requests
   L.lnpart = take((size_t)KB * LN_PART_MAX * sizeof(float2));  // row statistics for the fused LayerNorms
+  L.lnpart_u = take((size_t)16 * LN_PART_MAX * sizeof(float2));  // and for the new context rows (max_new <= 16)
   L.counters = take((size_t)N_COUNTER_SLOTS * COUNTER_STRIDE * 4);
   if (c.max_steps > 1) {
     L.dsoft = take(Mb * (size_t)c.V * es);
@@ -445,6 +446,7 @@ fm_status gemm(fm_handle* h, int epi, const void* A, int lda, int M, const void*
       const int grid = cdiv(N, 16 * AS_TILES) * S_as;
       const int mt = cdiv(M, 16);
       const bool ln_after = epi == EPI_RESID && e.ln_out;
+      if (e.ln_part) return fail(FM_EINVAL, "no row statistics from the LDS-slice contraction");
       if (ln_after && !resid_ln_fused(M, N, K, h->cfg.dtype))
         return fail(FM_EINVAL, "no LayerNorm-fused reduce for this contraction");
       if (KS_as == 512) {
@@ -567,10 +569,12 @@ fm_status probe_end(fm_handle* h, int kernel, hipStream_t st);
 // counters and the roofline describe, without its split-sum kernel); -1
 // records nothing
 // ln_part: where the reduce also writes h's per-16-column row statistics for
-// a fused LayerNorm that follows, or null
+// a fused LayerNorm that follows, or null.  n_u > 0: the reduce also applies
+// the context fusion's LayerNorm to the n_u rows that fuse_rows left in u_pre
+// (with their statistics), writing them to u_out.
 template <typename T>
 fm_status embed(fm_handle* h, const void* x, int ldx, int M, float alpha, float beta, hipStream_t st,
-                int probe = -1, float2* ln_part = nullptr) {
+                int probe = -1, float2* ln_part = nullptr, int n_u = 0, T* u_out = nullptr) {
   const fm_config& c = h->cfg;
   if (M > 64) return fail(FM_EINVAL, "embedding contraction with %d rows exceeds 64", M);
   EmbedPlan p = plan_embed(c.d, c.dtype, M);
@@ -594,6 +598,14 @@ fm_status embed(fm_handle* h, const void* x, int ldx, int M, float alpha, float 
   a.use_pos = 1;
   a.ln_part = ln_part;
   a.ln_part_ld = LN_PART_MAX;
+  a.u_pre = h->at<float>(h->lay.u_pre);
+  a.u_part = h->at<float2>(h->lay.lnpart_u);
+  a.u_part_ld = LN_PART_MAX;
+  a.u_out = u_out;
+  a.n_u = n_u;
+  a.eps = 1e-6f;
+  if (n_u < 0 || n_u > 16 || (n_u > 0 && (!u_out || c.d / 16 > LN_PART_MAX)))
+    return fail(FM_EINVAL, "%d context rows for the embedding's reduce to normalise", n_u);
   if (p.Ss > EMB_SPLITS_MAX) return fail(FM_EINVAL, "embedding with %d row splits (at most %d)", p.Ss, EMB_SPLITS_MAX);
   const dim3 grid(p.grid), block(EMB_WAVES * 64);
   FM_TRY(probe_begin(h, probe, st));
@@ -605,7 +617,7 @@ fm_status embed(fm_handle* h, const void* x, int ldx, int M, float alpha, float 
   }
   FM_LAUNCHED("embed_kernel");
   FM_TRY(probe_end(h, probe, st));
-  hipLaunchKernelGGL((embed_reduce_kernel<T>), dim3(cdiv(M * c.d, 256)), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((embed_reduce_kernel<T>), dim3(cdiv(M * c.d, 256) + n_u), dim3(256), 0, st, a);
   FM_LAUNCHED("embed_reduce_kernel");
   return FM_OK;
 }
@@ -820,16 +832,27 @@ const void* offset_rows(const void* p, size_t elems) {
   return reinterpret_cast<const T*>(p) + elems;
 }
 
-// u rows (fusion + LN) for n context rows, written to out (storage type)
+// whether the embedding's reduce can apply the context fusion's LayerNorm to
+// n new rows (their statistics fit its per-16-column buffer)
+bool ln_u_in_reduce(const fm_config& c, int n) { return n > 0 && n <= 16 && c.d / 16 <= LN_PART_MAX; }
+
+// u rows (fusion + LN) for n context rows, written to out (storage type).
+// ln_later: the contraction writes the rows' per-16-column statistics and the
+// LayerNorm is left to the embedding's reduce (out is then unused here).
 template <typename T>
-fm_status fuse_rows(fm_handle* h, const void* feats, int n, T* out, hipStream_t st) {
+fm_status fuse_rows(fm_handle* h, const void* feats, int n, T* out, hipStream_t st, bool ln_later = false) {
   const fm_config& c = h->cfg;
   const int K5 = c.n_ctx_layers * c.H;
   EpiParams e{};
   e.bias = h->w.b_f;
   e.out_f32 = h->at<float>(h->lay.u_pre);
   e.ld_f32 = c.d;
+  if (ln_later) {
+    e.ln_part = h->at<float2>(h->lay.lnpart_u);
+    e.ln_part_ld = LN_PART_MAX;
+  }
   FM_TRY(gemm<T>(h, EPI_F32, feats, K5, n, h->w.W_f, c.d, K5, e, st));
+  if (ln_later) return FM_OK;
   return ln_mod<T>(h, h->at<float>(h->lay.u_pre), n, nullptr, nullptr, out, c.d, st);
 }
 
@@ -926,14 +949,17 @@ fm_status draft_impl(fm_handle* h, const void* noise, int B, const void* new_fea
   float* hres = h->at<float>(h->lay.h);
   const float* mods_all = h->at<float>(h->lay.mods);
 
-  // context rows appended in this step: u goes below the block rows of act_qkv
-  if (n_new > 0) FM_TRY(fuse_rows<T>(h, new_feats, n_new, act_qkv + (size_t)Mb * d, st));
+  // context rows appended in this step: u goes below the block rows of act_qkv,
+  // normalised by the first embedding's reduce where it can
+  const bool u_in_reduce = ln_u_in_reduce(c, n_new);
+  if (n_new > 0) FM_TRY(fuse_rows<T>(h, new_feats, n_new, act_qkv + (size_t)Mb * d, st, u_in_reduce));
 
   for (int j = 0; j < h->n_steps; ++j) {
     const float s = h->times[j], t = h->times[j + 1];
     const float* mods = mods_all + (size_t)j * (6 * L + 2) * d;
     if (j == 0) {
-      FM_TRY(embed<T>(h, noise, c.V, Mb, 0.f, 1.f, st, FM_PROBE_EMBED, lnp));
+      FM_TRY(embed<T>(h, noise, c.V, Mb, 0.f, 1.f, st, FM_PROBE_EMBED, lnp, u_in_reduce ? n_new : 0,
+                      act_qkv + (size_t)Mb * d));
     } else {
       const float sp = h->times[j - 1];
       FM_TRY(embed<T>(h, h->at<T>(h->lay.dsoft), c.V, Mb, (1.f - s) / (1.f - sp), (s - sp) / (1.f - sp), st, -1,

@@ -59,8 +59,8 @@ struct EpiParams {
   const float* ln_scale;
   void* ln_out;
   int ln_ldo;
-  // EPI_RESID: per-16-column statistics (mean, M2) of the updated rows for the
-  // LayerNorm fused into the next contraction, at ln_part[m * ln_part_ld + n / 16]
+  // EPI_RESID / EPI_F32: per-16-column statistics (mean, M2) of the stored rows
+  // for a LayerNorm applied later, at ln_part[m * ln_part_ld + n / 16]
   float2* ln_part;
   int ln_part_ld;
 };
@@ -78,13 +78,13 @@ struct GemmArgs {
   uint32_t* counters;  // one per 16-row tile, COUNTER_STRIDE apart; zero on entry and exit
 };
 
-// returns the stored residual value for EPI_RESID (0 otherwise)
+// returns the stored float32 value for EPI_F32 and EPI_RESID (0 otherwise)
 template <typename T, int EPI>
 __device__ __forceinline__ float epilogue(const EpiParams& e, int m, int n, float v) {
   if (e.bias) v += to_f32<T>(reinterpret_cast<const T*>(e.bias)[n]);
   if (EPI == EPI_F32) {
     e.out_f32[(size_t)m * e.ld_f32 + n] = v;
-    return 0.f;
+    return v;
   } else if (EPI == EPI_ACT) {
     reinterpret_cast<T*>(e.out_act)[(size_t)m * e.ld_act + n] = from_f32<T>(v);
   } else if (EPI == EPI_GELU) {
@@ -127,14 +127,15 @@ __device__ __forceinline__ float epilogue(const EpiParams& e, int m, int n, floa
   return 0.f;
 }
 
-// The epilogue of output (m, n) when ok, then (EPI_RESID with ln_part) the
-// statistics of the updated row over the tile's 16 columns, which the 16
-// lanes of a DPP row hold (row m, columns 16 (n / 16) ..): every lane calls it.
+// The epilogue of output (m, n) when ok, then (EPI_F32 or EPI_RESID with
+// ln_part) the statistics of the stored row over the tile's 16 columns, which
+// the 16 lanes of a DPP row hold (row m, columns 16 (n / 16) ..): every lane
+// calls it.
 template <typename T, int EPI>
 __device__ __forceinline__ void epilogue_out(const EpiParams& e, int m, int n, float v, bool ok) {
   float r = 0.f;
   if (ok) r = epilogue<T, EPI>(e, m, n, v);
-  if constexpr (EPI == EPI_RESID) {
+  if constexpr (EPI == EPI_RESID || EPI == EPI_F32) {
     if (e.ln_part) row16_stats(r, ok, e.ln_part + (size_t)(ok ? m : 0) * e.ln_part_ld + (n >> 4));
   }
 }
