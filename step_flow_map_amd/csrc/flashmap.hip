@@ -398,7 +398,10 @@ namespace {
 // ------------------------------------------------------------------ launchers
 template <typename T, int MT, int EPI>
 void launch_gemm_mt(const GemmArgs& a, const EpiParams& e, int grid, int waves, int tg, hipStream_t st) {
-  if (tg == 2)
+  if (tg == 2 && MT == 1 && a.k_split > 8 * ChunkT<T>::KC)  // several chunks a wave
+    hipLaunchKernelGGL((gemm_tg_kernel<T, 1, 8, 2, EPI, false, true>), dim3(grid), dim3(8 * 64), 0, st, a, e,
+                       LnArgs{});
+  else if (tg == 2)
     hipLaunchKernelGGL((gemm_tg_kernel<T, MT, 8, 2, EPI, false>), dim3(grid), dim3(8 * 64), 0, st, a, e, LnArgs{});
   else if (tg == 1 && waves == 8)
     hipLaunchKernelGGL((gemm_tg_kernel<T, MT, 8, 1, EPI, false>), dim3(grid), dim3(8 * 64), 0, st, a, e, LnArgs{});

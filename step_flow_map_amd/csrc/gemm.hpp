@@ -301,7 +301,9 @@ constexpr int LN_PART_MAX = 128;  // K / 16 for K up to 2048, the fused LayerNor
 // NW chunks): a workgroup owns TT adjacent tiles and wave w takes chunks w,
 // w+NW, ...  For a chunk it loads the A operand first (it is consumed first,
 // and loads complete in issue order), then the TT weight chunks, and applies
-// the A fragments to all TT tiles, so A is fetched once per TT tiles.  The
+// the A fragments to all TT tiles, so A is fetched once per TT tiles.  PIPE
+// (one row tile, several chunks a wave): a wave's next chunk is in flight
+// while it consumes the current one.  The
 // waves then reduce through LDS in wave order and run the epilogue.
 //
 // With LN the k range is at most NW chunks, so each wave holds one chunk of
@@ -314,7 +316,7 @@ constexpr int LN_PART_MAX = 128;  // K / 16 for K up to 2048, the fused LayerNor
 // LeVeque), and every wave then normalises and modulates its values, rounds
 // them to the storage type into its LDS tile in the weights' layout, and
 // reads its MFMA fragments back from there.
-template <typename T, int MT, int NW, int TT, int EPI, bool LN>
+template <typename T, int MT, int NW, int TT, int EPI, bool LN, bool PIPE = false>
 __global__ __launch_bounds__(NW * 64) void gemm_tg_kernel(GemmArgs g, EpiParams e, LnArgs ln) {
   typedef typename Vec<T>::type VT;
   constexpr int VE = ChunkT<T>::VE;
@@ -328,8 +330,10 @@ __global__ __launch_bounds__(NW * 64) void gemm_tg_kernel(GemmArgs g, EpiParams 
   // the weights' layout) rather than as fragments in registers
   static_assert(!LN || MT <= 2, "fused LayerNorm supports at most 16 further rows");
   static_assert(!LN || NW == 8, "fused LayerNorm: 32 threads per row of statistics");
+  static_assert(!PIPE || (!LN && MT == 1), "two register sets of chunks fit one row tile only");
   constexpr bool CTX_LDS = LN && MT == 2;
   __shared__ uint4 sctx[CTX_LDS ? NW : 1][CTX_LDS ? 512 : 1];
+  __shared__ uint4 sa[PIPE ? NW : 1][PIPE ? 512 : 1];  // PIPE: the A chunk of each wave
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int j = lane & 15, grp = lane >> 4;
@@ -353,8 +357,9 @@ __global__ __launch_bounds__(NW * 64) void gemm_tg_kernel(GemmArgs g, EpiParams 
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int c = wave; LN ? c == wave : c < nch; c += NW) {
-    const bool has = c < nch;  // LN: every wave takes part in the statistics
+  if constexpr (LN) {
+    const int c = wave;
+    const bool has = c < nch;  // every wave takes part in the statistics
     const int k0 = k_begin + c * KC;
     bool kok[8];
 #pragma unroll
@@ -375,7 +380,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_tg_kernel(GemmArgs g, EpiParams 
     constexpr int PU = LN ? LN_PART_MAX / 32 : 1;
     const int prow = tid >> 5, psub = tid & 31, np = g.K >> 4;
     float2 pp[PU];
-    if constexpr (LN) {
+    {
 #pragma unroll
       for (int u = 0; u < PU; ++u)  // unconditional (clamped) loads: the count masks the unused ones
         pp[u] = ln.part[(size_t)prow * ln.part_ld + min(psub + 32 * u, np - 1)];
@@ -394,7 +399,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_tg_kernel(GemmArgs g, EpiParams 
     uint4 r[TT][8];
 #pragma unroll
     for (int t = 0; t < TT; ++t) chunk_load<T>(r[t], W, g.ldw, n0 + 16 * t, g.N, k0, k_end);
-    if constexpr (LN) {
+    {
       // every load above is issued before the statistics consume the first one
       __builtin_amdgcn_sched_barrier(0);
       // Row statistics: thread t merges its partials of row t / 32 in order
@@ -457,19 +462,9 @@ __global__ __launch_bounds__(NW * 64) void gemm_tg_kernel(GemmArgs g, EpiParams 
       wave_lds_sync();
       // the context rows (issued after the residual rows) wait in their tile
       if constexpr (CTX_LDS) chunk_to_lds(ra[1], sctx[wave]);
-    } else {
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        chunk_to_lds(ra[mt], wt);
-        wave_lds_sync();
-#pragma unroll
-        for (int st = 0; st < 8; ++st) af[mt][st] = as_vec<T>(chunk_frag(wt, st));
-        wave_lds_sync();
-      }
     }
-    if (!has) break;
 #pragma unroll
-    for (int t = 0; t < TT; ++t) {
+    for (int t = 0; t < TT && has; ++t) {
       chunk_to_lds(r[t], wt);
       wave_lds_sync();
 #pragma unroll
@@ -482,6 +477,82 @@ __global__ __launch_bounds__(NW * 64) void gemm_tg_kernel(GemmArgs g, EpiParams 
         }
       }
       wave_lds_sync();
+    }
+  } else if constexpr (!PIPE) {
+    for (int c = wave; c < nch; c += NW) {
+      const int k0 = k_begin + c * KC;
+      bool kok[8];
+#pragma unroll
+      for (int st = 0; st < 8; ++st) kok[st] = k0 + (4 * st + grp) * VE < k_end;
+      // A rows of the chunk in the weights' pattern; their fragments come
+      // back through LDS
+      uint4 ra[MT][8];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) chunk_load_act<T>(ra[mt], A, g.lda, mt * 16, g.M, k0, k_end);
+      VT af[MT][8];
+      uint4 r[TT][8];
+#pragma unroll
+      for (int t = 0; t < TT; ++t) chunk_load<T>(r[t], W, g.ldw, n0 + 16 * t, g.N, k0, k_end);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        chunk_to_lds(ra[mt], wt);
+        wave_lds_sync();
+#pragma unroll
+        for (int st = 0; st < 8; ++st) af[mt][st] = as_vec<T>(chunk_frag(wt, st));
+        wave_lds_sync();
+      }
+#pragma unroll
+      for (int t = 0; t < TT; ++t) {
+        chunk_to_lds(r[t], wt);
+        wave_lds_sync();
+#pragma unroll
+        for (int st = 0; st < 8; ++st) {
+          const VT b = as_vec<T>(chunk_frag(wt, st));
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) mma(acc[t][mt], (kok[st] && aok[mt]) ? af[mt][st] : vzero<VT>(), b);
+        }
+        wave_lds_sync();
+      }
+    }
+  } else {
+    // One row tile, several chunks a wave: two register sets in turn, the
+    // next chunk's loads in flight while the current chunk is consumed (a
+    // wave without a next chunk issues placeholder loads of one line).  The A
+    // chunk waits in a second wave-private tile, read at each MFMA step.
+    uint4* at = sa[wave];
+    auto issue = [&](int c, uint4 (&xa)[8], uint4 (&xr)[TT][8]) {
+      const bool live = c < nch;
+      const int k0 = k_begin + c * KC;
+      chunk_load_act<T>(xa, A, g.lda, 0, g.M, k0, k_end, live);
+#pragma unroll
+      for (int t = 0; t < TT; ++t) chunk_load<T>(xr[t], W, g.ldw, n0 + 16 * t, g.N, k0, k_end, live);
+    };
+    auto consume = [&](int c, const uint4 (&xa)[8], const uint4 (&xr)[TT][8]) {
+      const int k0 = k_begin + c * KC;
+      bool kok[8];
+#pragma unroll
+      for (int st = 0; st < 8; ++st) kok[st] = aok[0] && k0 + (4 * st + grp) * VE < k_end;
+      chunk_to_lds(xa, at);
+#pragma unroll
+      for (int t = 0; t < TT; ++t) {
+        chunk_to_lds(xr[t], wt);
+        wave_lds_sync();
+#pragma unroll
+        for (int st = 0; st < 8; ++st) {
+          const VT a = as_vec<T>(chunk_frag(at, st));
+          mma(acc[t][0], kok[st] ? a : vzero<VT>(), as_vec<T>(chunk_frag(wt, st)));
+        }
+        wave_lds_sync();
+      }
+    };
+    uint4 a0[8], r0[TT][8], a1[8], r1[TT][8];
+    issue(wave, a0, r0);
+    for (int c = wave; c < nch; c += 2 * NW) {
+      issue(c + NW, a1, r1);
+      consume(c, a0, r0);
+      if (c + NW >= nch) break;
+      issue(c + 2 * NW, a0, r0);
+      consume(c + NW, a1, r1);
     }
   }
 

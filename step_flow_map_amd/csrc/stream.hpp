@@ -35,17 +35,20 @@ struct ChunkT {
 // that load right away and defeat the prefetch.  Rows >= N only feed output
 // columns that are never stored, and columns >= K meet A values that the
 // consumer zeroes, so the clamped data never reaches a result.
+// live = false: every lane reads the matrix's first 16 bytes (one line per
+// instruction), a placeholder for a chunk that does not exist.
 template <typename T>
-__device__ __forceinline__ void chunk_load(uint4 (&r)[8], const T* W, size_t ldw, int n0, int N, int k0, int K) {
+__device__ __forceinline__ void chunk_load(uint4 (&r)[8], const T* W, size_t ldw, int n0, int N, int k0, int K,
+                                           bool live = true) {
   constexpr int VE = ChunkT<T>::VE;
   const int lane = threadIdx.x & 63;
   const int half = lane >> 5, p = lane & 31;
   const int kk = k0 + p * VE;
-  const int kc = kk < K ? kk : 0;
+  const int kc = live && kk < K ? kk : 0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int row = n0 + 2 * i + half;
-    r[i] = ldg_stream(W + (size_t)(row < N ? row : 0) * ldw + kc);
+    r[i] = ldg_stream(W + (size_t)(live && row < N ? row : 0) * ldw + kc);
   }
 }
 
@@ -53,16 +56,17 @@ __device__ __forceinline__ void chunk_load(uint4 (&r)[8], const T* W, size_t ldw
 // with ordinary cached loads: every workgroup reads the same A.  Rows >= R
 // read row 0 and columns >= K read column 0 (both masked by the consumer).
 template <typename T>
-__device__ __forceinline__ void chunk_load_act(uint4 (&r)[8], const T* A, size_t lda, int r0, int R, int k0, int K) {
+__device__ __forceinline__ void chunk_load_act(uint4 (&r)[8], const T* A, size_t lda, int r0, int R, int k0, int K,
+                                               bool live = true) {
   constexpr int VE = ChunkT<T>::VE;
   const int lane = threadIdx.x & 63;
   const int half = lane >> 5, p = lane & 31;
   const int kk = k0 + p * VE;
-  const int kc = kk < K ? kk : 0;
+  const int kc = live && kk < K ? kk : 0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int row = r0 + 2 * i + half;
-    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(A + (size_t)(row < R ? row : 0) * lda + kc);
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(A + (size_t)(live && row < R ? row : 0) * lda + kc);
     r[i] = make_uint4(v[0], v[1], v[2], v[3]);
   }
 }

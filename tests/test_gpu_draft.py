@@ -30,6 +30,14 @@ WIDE_F32 = TINY.with_(name="wide_f32", V=1000, d=1152, nh=9)
 W2048_BF16 = TINY.with_(name="w2048_bf16", dtype="bf16", V=2000, d=2048, nh=16, H=520, c_prefill=40)
 
 
+# context fusions long enough that a wave of the fusion contraction owns
+# several chunks of its k split (the two-register-set pipeline): bf16 with
+# 5*3304 = 16520 = 64.5 chunks (a ragged last chunk, a last split of two
+# chunks), float32 with 5*2048 = 10240 = 80 chunks of 128
+LONG_FUSE_BF16 = TINY.with_(name="long_fuse_bf16", dtype="bf16", V=1000, H=3304)
+LONG_FUSE_F32 = TINY.with_(name="long_fuse_f32", H=2048)
+
+
 def _case(cfg, variant="random", B=1, draw=0):
     w = synth.make_weights(cfg, variant)
     feats = synth.make_features(cfg)
@@ -62,6 +70,25 @@ def test_draft_matches_oracle(cfg, variant):
         return ties
 
     exact_or_reseed(case, f"{cfg.name} {variant}")
+
+
+@pytest.mark.parametrize("cfg", [LONG_FUSE_BF16, LONG_FUSE_F32], ids=["bf16", "f32"])
+def test_long_context_fusion_matches_oracle(cfg):
+    print(f"[draft parity] {cfg.name}", flush=True)
+    w = synth.make_weights(cfg)
+    feats = synth.make_features(cfg)
+    dr = make_drafter(cfg, w)
+    dr.set_schedule(cfg.times)
+
+    def case(draw):
+        noise = synth.make_noise(cfg, 1, draw)
+        dr.truncate(0)
+        tok, logits, hidden = run_draft(dr, cfg, noise, feats, cfg.c_prefill, want_hidden=True)
+        rel, ties = check_draft(cfg, w, noise, feats, cfg.c_prefill, tok, logits, hidden)
+        print(f"  draw {draw}: max row logit error {rel:.2e}, near-ties {ties}")
+        return ties
+
+    exact_or_reseed(case, cfg.name)
 
 
 def test_context_paths_agree():
