@@ -29,6 +29,7 @@
 // Results never depend on scheduling.
 #pragma once
 #include "common.hpp"
+#include "l2warm.hpp"
 #include "stream.hpp"
 
 namespace fm {
@@ -67,6 +68,7 @@ struct AttnArgs {
   uint32_t* counters;  // [B*nh], COUNTER_STRIDE apart
   void* out;           // [B*K][d]
   float scale;         // 1/sqrt(hd)
+  L2Warm warm;         // attention_kernel: workgroups from warm.first_wg on warm the L2s
 };
 
 // Context rows branch b sees: its request's length when the stream reaches the
@@ -231,6 +233,10 @@ __global__ __launch_bounds__(NW * 64) void attention_kernel(AttnArgs g) {
   __shared__ float sm[NW][KB], sl[NW][KB];
   __shared__ int flag;
 
+  if (g.warm.base && (int)blockIdx.x >= g.warm.first_wg) {  // the next contraction's weights
+    l2_warm(g.warm, blockIdx.x, NW * 64);
+    return;
+  }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int j = lane & 15, grp = lane >> 4;
   const int range = blockIdx.x % g.n_ranges;

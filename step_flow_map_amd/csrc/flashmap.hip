@@ -386,7 +386,7 @@ struct fm_handle {
   template <typename P> P* at(size_t off) { return reinterpret_cast<P*>(ws + off); }
   // device-resident context lengths (and the overflow flag after them)
   int* ctx_dev() { return at<int>(lay.ctx); }
-  // key / value cache of DiT block l
+  int n_cu = 256;  // compute units of the device (sizes the L2 warming)
   // key / value cache of DiT block l, request 0 (request r at + r * req_stride())
   size_t req_stride() const { return (size_t)cache_positions(cfg) * cfg.d; }
   template <typename T> T* kcache(int l) { return at<T>(lay.cache) + (size_t)l * 2 * cfg.max_requests * req_stride(); }
@@ -504,6 +504,23 @@ fm_status gemm(fm_handle* h, int epi, const void* A, int lda, int M, const void*
     case EPI_RESID: return launch_gemm_epi<T, EPI_RESID>(a, e, p, st);
     default: return launch_gemm_epi<T, EPI_QKV>(a, e, p, st);
   }
+}
+
+// The L2 warming for the contraction gemm() runs for (M, N, K) on weights W,
+// where its workgroup b reads tile group b alone: the tile paths without a k
+// split (gemm_kernel, or gemm_tg_kernel with its tiles per workgroup), and N
+// a whole number of groups.  False: no such mapping.
+bool l2_warm_plan(const fm_handle* h, int M, int N, int K, const void* W, L2Warm* w) {
+  const fm_dtype t = h->cfg.dtype;
+  int S_as, KS_as;
+  if (t == FM_BF16 && use_as(M, N, K, t, &S_as, &KS_as)) return false;
+  const GemmPlan p = plan_gemm(M, N, K, t);
+  const int tiles = p.tg == 2 ? 2 : 1;
+  if (p.S != 1 || N % (16 * tiles) || p.grid != N / (16 * tiles)) return false;
+  w->base = reinterpret_cast<const uint4*>(W);
+  w->group_u4 = (size_t)16 * tiles * K * esize(t) / 16;
+  w->n_groups = N / (16 * tiles);
+  return (size_t)16 * tiles * K * esize(t) % 16 == 0;
 }
 
 // LayerNorm + modulation of the 16 residual rows x fused into the contraction's
@@ -629,8 +646,11 @@ fm_status embed(fm_handle* h, const void* x, int ldx, int M, float alpha, float 
 // branch b's request (its visible context is that request's device-resident
 // length plus n_new[b]).  Grids are sized for the cache capacity; the ranges
 // in use follow the current length on the device.
+// warm: the next contraction's L2 warming, carried by extra workgroups of
+// attention_kernel on the CUs it leaves idle (null: none)
 template <typename T>
-fm_status attention(fm_handle* h, int l, int B, const int* n_new, bool own_ctx, hipStream_t st) {
+fm_status attention(fm_handle* h, int l, int B, const int* n_new, bool own_ctx, hipStream_t st,
+                    const L2Warm* warm = nullptr) {
   const fm_config& c = h->cfg;
   const int hd = c.d / c.n_heads;
   AttnArgs a{};
@@ -682,7 +702,13 @@ fm_status attention(fm_handle* h, int l, int B, const int* n_new, bool own_ctx, 
     }
   }
   a.n_ranges = attn_max_ranges(cap_blocks + 1, ATT_WAVES);
-  const int grid = B * c.n_heads * a.n_ranges;
+  int grid = B * c.n_heads * a.n_ranges;
+  if (warm && grid + 8 <= h->n_cu) {
+    a.warm = *warm;
+    a.warm.first_wg = grid;
+    a.warm.n_wg = (h->n_cu - grid) / 8 * 8;
+    grid += a.warm.n_wg;
+  }
   if (hd == 128)
     hipLaunchKernelGGL((attention_kernel<T, 128, ATT_WAVES>), dim3(grid), dim3(ATT_WAVES * 64), 0, st, a);
   else
@@ -992,7 +1018,12 @@ fm_status draft_impl(fm_handle* h, const void* noise, int B, const void* new_fea
           FM_TRY(gemm<T>(h, EPI_QKV, act_qkv, d, m_qkv, blk(h, l, B_WQKV), 3 * d, d, e, st));
         }
       }
-      FM_TRY(attention<T>(h, l, B, nb_new, bt != nullptr, st));
+      {
+        // the CUs attention leaves idle warm the L2s with W_o's tiles
+        L2Warm wo{};
+        const bool warm = l2_warm_plan(h, Mb, d, d, blk(h, l, B_WO), &wo);
+        FM_TRY(attention<T>(h, l, B, nb_new, bt != nullptr, st, warm ? &wo : nullptr));
+      }
       {
         EpiParams e{};
         e.bias = blk(h, l, B_BO);
@@ -1216,6 +1247,9 @@ fm_status fm_create(const fm_config* cfg, void* workspace, size_t ws_bytes, int 
   h->device = device;
   h->ws = reinterpret_cast<char*>(workspace);
   h->lay = lay;
+  int n_cu = 0;
+  if (hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, device) == hipSuccess && n_cu > 0)
+    h->n_cu = n_cu;
   hipLaunchKernelGGL(zero_u32_kernel, dim3(64), dim3(256), 0, 0, h->at<uint32_t>(lay.counters),
                      (size_t)N_COUNTER_SLOTS * COUNTER_STRIDE);
   hipError_t e = hipGetLastError();

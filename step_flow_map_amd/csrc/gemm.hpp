@@ -15,6 +15,7 @@
 #pragma once
 #include "common.hpp"
 #include "stream.hpp"
+#include "lnfuse.hpp"
 #include "attention.hpp"
 #include "norm.hpp"
 
@@ -279,43 +280,20 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs g, EpiParams e) 
   }
 }
 
-// LayerNorm fused into the A operand (tile-group kernel): rows 0..15 of the
-// contraction are LN(h[r]) * (1 + scale) + shift rounded to the storage type,
-// computed inside the kernel from the float32 residual rows (never rounded
-// before the statistics and the normalisation, which are float32); rows 16..
-// come from GemmArgs::A as usual (context rows, already normalised).
-struct LnArgs {
-  const float* h;      // [16][ldh] float32 residual stream
-  int ldh;
-  const float* shift;  // [K]
-  const float* scale;  // [K]
-  float eps;
-  // per-16-column (mean, M2) of every row of h, written by the kernel that
-  // produced h: [16][part_ld], K / 16 entries per row
-  const float2* part;
-  int part_ld;
-};
-constexpr int LN_PART_MAX = 128;  // K / 16 for K up to 2048, the fused LayerNorm's longest row
-
 // Tile-group variant for wide layers (many 16-row tiles, a k range of at most
 // NW chunks): a workgroup owns TT adjacent tiles and wave w takes chunks w,
 // w+NW, ...  For a chunk it loads the A operand first (it is consumed first,
 // and loads complete in issue order), then the TT weight chunks, and applies
 // the A fragments to all TT tiles, so A is fetched once per TT tiles.  PIPE
 // (one row tile, several chunks a wave): a wave's next chunk is in flight
-// while it consumes the current one.  The
-// waves then reduce through LDS in wave order and run the epilogue.
+// while it consumes the current one.  The waves then reduce through LDS in
+// wave order and run the epilogue.
 //
-// With LN the k range is at most NW chunks, so each wave holds one chunk of
-// the 16 residual rows.  It loads the chunk coalesced (a 1 KB row piece per
-// instruction for bf16 storage, two 512-byte row pieces for float32: every
-// lane holds 4 consecutive columns of one row), sums its columns per row for
-// the mean and then for the sum of squared deviations (through its LDS tile,
-// in lane order, so each value has one summation order), the workgroup
-// combines the waves' pairs in wave order (pairwise update of Chan, Golub and
-// LeVeque), and every wave then normalises and modulates its values, rounds
-// them to the storage type into its LDS tile in the weights' layout, and
-// reads its MFMA fragments back from there.
+// With LN (the k range is at most NW = 8 chunks) row tile 0 is the LayerNorm
+// of the 16 residual rows (ln_issue / ln_finish): each wave loads its chunk of
+// the rows coalesced (every lane holds 4 consecutive columns of one row) and
+// the row statistics from the producer's per-16-column partials, all before
+// its weights, and normalises into MFMA fragments while the weights stream.
 template <typename T, int MT, int NW, int TT, int EPI, bool LN, bool PIPE = false>
 __global__ __launch_bounds__(NW * 64) void gemm_tg_kernel(GemmArgs g, EpiParams e, LnArgs ln) {
   typedef typename Vec<T>::type VT;
@@ -367,29 +345,8 @@ __global__ __launch_bounds__(NW * 64) void gemm_tg_kernel(GemmArgs g, EpiParams 
     // ---- issue: residual rows, modulation, A rows, weights.  Addresses are
     // clamped in range and nothing here is conditional, so no load waits for
     // another one before the statistics need the residual rows.
-    // LN: float4 element i of the lane covers row hrow(i), columns
-    // k0 + hcol .. + 3 of the chunk (the same columns in every row it holds)
-    constexpr int HN = LN ? KC / 16 : 1;  // float4 per lane: 16 rows x KC floats / (64 lanes x 4)
-    const int hcol = (lane * 4) % KC;
-    auto hrow = [&](int i) { return (i * 256 + lane * 4) / KC; };
-    const bool hok = has && k0 + hcol < k_end;
-    float4 hv[HN];
-    float4 msc = float4{0.f, 0.f, 0.f, 0.f}, msh = float4{0.f, 0.f, 0.f, 0.f};
-    // LN: thread t takes row t / 32 and its statistics partials (t % 32) + 32u,
-    // loaded first so that the row statistics are ready before the rows
-    constexpr int PU = LN ? LN_PART_MAX / 32 : 1;
-    const int prow = tid >> 5, psub = tid & 31, np = g.K >> 4;
-    float2 pp[PU];
-    {
-#pragma unroll
-      for (int u = 0; u < PU; ++u)  // unconditional (clamped) loads: the count masks the unused ones
-        pp[u] = ln.part[(size_t)prow * ln.part_ld + min(psub + 32 * u, np - 1)];
-      const int kc = hok ? k0 + hcol : 0;
-#pragma unroll
-      for (int i = 0; i < HN; ++i) hv[i] = *reinterpret_cast<const float4*>(ln.h + (size_t)hrow(i) * ln.ldh + kc);
-      msc = *reinterpret_cast<const float4*>(ln.scale + kc);
-      msh = *reinterpret_cast<const float4*>(ln.shift + kc);
-    }
+    LnChunk<T> lc;
+    ln_issue<T>(lc, ln, g.K, k0, k_end, has);
     // A rows of the chunk in the weights' pattern; their fragments come back
     // through LDS below
     uint4 ra[MT][8];
@@ -402,64 +359,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_tg_kernel(GemmArgs g, EpiParams 
     {
       // every load above is issued before the statistics consume the first one
       __builtin_amdgcn_sched_barrier(0);
-      // Row statistics: thread t merges its partials of row t / 32 in order
-      // (pairwise update of Chan, Golub and LeVeque; every partial covers 16
-      // columns), the 32 threads of the row merge in a fixed tree (a DPP row,
-      // then its two halves), and thread 32r publishes row r's mean and
-      // 1 / std through LDS.
-      float n = 0.f, mean = 0.f, M2 = 0.f;
-      auto merge = [&](float nb, float mb, float m2b) {
-        const float nn = n + nb, delta = mb - mean;
-        const float f = nb > 0.f ? nb / nn : 0.f;
-        mean += delta * f;
-        M2 += nb > 0.f ? m2b + delta * delta * (n * f) : 0.f;
-        n = nn;
-      };
-#pragma unroll
-      for (int u = 0; u < PU; ++u) merge(psub + 32 * u < np ? 16.f : 0.f, pp[u].x, pp[u].y);
-      {
-        float on = dpp_mov<0xB1>(n), om = dpp_mov<0xB1>(mean), o2 = dpp_mov<0xB1>(M2);
-        merge(on, om, o2);
-        on = dpp_mov<0x4E>(n), om = dpp_mov<0x4E>(mean), o2 = dpp_mov<0x4E>(M2);
-        merge(on, om, o2);
-        on = dpp_mov<0x141>(n), om = dpp_mov<0x141>(mean), o2 = dpp_mov<0x141>(M2);
-        merge(on, om, o2);
-        on = dpp_mov<0x140>(n), om = dpp_mov<0x140>(mean), o2 = dpp_mov<0x140>(M2);
-        merge(on, om, o2);
-        on = __shfl_xor(n, 16, 64), om = __shfl_xor(mean, 16, 64), o2 = __shfl_xor(M2, 16, 64);
-        merge(on, om, o2);
-      }
-      if (psub == 0) {
-        sstat[prow][0] = mean;
-        sstat[prow][1] = 1.f / sqrtf(M2 / (float)g.K + ln.eps);
-      }
-      lds_barrier();  // the rows and the weights stay in flight
-      // normalise, modulate, round, and place in the wave's tile as the
-      // weights' chunk layout (piece p of row r at r * 32 + (p ^ r))
-#pragma unroll
-      for (int i = 0; i < HN; ++i) {
-        const int rr = hrow(i);
-        const float m_r = sstat[rr][0], s_r = sstat[rr][1];
-        const float y0 = ((hv[i].x - m_r) * s_r) * (1.f + msc.x) + msh.x;
-        const float y1 = ((hv[i].y - m_r) * s_r) * (1.f + msc.y) + msh.y;
-        const float y2 = ((hv[i].z - m_r) * s_r) * (1.f + msc.z) + msh.z;
-        const float y3 = ((hv[i].w - m_r) * s_r) * (1.f + msc.w) + msh.w;
-        if constexpr (sizeof(T) == 2) {
-          const int pc = lane >> 1;  // 16-byte piece of 8 columns; this lane holds half of it
-          uint2 u;
-          u.x = (uint32_t)f32_to_bf16(y0) | ((uint32_t)f32_to_bf16(y1) << 16);
-          u.y = (uint32_t)f32_to_bf16(y2) | ((uint32_t)f32_to_bf16(y3) << 16);
-          reinterpret_cast<uint2*>(wt + rr * 32 + (pc ^ rr))[lane & 1] = u;
-        } else {
-          const int pc = lane & 31;
-          wt[rr * 32 + (pc ^ rr)] = make_uint4(__float_as_uint(y0), __float_as_uint(y1), __float_as_uint(y2),
-                                               __float_as_uint(y3));
-        }
-      }
-      wave_lds_sync();
-#pragma unroll
-      for (int st = 0; st < 8; ++st) af[0][st] = as_vec<T>(chunk_frag(wt, st));
-      wave_lds_sync();
+      ln_finish<T>(lc, ln, g.K, wt, sstat, af[0]);
       // the context rows (issued after the residual rows) wait in their tile
       if constexpr (CTX_LDS) chunk_to_lds(ra[1], sctx[wave]);
     }
