@@ -233,7 +233,7 @@ __global__ __launch_bounds__(NW * 64) void attention_kernel(AttnArgs g) {
   __shared__ float sm[NW][KB], sl[NW][KB];
   __shared__ int flag;
 
-  if (g.warm.base && (int)blockIdx.x >= g.warm.first_wg) {  // the next contraction's weights
+  if (g.warm.n_reg > 0 && (int)blockIdx.x >= g.warm.first_wg) {  // the next contractions' weights
     l2_warm(g.warm, blockIdx.x, NW * 64);
     return;
   }

@@ -427,6 +427,50 @@ fm_status launch_gemm_epi(const GemmArgs& a, const EpiParams& e, const GemmPlan&
   return FM_OK;
 }
 
+// The L2 region of the contraction gemm() runs for (M, N, K) on weights W,
+// where its workgroup b reads tile group b alone: the tile paths without a k
+// split (gemm_kernel, or gemm_tg_kernel with its tiles per workgroup), and N
+// a whole number of groups.  False: no such mapping.
+bool l2_region(const fm_handle* h, int M, int N, int K, const void* W, L2Region* r) {
+  const fm_dtype t = h->cfg.dtype;
+  int S_as, KS_as;
+  if (t == FM_BF16 && use_as(M, N, K, t, &S_as, &KS_as)) return false;
+  const GemmPlan p = plan_gemm(M, N, K, t);
+  const int tiles = p.tg == 2 ? 2 : 1;
+  if (p.S != 1 || N % (16 * tiles) || p.grid != N / (16 * tiles)) return false;
+  r->base = reinterpret_cast<const uint4*>(W);
+  r->group_u4 = (size_t)16 * tiles * K * esize(t) / 16;
+  r->off_u4 = 0;
+  r->take_u4 = r->group_u4;
+  r->n_groups = N / (16 * tiles);
+  return true;
+}
+
+// The same for a fused-LayerNorm contraction (gemm_ln: workgroup b reads
+// tiles 2b and 2b + 1)
+bool l2_region_ln(const fm_handle* h, int N, int K, const void* W, L2Region* r) {
+  if (N % 32) return false;
+  r->base = reinterpret_cast<const uint4*>(W);
+  r->group_u4 = (size_t)32 * K * esize(h->cfg.dtype) / 16;
+  r->off_u4 = 0;
+  r->take_u4 = r->group_u4;
+  r->n_groups = N / 32;
+  return true;
+}
+
+// Warming workgroups for a launch of grid workgroups on the CUs it leaves
+// idle: fills w's workgroup range and returns the grid with them (w.n_reg = 0
+// or no idle CUs: grid unchanged, w disabled).
+int l2_warm_attach(const fm_handle* h, int grid, L2Warm& w) {
+  if (w.n_reg <= 0 || grid + 8 > h->n_cu) {
+    w.n_reg = 0;
+    return grid;
+  }
+  w.first_wg = grid;
+  w.n_wg = (h->n_cu - grid) / 8 * 8;
+  return grid + w.n_wg;
+}
+
 // out[m][n] = epilogue( sum_k A[m][k] W[n][k] )
 template <typename T>
 fm_status gemm(fm_handle* h, int epi, const void* A, int lda, int M, const void* W, int N, int K,
@@ -504,23 +548,6 @@ fm_status gemm(fm_handle* h, int epi, const void* A, int lda, int M, const void*
     case EPI_RESID: return launch_gemm_epi<T, EPI_RESID>(a, e, p, st);
     default: return launch_gemm_epi<T, EPI_QKV>(a, e, p, st);
   }
-}
-
-// The L2 warming for the contraction gemm() runs for (M, N, K) on weights W,
-// where its workgroup b reads tile group b alone: the tile paths without a k
-// split (gemm_kernel, or gemm_tg_kernel with its tiles per workgroup), and N
-// a whole number of groups.  False: no such mapping.
-bool l2_warm_plan(const fm_handle* h, int M, int N, int K, const void* W, L2Warm* w) {
-  const fm_dtype t = h->cfg.dtype;
-  int S_as, KS_as;
-  if (t == FM_BF16 && use_as(M, N, K, t, &S_as, &KS_as)) return false;
-  const GemmPlan p = plan_gemm(M, N, K, t);
-  const int tiles = p.tg == 2 ? 2 : 1;
-  if (p.S != 1 || N % (16 * tiles) || p.grid != N / (16 * tiles)) return false;
-  w->base = reinterpret_cast<const uint4*>(W);
-  w->group_u4 = (size_t)16 * tiles * K * esize(t) / 16;
-  w->n_groups = N / (16 * tiles);
-  return (size_t)16 * tiles * K * esize(t) % 16 == 0;
 }
 
 // LayerNorm + modulation of the 16 residual rows x fused into the contraction's
@@ -646,11 +673,11 @@ fm_status embed(fm_handle* h, const void* x, int ldx, int M, float alpha, float 
 // branch b's request (its visible context is that request's device-resident
 // length plus n_new[b]).  Grids are sized for the cache capacity; the ranges
 // in use follow the current length on the device.
-// warm: the next contraction's L2 warming, carried by extra workgroups of
-// attention_kernel on the CUs it leaves idle (null: none)
+// warm: L2 warming for the next contractions, carried by extra workgroups of
+// attention_kernel on the CUs it leaves idle
 template <typename T>
 fm_status attention(fm_handle* h, int l, int B, const int* n_new, bool own_ctx, hipStream_t st,
-                    const L2Warm* warm = nullptr) {
+                    const L2Warm& warm = L2Warm{}) {
   const fm_config& c = h->cfg;
   const int hd = c.d / c.n_heads;
   AttnArgs a{};
@@ -702,13 +729,8 @@ fm_status attention(fm_handle* h, int l, int B, const int* n_new, bool own_ctx, 
     }
   }
   a.n_ranges = attn_max_ranges(cap_blocks + 1, ATT_WAVES);
-  int grid = B * c.n_heads * a.n_ranges;
-  if (warm && grid + 8 <= h->n_cu) {
-    a.warm = *warm;
-    a.warm.first_wg = grid;
-    a.warm.n_wg = (h->n_cu - grid) / 8 * 8;
-    grid += a.warm.n_wg;
-  }
+  a.warm = warm;
+  const int grid = l2_warm_attach(h, B * c.n_heads * a.n_ranges, a.warm);
   if (hd == 128)
     hipLaunchKernelGGL((attention_kernel<T, 128, ATT_WAVES>), dim3(grid), dim3(ATT_WAVES * 64), 0, st, a);
   else
@@ -1019,10 +1041,16 @@ fm_status draft_impl(fm_handle* h, const void* noise, int B, const void* new_fea
         }
       }
       {
-        // the CUs attention leaves idle warm the L2s with W_o's tiles
-        L2Warm wo{};
-        const bool warm = l2_warm_plan(h, Mb, d, d, blk(h, l, B_WO), &wo);
-        FM_TRY(attention<T>(h, l, B, nb_new, bt != nullptr, st, warm ? &wo : nullptr));
+        // the CUs attention leaves idle warm the L2s with W_o's tiles and
+        // the first three quarters of each of fc1's groups (all of fc1
+        // besides W_o would overflow a 4 MB L2 at d = 2048)
+        L2Warm w{};
+        if (l2_region(h, Mb, d, d, blk(h, l, B_WO), &w.reg[w.n_reg])) ++w.n_reg;
+        if (fuse_ln && l2_region_ln(h, F, d, blk(h, l, B_W1), &w.reg[w.n_reg])) {
+          w.reg[w.n_reg].take_u4 = w.reg[w.n_reg].group_u4 * 3 / 4;
+          ++w.n_reg;
+        }
+        FM_TRY(attention<T>(h, l, B, nb_new, bt != nullptr, st, w));
       }
       {
         EpiParams e{};
