@@ -31,9 +31,9 @@ import synth  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 METRIC = "draft+verify steps/sec at K=16, batch 1 (Qwen3-8B-shaped); % of HBM peak"
-KERNEL_SOURCES = {"lmhead_kernel": ["lmhead.hpp", "common.hpp"],
-                  "lmhead_ks_kernel": ["lmhead.hpp", "common.hpp"],
-                  "embed_kernel": ["embed.hpp", "common.hpp"]}
+KERNEL_SOURCES = {"lmhead_kernel": ["lmhead.hpp", "common.hpp", "philox.hpp", "stream.hpp"],
+                  "lmhead_ks_kernel": ["lmhead.hpp", "common.hpp", "philox.hpp", "stream.hpp"],
+                  "embed_kernel": ["embed.hpp", "common.hpp", "stream.hpp"]}
 
 
 def lm_kernel_name(cfg) -> str:
