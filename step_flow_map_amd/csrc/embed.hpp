@@ -16,7 +16,10 @@
 // "split" of V), sum their accumulators through LDS in wave order and store
 // the split's float32 partial with plain stores.  embed_reduce_kernel,
 // launched next, sums a column block's splits in split order and writes e
-// and h, so the result never depends on scheduling.  Column blocks get Sf
+// and h, so the result never depends on scheduling; it also writes h's
+// per-16-column row statistics for the LayerNorm fused into the first QKV,
+// and further workgroups of it apply the context fusion's LayerNorm to the
+// rows the call appends.  Column blocks get Sf
 // row splits, or Ss for the blocks with cb % 4 == 1: with 16 blocks of 256
 // bytes those stream about 20% slower (their offset in each 4 KB row of E),
 // so they get shorter row ranges and every workgroup finishes at about the
