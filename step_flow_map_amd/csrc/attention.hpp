@@ -221,7 +221,8 @@ __device__ __forceinline__ void attn_block(const AttnTile<T, HD>& t, const typen
   }
 }
 
-template <typename T, int HD, int NW>
+// WARM: the kind of the L2 warming its extra workgroups do (L2W_NONE: none)
+template <typename T, int HD, int NW, int WARM>
 __global__ __launch_bounds__(NW * 64) void attention_kernel(AttnArgs g) {
   typedef typename Vec<T>::type VT;
   constexpr int KB = 16;              // block rows (queries) per branch
@@ -233,9 +234,11 @@ __global__ __launch_bounds__(NW * 64) void attention_kernel(AttnArgs g) {
   __shared__ float sm[NW][KB], sl[NW][KB];
   __shared__ int flag;
 
-  if (g.warm.n_reg > 0 && (int)blockIdx.x >= g.warm.first_wg) {  // the next contractions' weights
-    l2_warm(g.warm, blockIdx.x, NW * 64);
-    return;
+  if constexpr (WARM != L2W_NONE) {
+    if ((int)blockIdx.x >= g.warm.first_wg) {  // the next contractions' weights
+      l2_warm<WARM>(g.warm, blockIdx.x, NW * 64);
+      return;
+    }
   }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int j = lane & 15, grp = lane >> 4;

@@ -427,14 +427,28 @@ fm_status launch_gemm_epi(const GemmArgs& a, const EpiParams& e, const GemmPlan&
   return FM_OK;
 }
 
-// The L2 region of the contraction gemm() runs for (M, N, K) on weights W,
-// where its workgroup b reads tile group b alone: the tile paths without a k
-// split (gemm_kernel, or gemm_tg_kernel with its tiles per workgroup), and N
-// a whole number of groups.  False: no such mapping.
+// The L2 region of the contraction gemm() runs for (M, N, K) on weights W:
+// on the tile paths without a k split (gemm_kernel, or gemm_tg_kernel with its
+// tiles per workgroup) workgroup b reads tile group b alone, on the LDS-slice
+// path k slice b % S of row group b / S; N a whole number of groups.  False:
+// no such mapping.
 bool l2_region(const fm_handle* h, int M, int N, int K, const void* W, L2Region* r) {
   const fm_dtype t = h->cfg.dtype;
   int S_as, KS_as;
-  if (t == FM_BF16 && use_as(M, N, K, t, &S_as, &KS_as)) return false;
+  *r = L2Region{};
+  if (t == FM_BF16 && use_as(M, N, K, t, &S_as, &KS_as)) {
+    // the LDS-slice path: workgroup b = g * S + s reads rows 128 g .. + 128
+    // (AS_TILES tiles), k slice s of KS_as elements
+    const int rows = 16 * AS_TILES;
+    if (N % rows || (size_t)KS_as * esize(t) % 16 || (size_t)K * esize(t) % 16) return false;
+    r->base = reinterpret_cast<const uint4*>(W);
+    r->n_groups = N / rows;
+    r->slices = S_as;
+    r->rows = rows;
+    r->row_u4 = (size_t)K * esize(t) / 16;
+    r->take_u4 = (size_t)KS_as * esize(t) / 16;
+    return true;
+  }
   const GemmPlan p = plan_gemm(M, N, K, t);
   const int tiles = p.tg == 2 ? 2 : 1;
   if (p.S != 1 || N % (16 * tiles) || p.grid != N / (16 * tiles)) return false;
@@ -449,6 +463,7 @@ bool l2_region(const fm_handle* h, int M, int N, int K, const void* W, L2Region*
 // The same for a fused-LayerNorm contraction (gemm_ln: workgroup b reads
 // tiles 2b and 2b + 1)
 bool l2_region_ln(const fm_handle* h, int N, int K, const void* W, L2Region* r) {
+  *r = L2Region{};
   if (N % 32) return false;
   r->base = reinterpret_cast<const uint4*>(W);
   r->group_u4 = (size_t)32 * K * esize(h->cfg.dtype) / 16;
@@ -673,6 +688,17 @@ fm_status embed(fm_handle* h, const void* x, int ldx, int M, float alpha, float 
 // branch b's request (its visible context is that request's device-resident
 // length plus n_new[b]).  Grids are sized for the cache capacity; the ranges
 // in use follow the current length on the device.
+template <typename T, int HD>
+void launch_attention(const AttnArgs& a, int grid, int warm_kind, hipStream_t st) {
+  const dim3 g(grid), b(ATT_WAVES * 64);
+  if (warm_kind == L2W_TILES)
+    hipLaunchKernelGGL((attention_kernel<T, HD, ATT_WAVES, L2W_TILES>), g, b, 0, st, a);
+  else if (warm_kind == L2W_SLICES)
+    hipLaunchKernelGGL((attention_kernel<T, HD, ATT_WAVES, L2W_SLICES>), g, b, 0, st, a);
+  else
+    hipLaunchKernelGGL((attention_kernel<T, HD, ATT_WAVES, L2W_NONE>), g, b, 0, st, a);
+}
+
 // warm: L2 warming for the next contractions, carried by extra workgroups of
 // attention_kernel on the CUs it leaves idle
 template <typename T>
@@ -730,11 +756,15 @@ fm_status attention(fm_handle* h, int l, int B, const int* n_new, bool own_ctx, 
   }
   a.n_ranges = attn_max_ranges(cap_blocks + 1, ATT_WAVES);
   a.warm = warm;
+  // the warming's regions are of one kind: those of the first region's kind
+  const int kind = a.warm.n_reg <= 0 ? L2W_NONE : a.warm.reg[0].slices > 0 ? L2W_SLICES : L2W_TILES;
+  int n_same = 0;
+  while (n_same < a.warm.n_reg && (a.warm.reg[n_same].slices > 0) == (kind == L2W_SLICES)) ++n_same;
+  a.warm.n_reg = n_same;
   const int grid = l2_warm_attach(h, B * c.n_heads * a.n_ranges, a.warm);
-  if (hd == 128)
-    hipLaunchKernelGGL((attention_kernel<T, 128, ATT_WAVES>), dim3(grid), dim3(ATT_WAVES * 64), 0, st, a);
-  else
-    hipLaunchKernelGGL((attention_kernel<T, 64, ATT_WAVES>), dim3(grid), dim3(ATT_WAVES * 64), 0, st, a);
+  const int wk = a.warm.n_reg > 0 ? kind : L2W_NONE;
+  if (hd == 128) launch_attention<T, 128>(a, grid, wk, st);
+  else launch_attention<T, 64>(a, grid, wk, st);
   FM_LAUNCHED("attention_kernel");
   return FM_OK;
 }
