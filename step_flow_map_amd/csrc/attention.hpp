@@ -2,11 +2,11 @@
 // keys (every query sees every key, no mask).
 //
 // Cache layout, per DiT block and head, P positions (context rows, then one
-// 32-position scratch block per branch that holds that branch's 16 block rows):
-//   keys    kc[head][pos][hd]                         row-major
-//   values  vt[head][pos / 32][hd][32]                transposed in 32-key blocks,
-//           key kk of a block at slot vt_slot<T>(kk)
-// so that every MFMA operand of the kernel is one contiguous 16-byte load.
+// 32-position scratch block per branch that holds that branch's 16 block rows)
+// in 32-key blocks of 32 x hd keys (key cache) and 32 x hd values (value
+// cache).  Inside a block both are stored in the order of the MFMA operands
+// that read them (kt_off, vt_off): every operand is one 16-byte piece per
+// lane, and the 64 lanes of a wave read 1 KB in lane order.
 //
 // One wave handles whole 32-key blocks.  For a block it computes the
 // transposed scores S^T = K Q^T (MFMA, A = 16 keys, B = the 16 queries), which
@@ -46,11 +46,28 @@ template <> __host__ __device__ __forceinline__ int vt_slot<bf16_t>(int kk) {
 }
 template <> __host__ __device__ __forceinline__ int vt_slot<float>(int kk) { return kk; }
 
+// Offset of key kk (0..31), dimension dd of a 32-key block, in elements from
+// the block's start, for pieces of VE = 16 / sizeof(T) elements:
+//   keys:   operand (tile kk / 16, piece dd / VE), lane (kk % 16) + 16 (piece % 4),
+//           where the scores' MFMA step s takes pieces 4s .. 4s + 3 of each key;
+//   values: slot q = vt_slot(kk), operand (step q / (4 VE), dims 16 (dd / 16) ..),
+//           lane (dd % 16) + 16 ((q / VE) % 4).
+// Operand o of a block is its 16-byte words 64 o .. 64 o + 63 (word = lane).
+template <typename T> __host__ __device__ __forceinline__ int kt_off(int kk, int dd, int hd) {
+  constexpr int VE = 16 / (int)sizeof(T);
+  return (((kk >> 4) * (hd / VE) + dd / VE) * 16 + (kk & 15)) * VE + dd % VE;
+}
+template <typename T> __host__ __device__ __forceinline__ int vt_off(int kk, int dd, int hd) {
+  constexpr int VE = 16 / (int)sizeof(T);
+  const int q = vt_slot<T>(kk);
+  return ((((q / (4 * VE)) * (hd / 16) + (dd >> 4)) * 4 + (q / VE) % 4) * 16 + (dd & 15)) * VE + q % VE;
+}
+
 struct AttnArgs {
   const void* q;       // [B*K][ldq] queries of the block rows
   int ldq;
-  const void* kc;      // this DiT block's key cache   [nh][P][hd] (request 0)
-  const void* vt;      // this DiT block's value cache [nh][P/32][hd][32] (request 0)
+  const void* kc;      // this DiT block's key cache   [nh][P/32][32 hd] (request 0)
+  const void* vt;      // this DiT block's value cache [nh][P/32][32 hd] (request 0)
   size_t req_stride;   // elements between consecutive requests' caches
   int P;               // positions per head (multiple of 32)
   const int* ctx_len;  // device: context length of each request before this call
@@ -121,6 +138,22 @@ struct AttnTile {
   VT k[2][QS];                              // keys 16*tb + j, pieces 4s+grp
   VT v[PS][OT];                             // value dims 16t + j, slots ps*4*VE + grp*VE ..
 };
+
+// The operands of one 32-key block (keys at kb, values at vb, both in the
+// caches' block order): word lane of operands tb * QS + s and ps * OT + t.
+template <typename T, int HD>
+__device__ __forceinline__ void attn_tile_load(AttnTile<T, HD>& t, const T* kb, const T* vb, int lane) {
+  typedef AttnTile<T, HD> Tile;
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+    for (int s = 0; s < Tile::QS; ++s) t.k[tb][s] = vload<T>(kb + (size_t)((tb * Tile::QS + s) * 64 + lane) * Tile::VE);
+#pragma unroll
+  for (int ps = 0; ps < Tile::PS; ++ps)
+#pragma unroll
+    for (int ot = 0; ot < Tile::OT; ++ot)
+      t.v[ps][ot] = vload<T>(vb + (size_t)((ps * Tile::OT + ot) * 64 + lane) * Tile::VE);
+}
 
 template <typename T, int HD>
 __device__ __forceinline__ void attn_block(const AttnTile<T, HD>& t, const typename Vec<T>::type (&qf)[AttnTile<T, HD>::QS],
@@ -270,19 +303,8 @@ __global__ __launch_bounds__(NW * 64) void attention_kernel(AttnArgs g) {
   auto phys = [&](int bi) { return bi < ctx_blocks ? bi : g.scratch_blk + g.scratch_step * b; };
   auto nvalid = [&](int bi) { return bi < ctx_blocks ? min(ATT_BLK, C - ATT_BLK * bi) : KB; };
   auto load = [&](Tile& t, int bi) {
-    const int pb = phys(bi);
-#pragma unroll
-    for (int tb = 0; tb < 2; ++tb) {
-      const T* kr = kbase + (size_t)(pb * ATT_BLK + 16 * tb + j) * HD;
-#pragma unroll
-      for (int s = 0; s < QS; ++s) t.k[tb][s] = vload<T>(kr + (4 * s + grp) * VE);
-    }
-    const T* vb = vbase + (size_t)pb * HD * ATT_BLK;
-#pragma unroll
-    for (int ps = 0; ps < PS; ++ps)
-#pragma unroll
-      for (int ot = 0; ot < OT; ++ot)
-        t.v[ps][ot] = vload<T>(vb + (size_t)(16 * ot + j) * ATT_BLK + ps * 4 * VE + grp * VE);
+    const size_t off = (size_t)phys(bi) * ATT_BLK * HD;
+    attn_tile_load<T, HD>(t, kbase + off, vbase + off, lane);
   };
 
   float m_run = -INFINITY, l_run = 0.f;  // of query row j (same in all four groups)
@@ -381,9 +403,9 @@ __global__ __launch_bounds__(NW * 64) void attention_kernel(AttnArgs g) {
 // read from HBM once per workgroup: every wave loads a part of the next two
 // blocks into registers while the current two are computed, writes it into
 // the other half of a double-buffered LDS stage, and one barrier per step
-// hands the stage over.  Pieces are placed in LDS with XOR swizzles (key rows
-// by key, value rows by row / 4) so that the MFMA fragment reads of each 16
-// lanes hit distinct banks.  Each branch's own 16 block rows (its scratch
+// hands the stage over.  The stage keeps the caches' block order, in which
+// each MFMA operand is 1 KB read in lane order (no bank conflicts).  Each
+// branch's own 16 block rows (its scratch
 // block) are read by the branch's stream-0 wave of the last range straight
 // from HBM.  The waves of a branch merge through LDS; with several ranges the
 // ranges' partial states go to memory and attention_merge_kernel combines
@@ -440,39 +462,32 @@ __global__ __launch_bounds__(512) void attention_tree_kernel(AttnArgs g) {
 #pragma unroll
   for (int t = 0; t < OT; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // MFMA fragments of this wave's block of a step from the stage half
+  // MFMA fragments of this wave's block of a step from the stage half (the
+  // block's words in the caches' order: a wave reads 1 KB in lane order)
   auto frags = [&](Tile& t, int half) {
-    const uint4* kb = stage + half * STEP_U4 + stream * BLOCK_U4;
+    const uint4* kb = stage + half * STEP_U4 + stream * BLOCK_U4 + lane;
     const uint4* vb = kb + PART_U4;
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb) {
-      const int key = 16 * tb + j;
+    for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-      for (int s = 0; s < QS; ++s) t.k[tb][s] = kb[key * KP + ((4 * s + grp) ^ (key & (KP - 1)))];
-    }
+      for (int s = 0; s < QS; ++s) t.k[tb][s] = kb[(tb * QS + s) * 64];
 #pragma unroll
-    for (int ot = 0; ot < OT; ++ot) {
-      const int r = 16 * ot + j;
-      t.v[0][ot] = vb[r * 4 + (grp ^ ((r >> 2) & 3))];
-    }
+    for (int ot = 0; ot < OT; ++ot) t.v[0][ot] = vb[ot * 64];
   };
 
-  // lane's share of a step: element e = u*512 + tid of the step's uint4
-  // (stream, keys/values, slot); the global piece is chosen so that it lands
-  // at that slot of the swizzled layout.  Blocks past the range load block
-  // blo instead (never used).  Both addresses are formed and one selected, so
-  // no branch surrounds the load.
+  // lane's share of a step: word e = u*512 + tid of the step's (stream,
+  // keys/values, word), copied in the caches' order.  Blocks past the range
+  // load block blo instead (never used).  Both addresses are formed and one
+  // selected, so no branch surrounds the load.
   const uint4* src[PER_LANE];
   int src_blk[PER_LANE];
 #pragma unroll
   for (int u = 0; u < PER_LANE; ++u) {
     const int e = u * NW * 64 + tid;
     const int sb = e / BLOCK_U4, w = e % BLOCK_U4;
-    const int key = w / KP, kpiece = (w % KP) ^ (key & (KP - 1));
-    const int wv = w - PART_U4, r = wv >> 2, vpiece = (wv & 3) ^ ((r >> 2) & 3);
-    const T* ks = kbase + (size_t)key * HD + kpiece * VE;
-    const T* vs = vbase + (size_t)r * ATT_BLK + vpiece * VE;
-    src[u] = reinterpret_cast<const uint4*>(w < PART_U4 ? ks : vs);
+    const uint4* ks = reinterpret_cast<const uint4*>(kbase) + w;
+    const uint4* vs = reinterpret_cast<const uint4*>(vbase) + (w - PART_U4);
+    src[u] = w < PART_U4 ? ks : vs;
     src_blk[u] = sb;
   }
   // uint4 offset of block bi from block 0: keys ATT_BLK*HD elements, values HD*ATT_BLK
@@ -522,16 +537,8 @@ __global__ __launch_bounds__(512) void attention_tree_kernel(AttnArgs g) {
   // the branch's own block rows: the last range, the branch's stream-0 wave
   if (computes && range == n_ranges - 1 && stream == 0) {
     Tile t;
-    const int pb = g.scratch_blk + b;
-#pragma unroll
-    for (int tb = 0; tb < 2; ++tb) {
-      const T* kr = kbase + (size_t)(pb * ATT_BLK + 16 * tb + j) * HD;
-#pragma unroll
-      for (int s = 0; s < QS; ++s) t.k[tb][s] = vload<T>(kr + (4 * s + grp) * VE);
-    }
-    const T* vb = vbase + (size_t)pb * HD * ATT_BLK;
-#pragma unroll
-    for (int ot = 0; ot < OT; ++ot) t.v[0][ot] = vload<T>(vb + (size_t)(16 * ot + j) * ATT_BLK + grp * VE);
+    const size_t off = (size_t)(g.scratch_blk + b) * ATT_BLK * HD;
+    attn_tile_load<T, HD>(t, kbase + off, vbase + off, lane);
     attn_block<T, HD>(t, qf, KB_ROWS, g.scale, m_run, l_run, o);
   }
 

@@ -40,8 +40,8 @@ struct EpiParams {
   const float* gate;    // EPI_RESID, [N]
   // EPI_QKV (cache layout: attention.hpp)
   int rows_block;       // rows < rows_block are block rows (branch m / 16), the rest context rows
-  void* kcache;         // this DiT block's key cache   [nh][P][hd] of request 0
-  void* vcache;         // this DiT block's value cache [nh][P/32][hd][32] of request 0
+  void* kcache;         // this DiT block's key cache   [nh][P/32][32 hd] of request 0
+  void* vcache;         // this DiT block's value cache [nh][P/32][32 hd] of request 0
   size_t req_stride;    // elements from one request's key (value) cache to the next one's
   int P, hd, d;         // positions per head, head width, model width
   int scratch_pos0;     // position of the first block row
@@ -118,12 +118,12 @@ __device__ __forceinline__ float epilogue(const EpiParams& e, int m, int n, floa
     const int which = nn >= 2 * e.d;  // 0: key, 1: value
     const int col = nn - (1 + which) * e.d;
     const int head = col / e.hd, c = col - head * e.hd;
-    const size_t rb = (size_t)req * e.req_stride;
+    // the position's 32-key block, then the element's place in it
+    const size_t blk0 = (size_t)req * e.req_stride + ((size_t)head * e.P + (pos & ~31)) * e.hd;
     if (!which)
-      reinterpret_cast<T*>(e.kcache)[rb + ((size_t)head * e.P + pos) * e.hd + c] = from_f32<T>(v);
+      reinterpret_cast<T*>(e.kcache)[blk0 + kt_off<T>(pos & 31, c, e.hd)] = from_f32<T>(v);
     else
-      reinterpret_cast<T*>(e.vcache)[rb + (((size_t)head * (e.P >> 5) + (pos >> 5)) * e.hd + c) * 32 +
-                                     vt_slot<T>(pos & 31)] = from_f32<T>(v);
+      reinterpret_cast<T*>(e.vcache)[blk0 + vt_off<T>(pos & 31, c, e.hd)] = from_f32<T>(v);
   }
   return 0.f;
 }
