@@ -322,6 +322,53 @@ def main():
         for r in range(R):
             dr.truncate_req(r, cfg.c_prefill)
 
+    # Spread of single-step times: an event between consecutive replays on the
+    # replay stream (the timed loop above stays one bracket of K steps).
+    n_dist = min(args.steps, 200)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_dist + 1)]
+    evs[0].record(stream)
+    for i in range(n_dist):
+        run(i)
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per_us = np.array([evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(n_dist)])
+    step_us = {"median": float(np.median(per_us)), "p10": float(np.percentile(per_us, 10)),
+               "p90": float(np.percentile(per_us, 90)), "steps": n_dist}
+    if args.cycle:
+        for r in range(R):
+            dr.truncate_req(r, cfg.c_prefill)
+
+    # The loop as a host would drive it: after every step the accept lengths
+    # come back to pinned host memory and the host waits for them (wall clock).
+    acc_host = torch.empty(accept.shape, dtype=accept.dtype, pin_memory=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(n_dist):
+        run(i)
+        acc_host.copy_(accept, non_blocking=True)
+        stream.synchronize()
+    ms_sync = (time.perf_counter() - t0) * 1e3 / n_dist
+    host_sync = {"ms_per_step": ms_sync, "steps_per_s": 1000.0 / ms_sync, "steps": n_dist}
+    if args.cycle:
+        for r in range(R):
+            dr.truncate_req(r, cfg.c_prefill)
+
+    # practical streaming ceiling: a plain 1 GiB device-to-device copy (bytes
+    # read + bytes written per copy)
+    cp_src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    cp_dst = torch.empty_like(cp_src)
+    cp_dst.copy_(cp_src)
+    c0 = torch.cuda.Event(enable_timing=True)
+    c1 = torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(5):
+        cp_dst.copy_(cp_src)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    cp_gbs = 5 * 2 * (1 << 30) / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    copy_ceiling = {"bytes_per_copy": 2 * (1 << 30), "gbs": cp_gbs, "frac_of_peak": cp_gbs / HBM_PEAK_GBS}
+    del cp_src, cp_dst
+
     # live per-kernel durations: events around the kernel's launch, eager calls
     kernels = {}
     for name, probe in ((lm_kernel_name(cfg), fm.FM_PROBE_LM_HEAD), ("embed_kernel", fm.FM_PROBE_EMBED)):
@@ -340,6 +387,31 @@ def main():
         us = float(np.mean(durs[5:])) * 1e3
         ab = kernel_alg_bytes(cfg, name)
         kernels[name] = {"us": us, "alg_bytes": ab, "gbs": ab / us / 1e3}
+    # several jumps: the same step with the one-jump schedule, same context and
+    # inputs, so the cost of each further jump is the difference
+    one_jump = None
+    if cfg.num_steps > 1 and not args.cycle and not args.eager:
+        dr.set_schedule((0.0, 1.0))
+        g1 = []
+        for T, seed, _ in sets:
+            step(T, seed)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(T, seed)
+            g1.append(g)
+        for i in range(args.warmup):
+            g1[i % len(g1)].replay()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(args.steps):
+            g1[i % len(g1)].replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms1 = e0.elapsed_time(e1) / args.steps
+        one_jump = {"ms_per_step": ms1, "ms_per_further_jump": (ms - ms1) / (cfg.num_steps - 1),
+                    "ratio": ms / ms1}
+        dr.set_schedule(cfg.times)
     dom = max(kernels, key=lambda k: kernels[k]["us"])
     kd = kernels[dom]
     traffic = measured_traffic(dom, cfg.name)
@@ -371,11 +443,16 @@ def main():
                      "alg_bytes_per_launch": kd["alg_bytes"], "us_per_launch": kd["us"]},
         "step_roofline": {"alg_bytes": ab["total"], "achieved_gbs": ab["total"] / ms / 1e6,
                           "frac": ab["total"] / ms / 1e6 / HBM_PEAK_GBS},
+        "step_us": step_us,
+        "host_sync": host_sync,
+        "copy_ceiling": copy_ceiling,
         "kernels": kernels,
         "accept": accepts,
         "tau": float(np.mean([np.mean(a) for a in accepts]) + 1.0),
         "cpu_baseline": baseline,
     }
+    if one_jump is not None:
+        out["one_jump_same_context"] = one_jump
     print(json.dumps(out))
 
 
